@@ -1,0 +1,186 @@
+/*
+ * moe.h - C ABI of libmoe: forward pass of one sparse Mixture-of-Experts layer
+ * on an AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages define it (page "Mixture-of-Experts", beta.fermi.ai
+ * wiki, "Step-by-step mechanism for one MoE layer", steps 1-7, and its
+ * MoE_Layer pseudocode; page "Mixture of Experts (MoE): Architecture, Routing,
+ * and Scaling", "Core Architecture"):
+ *
+ *   1. router logits L = x W_g (+ optional per-expert logit bias), softmax over N
+ *   2. top-k experts per token                    (ties: lower expert id first)
+ *   3. combine weights = top-k softmax scores renormalised to sum to 1
+ *   4. capacity C per expert; at an over-full expert the lowest-scoring
+ *      requests are dropped (rank: softmax probability, ties: lower token)
+ *   5. dispatch: kept (token, expert) pairs grouped by expert
+ *   6. each expert's FFN  o = W2 GELU(W1 x + b1) + b2     (exact erf GELU)
+ *   7. combine: y[t] = sum over kept picks j of w[t,j] * o[t,j]; a dropped pick
+ *      contributes zero; a token with every pick dropped gets y[t] = 0.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code. On error nothing
+ *    has been launched. MOE_ERR_HIP means a launch failed; the HIP error code
+ *    is then available from moe_last_hip_error() (per calling thread).
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller. The library
+ *    never allocates or frees device memory and keeps no state between calls.
+ *    Scratch memory comes from the caller's `workspace` (device memory of at
+ *    least moe_workspace_bytes(...) bytes, 256-byte aligned).
+ *  - Inputs are never written. Outputs are fully overwritten (rows past the
+ *    kept-slot count S of slot-indexed outputs are left untouched).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*; NULL = the default stream). No call synchronises and no call
+ *    reads data-dependent sizes back to the host: S, the per-expert counts
+ *    and the drop count stay in device memory.
+ *  - Layouts are row-major and contiguous; base pointers 16-byte aligned.
+ *      x      [T, d]            activation dtype
+ *      W_g    [d, N]            activation dtype (router weight, L = x W_g)
+ *      W1     [N, d_ff, d]      activation dtype (nn.Linear(d, d_ff) weight per expert)
+ *      b1     [N, d_ff]         activation dtype, may be NULL
+ *      W2     [N, d, d_ff]      activation dtype (nn.Linear(d_ff, d) weight per expert)
+ *      b2     [N, d]            activation dtype, may be NULL
+ *      logit_bias [N]           fp32, may be NULL
+ *      y      [T, d]            activation dtype
+ *    Router logits and combine weights are fp32; rank keys are fp64.
+ *  - dtype: MOE_F32 (all activation tensors fp32) or MOE_BF16 (bf16 storage,
+ *    fp32 accumulation).
+ *  - Limits: 1 <= N <= 1024; 1 <= k <= min(N, 16); d and d_ff multiples of 8,
+ *    1 <= d, d_ff <= 65536; 0 <= T and T * max(k, N) < 2^31. T = 0 is a
+ *    successful no-op. Violations return MOE_ERR_INVALID_ARG or
+ *    MOE_ERR_UNSUPPORTED.
+ *  - capacity_factor: C = ceil(cf * k * T / N - 1e-6 * max(1, cf * k * T / N))
+ *    clamped to [1, T] (capacity formula in "Communication cost in distributed
+ *    settings" of the wiki page; the small guard absorbs the representation
+ *    error of cf). cf <= 0 means no limit (C = T).
+ *  - Results are deterministic: no floating-point atomics anywhere, so equal
+ *    inputs give bit-identical outputs from run to run.
+ *  - Thread safety: concurrent calls are safe when they use distinct
+ *    workspaces and outputs. Calls that share a workspace must be ordered on
+ *    one stream.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null required pointer, bad size or limit */
+#define MOE_ERR_UNSUPPORTED (-2) /* dtype, alignment or shape outside the limits */
+#define MOE_ERR_WORKSPACE (-3)   /* workspace missing, too small or misaligned */
+#define MOE_ERR_HIP (-4)         /* a HIP launch failed; see moe_last_hip_error() */
+
+#define MOE_F32 0
+#define MOE_BF16 1
+
+/* flags of moe_expert_ffn / moe_forward (bitwise or; 0 = defaults) */
+#define MOE_FLAG_HIDDEN_SPLIT 1 /* bf16 only: carry each hidden activation h into the
+                                   second GEMM as bf16(h) plus the bf16 residual
+                                   h - bf16(h) (about 16 significant bits instead of
+                                   8) at twice the second GEMM's matrix-core work */
+#define MOE_FLAG_Y_F32 2        /* moe_forward writes y as fp32 whatever `dtype` is */
+
+/* Library ABI version (major*100 + minor). */
+int moe_version(void);
+
+/* Human-readable text of a status code (static string). */
+const char* moe_strerror(int status);
+
+/* HIP error code (hipError_t as int) of the last failed launch on this thread. */
+int moe_last_hip_error(void);
+
+/* Expert capacity C for T tokens, N experts, top-k and capacity factor cf
+ * (formula above). Returns 0 for T = 0, a negative MOE_ERR_* code for bad
+ * arguments. Wiki page, "Communication cost in distributed settings". */
+int moe_capacity(int T, int N, int k, double capacity_factor);
+
+/* Device workspace, in bytes, that is enough for any entry point below called
+ * with these sizes and any flags (256-byte aligned pieces are carved from it).
+ * Returns 0 on invalid arguments. */
+size_t moe_workspace_bytes(int T, int d, int d_ff, int N, int k, double capacity_factor, int dtype);
+
+/* Steps 1-3 (wiki page, steps 1-3; "Inside the Router" on the corecocept page
+ * for keeping logits at higher precision).
+ *   in : x [T,d], W_g [d,N], logit_bias [N] fp32 or NULL
+ *   out: logits   [T,N] fp32, L = x W_g + bias (fp32 accumulation)
+ *        topk_idx [T,k] int32, expert ids in descending logit order,
+ *                 equal logits ordered by lower expert id
+ *        topk_w   [T,k] fp32, renormalised softmax scores, sum_j = 1
+ *        topk_key [T,k] fp64, log softmax probability L[t,e] - logsumexp_t(L)
+ *                 computed in fp64 from the fp32 logits (the capacity rank)
+ * Needs no workspace. */
+int moe_route(const void* x, const void* W_g, const float* logit_bias,
+              int T, int d, int N, int k, int dtype,
+              float* logits, int32_t* topk_idx, float* topk_w, double* topk_key,
+              void* stream);
+
+/* Steps 4-5 (wiki page, steps 4-5 and the capacity-constrained dispatch of
+ * its pseudocode; worked example with N=4, k=2, T=5, C=2).
+ * Pair index p = t*k + j names token t's j-th pick.
+ *   in : topk_idx, topk_w, topk_key as produced by moe_route
+ *   out: req_counts [N]   requests per expert before capacity
+ *        counts     [N]   kept pairs per expert = min(req_counts, C)
+ *        offsets    [N+1] exclusive scan of counts; S = offsets[N]
+ *        perm       [T*k] slot -> pair index; slots grouped by expert
+ *                         ascending, tokens ascending inside an expert;
+ *                         first S entries valid
+ *        inv        [T*k] pair -> slot, or -1 when the pair was dropped
+ *        slot_gate  [T*k] combine weight topk_w of each slot; first S valid
+ *        n_dropped  [1]   T*k - S
+ * At an expert with more than C requests the C pairs with the largest key
+ * are kept (equal keys: lower token first). Needs workspace. */
+int moe_dispatch(const int32_t* topk_idx, const float* topk_w, const double* topk_key,
+                 int T, int N, int k, double capacity_factor,
+                 int32_t* req_counts, int32_t* counts, int32_t* offsets,
+                 int32_t* perm, int32_t* inv, float* slot_gate, int32_t* n_dropped,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/* Step 6 with the gate of step 7 folded in (page "Mixture of Experts (MoE):
+ * Architecture, Routing, and Scaling", "Core Architecture": FFN(x) =
+ * W2 GELU(W1 x + b1) + b2).
+ *   in : x [T,d]; perm, offsets, slot_gate from moe_dispatch; W1, b1, W2, b2
+ *   out: slot_out [T*k, d] fp32 (either dtype); for each slot s < S of expert
+ *        e and token t = perm[s] / k:
+ *          slot_out[s] = slot_gate[s] * (W2[e] GELU(W1[e] x[t] + b1[e]) + b2[e])
+ *        (hidden activations are rounded to the activation dtype; the
+ *        gate-scaled outputs stay fp32 so that only y is rounded once more).
+ * flags: MOE_FLAG_HIDDEN_SPLIT is honoured (bf16); MOE_FLAG_Y_F32 has no
+ * effect here. T, k, capacity_factor bound S (S <= min(T*k, N*C)) for launch
+ * sizing. Needs workspace (the hidden activations live there). */
+int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
+                   const float* slot_gate,
+                   const void* W1, const void* b1, const void* W2, const void* b2,
+                   int T, int d, int d_ff, int N, int k, double capacity_factor, int dtype,
+                   int flags, void* slot_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Step 7 (wiki page, step 7; weighted combine of the pseudocode).
+ *   in : slot_out [T*k, d] fp32 (already gate-scaled), inv [T*k]
+ *   out: y [T,d] in `dtype`, y[t] = sum over j = 0..k-1 with inv[t*k+j] >= 0
+ *        of slot_out[inv[t*k+j]], summed in fp32 in increasing j; 0 if none.
+ * Needs no workspace. */
+int moe_combine(const void* slot_out, const int32_t* inv, int T, int d, int k, int dtype,
+                void* y, void* stream);
+
+/* Whole layer, steps 1-7, as one enqueue of the calls above on `stream`.
+ *   out: y [T,d] (required) in `dtype`, or fp32 with MOE_FLAG_Y_F32; optional
+ *        copies of intermediate results, each NULL to skip: logits_opt [T,N]
+ *        fp32, topk_idx_opt [T,k], inv_opt [T*k], req_counts_opt [N],
+ *        counts_opt [N], n_dropped_opt [1].
+ * flags: MOE_FLAG_* (unknown bits: MOE_ERR_INVALID_ARG).
+ * Needs workspace of moe_workspace_bytes(...) bytes. */
+int moe_forward(const void* x, const void* W_g, const float* logit_bias,
+                const void* W1, const void* b1, const void* W2, const void* b2,
+                int T, int d, int d_ff, int N, int k, double capacity_factor, int dtype,
+                int flags, void* y, float* logits_opt, int32_t* topk_idx_opt, int32_t* inv_opt,
+                int32_t* req_counts_opt, int32_t* counts_opt, int32_t* n_dropped_opt,
+                void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,24 @@
+"""Sparse Mixture-of-Experts layer forward on AMD Instinct MI355X (gfx950).
+
+The layer runs in libmoe.so (hand-written HIP kernels behind the C ABI in
+include/moe.h); this package is its thin Python binding. Importing it loads
+the library and raises if it is missing: there is no CPU fallback.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    MOE_BF16,
+    MOE_F32,
+    MOE_FLAG_HIDDEN_SPLIT,
+    MOE_FLAG_Y_F32,
+    MoeError,
+    alloc_workspace,
+    moe_capacity,
+    moe_combine,
+    moe_dispatch,
+    moe_expert_ffn,
+    moe_forward,
+    moe_route,
+    moe_version,
+    moe_workspace_bytes,
+)

@@ -1,0 +1,246 @@
+// C ABI of libmoe: argument checks, workspace carving and the launch sequence
+// of the MoE layer forward (declarations and contracts in include/moe.h).
+#include "../../include/moe.h"
+#include "moe_common.h"
+
+#include <math.h>
+
+namespace moe {
+
+static thread_local int g_last_hip = 0;
+
+int capacity_host(int T, int N, int k, double cf) {
+  if (T <= 0) return 0;
+  if (!(cf > 0.0)) return T;  // no limit
+  const double c = cf * (double)k * (double)T / (double)N;
+  double g = c - 1e-6 * (c > 1.0 ? c : 1.0);
+  double ci = ceil(g);
+  if (ci < 1.0) ci = 1.0;
+  if (ci > (double)T) ci = (double)T;
+  return (int)ci;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int check_shape(int T, int d, int d_ff, int N, int k, int dtype, bool need_dff) {
+  if (T < 0 || N < 1 || N > kMaxN || k < 1 || k > N || k > kMaxK) return MOE_ERR_INVALID_ARG;
+  if (d < 8 || d > 65536 || (d % 8) != 0) return MOE_ERR_UNSUPPORTED;
+  if (need_dff && (d_ff < 8 || d_ff > 65536 || (d_ff % 8) != 0)) return MOE_ERR_UNSUPPORTED;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const long long big = (long long)T * (long long)(k > N ? k : N);
+  if (big >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+static int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip = (int)e;
+  return MOE_ERR_HIP;
+}
+
+// Pieces of the moe_forward workspace.
+struct ForwardWs {
+  float* logits;
+  int32_t* idx;
+  float* w;
+  double* key;
+  int32_t *req, *cnt, *off, *ndrop;
+  int32_t *perm, *inv;
+  float* gate;
+  void* slot_out;
+  DispatchScratch ds;
+  FfnScratch fs;
+  size_t bytes;
+};
+
+static void carve_forward(void* base, int T, int d, int d_ff, int N, int k, int C, int dtype,
+                          int flags, ForwardWs* f) {
+  Carver c(base);
+  const size_t P = (size_t)(T > 0 ? T : 1) * k;
+  const int S_max = (int)((long long)T * k < (long long)N * C ? (long long)T * k : (long long)N * C);
+  f->logits = c.take<float>((size_t)(T > 0 ? T : 1) * N);
+  f->idx = c.take<int32_t>(P);
+  f->w = c.take<float>(P);
+  f->key = c.take<double>(P);
+  f->req = c.take<int32_t>(N);
+  f->cnt = c.take<int32_t>(N);
+  f->off = c.take<int32_t>((size_t)N + 1);
+  f->ndrop = c.take<int32_t>(1);
+  f->perm = c.take<int32_t>(P);
+  f->inv = c.take<int32_t>(P);
+  f->gate = c.take<float>(P);
+  f->slot_out = c.take<float>((size_t)(S_max > 0 ? S_max : 1) * d);
+  carve_dispatch(c, T * k, N, &f->ds);
+  carve_ffn(c, T, d, d_ff, N, k, C, S_max, dtype, flags, &f->fs);
+  f->bytes = align_up(c.off, 256);
+}
+
+static size_t dispatch_bytes(int T, int N, int k) {
+  Carver c(nullptr);
+  DispatchScratch ds;
+  carve_dispatch(c, T * k, N, &ds);
+  return align_up(c.off, 256);
+}
+
+static size_t ffn_bytes(int T, int d, int d_ff, int N, int k, int C, int dtype, int flags) {
+  Carver c(nullptr);
+  FfnScratch fs;
+  const int S_max = (int)((long long)T * k < (long long)N * C ? (long long)T * k : (long long)N * C);
+  carve_ffn(c, T, d, d_ff, N, k, C, S_max, dtype, flags, &fs);
+  return align_up(c.off, 256);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_version(void) { return 100; }
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, size or limit)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype, alignment or shape";
+    case MOE_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case MOE_ERR_HIP: return "HIP launch failed (see moe_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip; }
+
+int moe_capacity(int T, int N, int k, double capacity_factor) {
+  if (T < 0 || N < 1 || k < 1 || k > N || isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
+  return capacity_host(T, N, k, capacity_factor);
+}
+
+size_t moe_workspace_bytes(int T, int d, int d_ff, int N, int k, double capacity_factor,
+                           int dtype) {
+  if (check_shape(T, d, d_ff, N, k, dtype, true) != MOE_OK || isnan(capacity_factor)) return 0;
+  // enough for every flag combination: the split plan needs the most
+  ForwardWs f;
+  carve_forward(nullptr, T, d, d_ff, N, k, capacity_host(T, N, k, capacity_factor), dtype,
+                MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32, &f);
+  return f.bytes;
+}
+
+int moe_route(const void* x, const void* W_g, const float* logit_bias, int T, int d, int N, int k,
+              int dtype, float* logits, int32_t* topk_idx, float* topk_w, double* topk_key,
+              void* stream) {
+  int st = check_shape(T, d, 8, N, k, dtype, false);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !W_g || !logits || !topk_idx || !topk_w || !topk_key) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(W_g, 16) || !aligned(logits, 4) || !aligned(topk_idx, 4) ||
+      !aligned(topk_w, 4) || !aligned(topk_key, 8) || (logit_bias && !aligned(logit_bias, 4)))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_route(x, W_g, logit_bias, T, d, N, k, dtype, logits, topk_idx, topk_w,
+                                 topk_key, (hipStream_t)stream));
+}
+
+int moe_dispatch(const int32_t* topk_idx, const float* topk_w, const double* topk_key, int T,
+                 int N, int k, double capacity_factor, int32_t* req_counts, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* inv, float* slot_gate,
+                 int32_t* n_dropped, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_shape(T, 8, 8, N, k, MOE_F32, false);
+  if (st != MOE_OK) return st;
+  if (isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!topk_idx || !topk_w || !topk_key || !req_counts || !counts || !offsets || !perm || !inv ||
+      !slot_gate || !n_dropped)
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < dispatch_bytes(T, N, k))
+    return MOE_ERR_WORKSPACE;
+  const int C = capacity_host(T, N, k, capacity_factor);
+  Carver c(workspace);
+  DispatchScratch ds;
+  carve_dispatch(c, T * k, N, &ds);
+  return hip_status(launch_dispatch(topk_idx, topk_w, topk_key, T, N, k, C, req_counts, counts,
+                                    offsets, perm, inv, slot_gate, n_dropped, ds,
+                                    (hipStream_t)stream));
+}
+
+int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
+                   const float* slot_gate, const void* W1, const void* b1, const void* W2,
+                   const void* b2, int T, int d, int d_ff, int N, int k, double capacity_factor,
+                   int dtype, int flags, void* slot_out, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  int st = check_shape(T, d, d_ff, N, k, dtype, true);
+  if (st != MOE_OK) return st;
+  if (flags & ~(MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32)) return MOE_ERR_INVALID_ARG;
+  if (isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !perm || !offsets || !slot_gate || !W1 || !W2 || !slot_out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(W1, 16) || !aligned(W2, 16) || !aligned(slot_out, 16) ||
+      (b1 && !aligned(b1, 16)) || (b2 && !aligned(b2, 16)))
+    return MOE_ERR_UNSUPPORTED;
+  const int C = capacity_host(T, N, k, capacity_factor);
+  if (!workspace || !aligned(workspace, 256) ||
+      ws_bytes < ffn_bytes(T, d, d_ff, N, k, C, dtype, flags))
+    return MOE_ERR_WORKSPACE;
+  const int S_max = (int)((long long)T * k < (long long)N * C ? (long long)T * k : (long long)N * C);
+  Carver c(workspace);
+  FfnScratch fs;
+  carve_ffn(c, T, d, d_ff, N, k, C, S_max, dtype, flags, &fs);
+  return hip_status(launch_expert_ffn(x, perm, offsets, slot_gate, W1, b1, W2, b2, T, d, d_ff, N,
+                                      k, C, S_max, dtype, flags, slot_out, fs,
+                                      (hipStream_t)stream));
+}
+
+int moe_combine(const void* slot_out, const int32_t* inv, int T, int d, int k, int dtype, void* y,
+                void* stream) {
+  if (T < 0 || k < 1 || k > kMaxK || d < 8 || d > 65536 || (d % 8) != 0) {
+    return (T < 0 || k < 1 || k > kMaxK) ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED;
+  }
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!slot_out || !inv || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(slot_out, 16) || !aligned(y, 16)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_combine(slot_out, inv, T, d, k, dtype, y, (hipStream_t)stream));
+}
+
+int moe_forward(const void* x, const void* W_g, const float* logit_bias, const void* W1,
+                const void* b1, const void* W2, const void* b2, int T, int d, int d_ff, int N,
+                int k, double capacity_factor, int dtype, int flags, void* y, float* logits_opt,
+                int32_t* topk_idx_opt, int32_t* inv_opt, int32_t* req_counts_opt,
+                int32_t* counts_opt, int32_t* n_dropped_opt, void* workspace, size_t ws_bytes,
+                void* stream) {
+  int st = check_shape(T, d, d_ff, N, k, dtype, true);
+  if (st != MOE_OK) return st;
+  if (isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (flags & ~(MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !W_g || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(W_g, 16) || !aligned(W1, 16) || !aligned(W2, 16) ||
+      !aligned(y, 16) || (b1 && !aligned(b1, 16)) || (b2 && !aligned(b2, 16)) ||
+      (logit_bias && !aligned(logit_bias, 4)) || (logits_opt && !aligned(logits_opt, 4)))
+    return MOE_ERR_UNSUPPORTED;
+  const int C = capacity_host(T, N, k, capacity_factor);
+  ForwardWs f;
+  carve_forward(nullptr, T, d, d_ff, N, k, C, dtype, flags, &f);
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < f.bytes) return MOE_ERR_WORKSPACE;
+  carve_forward(workspace, T, d, d_ff, N, k, C, dtype, flags, &f);
+  if (logits_opt) f.logits = logits_opt;
+  if (topk_idx_opt) f.idx = topk_idx_opt;
+  if (inv_opt) f.inv = inv_opt;
+  if (req_counts_opt) f.req = req_counts_opt;
+  if (counts_opt) f.cnt = counts_opt;
+  if (n_dropped_opt) f.ndrop = n_dropped_opt;
+  const int S_max = (int)((long long)T * k < (long long)N * C ? (long long)T * k : (long long)N * C);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_route(x, W_g, logit_bias, T, d, N, k, dtype, f.logits, f.idx, f.w, f.key, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = launch_dispatch(f.idx, f.w, f.key, T, N, k, C, f.req, f.cnt, f.off, f.perm, f.inv, f.gate,
+                      f.ndrop, f.ds, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = launch_expert_ffn(x, f.perm, f.off, f.gate, W1, b1, W2, b2, T, d, d_ff, N, k, C, S_max,
+                        dtype, flags, f.slot_out, f.fs, s);
+  if (e != hipSuccess) return hip_status(e);
+  const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
+  return hip_status(launch_combine(f.slot_out, f.inv, T, d, k, y_dtype, y, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// Shared device helpers and host-side launch declarations of libmoe.
+// gfx950 (CDNA4) only: wave64, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+constexpr int kWave = 64;
+constexpr int kMaxN = 1024;
+constexpr int kMaxK = 16;
+
+enum Dtype : int { kF32 = 0, kBF16 = 1 };
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// Exact GELU, z * Phi(z) = z * (1 + erf(z / sqrt(2))) / 2, with the device
+// library's single-precision erf.
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+template <typename T>
+__device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, wave_shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += wave_shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += wave_shfl_xor(v, o);
+  return v;
+}
+
+// Order-preserving map of an fp64 key to uint64 (larger key -> larger code).
+// -0.0 is folded onto +0.0 first so that equal keys give equal codes.
+__device__ __forceinline__ unsigned long long key_code(double k) {
+  if (k == 0.0) k = 0.0;
+  unsigned long long b = (unsigned long long)__double_as_longlong(k);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ __forceinline__ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- host side
+// Capacity per the documented formula (moe.h).
+int capacity_host(int T, int N, int k, double cf);
+
+// Workspace carve: every piece 256-byte aligned.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = align_up(off, 256);
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+// Dispatch scratch (sizes depend on T*k and N only).
+struct DispatchScratch {
+  int32_t* tilecnt;   // [ntiles, N] requests per expert in each tile of pairs
+  int32_t* tilebase;  // [ntiles, N] requests per expert in earlier tiles
+  int32_t* bucket;    // [T*k] pairs grouped by expert, token order
+  int32_t* reqoff;    // [N+1] exclusive scan of requests per expert
+  unsigned long long* codes;  // [T*k] order-preserving key codes, bucket order
+};
+constexpr int kDispatchTile = 512;  // pairs per histogram tile (one wave each)
+void carve_dispatch(Carver& c, int P, int N, DispatchScratch* s);
+
+// Expert FFN scratch.
+struct FfnScratch {
+  void* hidden;       // [S_max, d_ff] activation dtype
+  void* hidden_lo;    // [S_max, d_ff] bf16 residual of the hidden layer (split mode) or null
+  int32_t* tiles;     // GEMM tile tables (int4 entries) for both GEMMs
+  int32_t* counts;    // [4] tile counts written by the schedule kernel
+};
+constexpr int kFlagHiddenSplit = 1;  // MOE_FLAG_HIDDEN_SPLIT
+constexpr int kFlagYF32 = 2;         // MOE_FLAG_Y_F32
+void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype,
+               int flags, FfnScratch* s);
+
+// Launchers (return hipError_t of the last launch).
+hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T, int d, int N,
+                        int k, int dtype, float* logits, int32_t* idx, float* w, double* key,
+                        hipStream_t st);
+hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key, int T, int N,
+                           int k, int C, int32_t* req, int32_t* cnt, int32_t* off, int32_t* perm,
+                           int32_t* inv, float* gate, int32_t* n_dropped,
+                           const DispatchScratch& s, hipStream_t st);
+hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* off,
+                             const float* gate, const void* W1, const void* b1, const void* W2,
+                             const void* b2, int T, int d, int d_ff, int N, int k, int C,
+                             int S_max, int dtype, int flags, void* slot_out,
+                             const FfnScratch& s, hipStream_t st);
+hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d, int k,
+                          int dtype, void* y, hipStream_t st);
+
+}  // namespace moe
