@@ -1,0 +1,267 @@
+"""Benchmark of the sparse MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one moe_forward call (router, dispatch, both expert GEMMs, combine)
+on one batch of seeded synthetic inputs already resident in HBM. W untimed
+warm-up steps, then exactly K timed steps between two device synchronisations.
+Prints ONE JSON line (metric, value in tokens/s, roofline of the dominant
+kernel measured with HIP events recorded by the library inside the timed
+steps, and the CPU oracle timed on a bounded sample on the host).
+Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/sec + % of bf16 MFMA peak (or % HBM BW at small T)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+# Oracle sample (tokens whose outputs the CPU oracle computes) per workload,
+# sized for roughly 10-30 s of host work; routing always covers every token.
+CPU_SAMPLE = {"tiny_f32": 256, "switch_top1": 256, "mixtral_prefill": 24, "decode": 32,
+              "fine_grained": 256}
+DEFAULT_FLAGS = {"switch_top1": "split", "fine_grained": "split"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self):
+        h = ctypes.c_void_p()
+        if self.rt.hipEventCreate(ctypes.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.made.append(h.value)
+        return h.value
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        self.rt.hipEventSynchronize(ctypes.c_void_p(b))
+        if self.rt.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for h in self.made:
+            self.rt.hipEventDestroy(ctypes.c_void_p(h))
+        self.made = []
+
+
+def source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "sparse_mixture_experts_43_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else float(k["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(w, inp, sample):
+    import numpy as np
+    import oracle
+
+    toks = np.unique(np.linspace(0, w.T - 1, min(sample, w.T)).astype(np.int64))
+    t0 = time.perf_counter()
+    oracle.moe_forward(inp["x"], inp["W_g"], inp["logit_bias"], inp["W1"], inp["b1"], inp["W2"],
+                       inp["b2"], w.k, w.capacity_factor, tokens=toks)
+    dt = time.perf_counter() - t0
+    threads = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 0) for i in info), default=None)
+    except Exception:  # noqa: BLE001
+        pass
+    if not threads:
+        threads = len(os.sched_getaffinity(0))
+    return {
+        "value": len(toks) / dt,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: routing and capacity for all {w.T} tokens, expert FFN and "
+                   f"combine for {len(toks)} evenly spaced tokens; {dt:.1f} s wall"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--flags", default=None, help="'split' for the bf16 hi+lo hidden layer, 'plain' for bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(expert parallelism is a design note only); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_mixture_experts_43_amd as moe
+    from moe_inputs import get_workload, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = get_workload(args.workload)
+    fl = args.flags or DEFAULT_FLAGS.get(w.name, "plain")
+    flags = moe.MOE_FLAG_Y_F32 | (moe.MOE_FLAG_HIDDEN_SPLIT if fl == "split" else 0)
+    log(f"workload {w.name}: T={w.T} d={w.d} d_ff={w.d_ff} N={w.N} k={w.k} cf={w.capacity_factor} "
+        f"dtype={w.dtype} flags={fl}+y_f32")
+    t0 = time.time()
+    inp = make_inputs(w)
+    log(f"inputs drawn on the host in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    dv = {k: (None if v is None else v.to(dev).contiguous()) for k, v in inp.items()}
+    ws = moe.alloc_workspace(moe.moe_workspace_bytes(w.T, w.d, w.d_ff, w.N, w.k, w.capacity_factor,
+                                                     dv["x"].dtype), dev)
+    y = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
+
+    def step():
+        moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"], dv["b2"],
+                        w.k, w.capacity_factor, workspace=ws, y=y, flags=flags)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warm-up done ({args.warmup} steps)")
+
+    ev = HipEvents()
+    marks = [[ev.create() for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        moe.moe_set_profile_events(marks[i])
+        step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    moe.moe_set_profile_events([])
+    ms_step = (t_end - t_start) * 1e3 / args.steps
+    names = ["router", "dispatch", "schedule", "expert_gemm1", "expert_gemm2", "combine"]
+    per = {n: 0.0 for n in names}
+    for m in marks:
+        for j, n in enumerate(names):
+            per[n] += ev.ms(m[j], m[j + 1])
+    per = {n: v / args.steps for n, v in per.items()}
+    ev_total = ev.ms(marks[0][0], marks[-1][6]) / args.steps
+    ev.close()
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (events {ev_total:.3f}); per kernel "
+        + ", ".join(f"{n} {v * 1e3:.1f}us" for n, v in per.items()))
+
+    # routing statistics of the timed input (read back after timing)
+    _, ex = moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"],
+                            dv["b2"], w.k, w.capacity_factor, workspace=ws, want_routing=True,
+                            flags=flags)
+    torch.cuda.synchronize()
+    counts = ex["counts"].cpu()
+    S = int(counts.sum())
+    touched = int((counts > 0).sum())
+    dropped = int(ex["n_dropped"].item())
+
+    es = 4 if w.dtype == "f32" else 2
+    gemm_flops = 2.0 * S * w.d * w.d_ff  # per expert GEMM
+    layer_flops = 2.0 * w.T * w.d * w.N + 2 * gemm_flops
+    w_bytes = touched * w.d * w.d_ff * es  # one expert matrix set (W1 or W2) of touched experts
+    layer_bytes = (w.T * w.d * es + w.d * w.N * es + 2 * w_bytes + w.T * w.d * 4
+                   + (0 if inp["b1"] is None else touched * (w.d + w.d_ff) * es))
+    # kernel-level algorithmic bytes: its weights + its unique activation inputs + its outputs
+    g1_bytes = w_bytes + w.T * w.d * es + S * w.d_ff * es
+    g2_bytes = w_bytes + S * w.d_ff * es + S * w.d * 4
+    peak_f = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    intensity = layer_flops / layer_bytes
+    bound = "mfma" if intensity > peak_f * 1e12 / (PEAK_HBM_GBPS * 1e9) else "hbm"
+    dom = "expert_gemm1" if per["expert_gemm1"] >= per["expert_gemm2"] else "expert_gemm2"
+    dom_ms = per[dom]
+    traffic = load_traffic(w.name, dom)
+    if bound == "mfma":
+        achieved = gemm_flops / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak_f, "unit": "TFLOP/s",
+                "frac": achieved / peak_f, "traffic": traffic, "kernel": dom,
+                "per_launch": f"{gemm_flops:.4g} flop (2*S*d*d_ff, S={S})"}
+    else:
+        kb = g1_bytes if dom == "expert_gemm1" else g2_bytes
+        achieved = kb / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "kernel": dom,
+                "per_launch": f"{kb:.4g} B (touched-expert weights + activations in/out)"}
+    tokens_per_s = w.T / (ms_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded normal draws of the workload's shapes and distributions)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "N": w.N, "k": w.k,
+                   "capacity_factor": w.capacity_factor, "hidden": fl, "y_dtype": "f32",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"tflops": layer_flops / (ms_step * 1e-3) / 1e12,
+                  "frac_bf16_peak": layer_flops / (ms_step * 1e-3) / 1e12 / peak_f,
+                  "alg_gbps": layer_bytes / (ms_step * 1e-3) / 1e9,
+                  "frac_hbm_peak": layer_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                  "flop_per_byte": intensity, "S": S, "dropped_pairs": dropped,
+                  "touched_experts": touched},
+        "kernels_us": {n: v * 1e3 for n, v in per.items()},
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on a {CPU_SAMPLE.get(w.name, 32)}-token sample")
+        out["cpu_baseline"] = cpu_baseline(w, inp, CPU_SAMPLE.get(w.name, 32))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

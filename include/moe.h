@@ -179,6 +179,16 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias,
                 int32_t* req_counts_opt, int32_t* counts_opt, int32_t* n_dropped_opt,
                 void* workspace, size_t ws_bytes, void* stream);
 
+/* Instrumentation for timing (not part of the layer): registers up to 7
+ * hipEvent_t handles (as void*, entries may be NULL) for the calling thread;
+ * n = 0 clears. While registered, moe_forward records event i on its stream
+ * at these points of its launch sequence: 0 before the router, 1 after the
+ * router, 2 after dispatch, 3 before the first expert GEMM, 4 after it,
+ * 5 after the second expert GEMM, 6 after the combine (moe_expert_ffn alone
+ * records 3-5). The caller owns the events. Returns MOE_ERR_INVALID_ARG for
+ * n outside [0, 7] or a NULL array with n > 0. */
+int moe_set_profile_events(void* const* events, int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     moe_expert_ffn,
     moe_forward,
     moe_route,
+    moe_set_profile_events,
     moe_version,
     moe_workspace_bytes,
 )

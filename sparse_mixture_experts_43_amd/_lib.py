@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "moe_combine": (_c_int, [_vp, _vp] + [_c_int] * 4 + [_vp, _vp]),
         "moe_forward": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_c_double, _c_int, _c_int]
                         + [_vp] * 7 + [_vp, _c_size, _vp]),
+        "moe_set_profile_events": (_c_int, [ctypes.POINTER(_vp), _c_int]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -67,7 +68,7 @@ _lib = _load()
 
 EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_capacity",
             "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
-            "moe_combine", "moe_forward")
+            "moe_combine", "moe_forward", "moe_set_profile_events")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -256,3 +257,10 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
                           _ptr(workspace), workspace.numel(), _stream(dev))
     _raise(st, "moe_forward")
     return (y, ex) if want_routing else y
+
+
+def moe_set_profile_events(events) -> None:
+    """Register raw hipEvent_t handles (ints or None, at most 7) for this thread; [] clears."""
+    n = len(events)
+    arr = (_vp * max(n, 1))(*[None if e is None else _vp(e) for e in events])
+    _raise(_lib.moe_set_profile_events(arr, n), "moe_set_profile_events")

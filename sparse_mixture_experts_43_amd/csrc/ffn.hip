@@ -508,12 +508,15 @@ hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, c
   set_lds_attr<BM, BN, WM, WN, false, SPLIT>(lds2);
   const int g1 = cdiv(pl.max1 > 0 ? pl.max1 : 1, 8) * 8;
   const int g2 = cdiv(pl.max2 > 0 ? pl.max2 : 1, 8) * 8;
+  profile_mark(3, st);
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true, SPLIT>), dim3(g1), dim3(NTH), lds1,
                      st, (const bf16*)x, nullptr, perm, k, (const bf16*)W1, (const bf16*)b1,
                      nullptr, t1, cnts + 0, d, d_ff, hid, hid_lo);
+  profile_mark(4, st);
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false, SPLIT>), dim3(g2), dim3(NTH), lds2,
                      st, (const bf16*)hid, (const bf16*)hid_lo, nullptr, k, (const bf16*)W2,
                      (const bf16*)b2, gate, t2, cnts + 1, d_ff, d, slot_out, nullptr);
+  profile_mark(5, st);
   return hipGetLastError();
 }
 
@@ -523,12 +526,15 @@ hipError_t launch_decode(const void* x, const int32_t* perm, const int32_t* off,
                          int d_ff, int N, int k, void* hid, bf16* hid_lo, void* slot_out,
                          hipStream_t st) {
   const int nb1 = cdiv(d_ff, kDecRows), nb2 = cdiv(d, kDecRows);
+  profile_mark(3, st);
   hipLaunchKernelGGL((decode_bf16_kernel<true, SPLIT>), dim3(N * nb1), dim3(256), 0, st,
                      (const bf16*)x, nullptr, perm, k, off, (const bf16*)W1, (const bf16*)b1,
                      nullptr, d, d_ff, nb1, hid, hid_lo);
+  profile_mark(4, st);
   hipLaunchKernelGGL((decode_bf16_kernel<false, SPLIT>), dim3(N * nb2), dim3(256), 0, st,
                      (const bf16*)hid, (const bf16*)hid_lo, perm, k, off, (const bf16*)W2,
                      (const bf16*)b2, gate, d_ff, d, nb2, slot_out, nullptr);
+  profile_mark(5, st);
   return hipGetLastError();
 }
 
@@ -565,12 +571,15 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, off, N, pl.BM,
                      cdiv(d_ff, pl.BN1), cdiv(d, pl.BN2), pl.max1, pl.max2, t1, t2, s.counts);
   if (pl.path == kPathF32) {
+    profile_mark(3, st);
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(pl.max1 > 0 ? pl.max1 : 1), dim3(256), 0, st,
                        (const float*)x, perm, k, (const float*)W1, (const float*)b1, nullptr, t1,
                        s.counts + 0, d, d_ff, (float*)s.hidden);
+    profile_mark(4, st);
     hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(pl.max2 > 0 ? pl.max2 : 1), dim3(256), 0, st,
                        (const float*)s.hidden, nullptr, k, (const float*)W2, (const float*)b2, gate,
                        t2, s.counts + 1, d_ff, d, (float*)slot_out);
+    profile_mark(5, st);
     return hipGetLastError();
   }
   if (pl.path == kPathTiledL)

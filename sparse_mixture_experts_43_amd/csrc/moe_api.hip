@@ -8,6 +8,13 @@
 namespace moe {
 
 static thread_local int g_last_hip = 0;
+constexpr int kProfileSlots = 7;
+static thread_local void* g_prof[kProfileSlots] = {};
+
+void profile_mark(int slot, hipStream_t st) {
+  if (slot >= 0 && slot < kProfileSlots && g_prof[slot] != nullptr)
+    hipEventRecord((hipEvent_t)g_prof[slot], st);
+}
 
 int capacity_host(int T, int N, int k, double cf) {
   if (T <= 0) return 0;
@@ -110,6 +117,12 @@ const char* moe_strerror(int status) {
 }
 
 int moe_last_hip_error(void) { return g_last_hip; }
+
+int moe_set_profile_events(void* const* events, int n) {
+  if (n < 0 || n > kProfileSlots || (n > 0 && events == nullptr)) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < kProfileSlots; ++i) g_prof[i] = (i < n) ? events[i] : nullptr;
+  return MOE_OK;
+}
 
 int moe_capacity(int T, int N, int k, double capacity_factor) {
   if (T < 0 || N < 1 || k < 1 || k > N || isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
@@ -231,16 +244,21 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
   if (n_dropped_opt) f.ndrop = n_dropped_opt;
   const int S_max = (int)((long long)T * k < (long long)N * C ? (long long)T * k : (long long)N * C);
   hipStream_t s = (hipStream_t)stream;
+  profile_mark(0, s);
   hipError_t e = launch_route(x, W_g, logit_bias, T, d, N, k, dtype, f.logits, f.idx, f.w, f.key, s);
   if (e != hipSuccess) return hip_status(e);
+  profile_mark(1, s);
   e = launch_dispatch(f.idx, f.w, f.key, T, N, k, C, f.req, f.cnt, f.off, f.perm, f.inv, f.gate,
                       f.ndrop, f.ds, s);
   if (e != hipSuccess) return hip_status(e);
+  profile_mark(2, s);
   e = launch_expert_ffn(x, f.perm, f.off, f.gate, W1, b1, W2, b2, T, d, d_ff, N, k, C, S_max,
                         dtype, flags, f.slot_out, f.fs, s);
   if (e != hipSuccess) return hip_status(e);
   const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
-  return hip_status(launch_combine(f.slot_out, f.inv, T, d, k, y_dtype, y, s));
+  e = launch_combine(f.slot_out, f.inv, T, d, k, y_dtype, y, s);
+  profile_mark(6, s);
+  return hip_status(e);
 }
 
 }  // extern "C"

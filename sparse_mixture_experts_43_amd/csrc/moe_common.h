@@ -109,6 +109,12 @@ constexpr int kFlagYF32 = 2;         // MOE_FLAG_Y_F32
 void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype,
                int flags, FfnScratch* s);
 
+// Profiling marks: records the event registered for `slot` (if any) on `st`.
+// Slots: 0 before the router, 1 after the router, 2 after dispatch, 3 before
+// the first expert GEMM, 4 after it, 5 after the second expert GEMM, 6 after
+// the combine.
+void profile_mark(int slot, hipStream_t st);
+
 // Launchers (return hipError_t of the last launch).
 hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T, int d, int N,
                         int k, int dtype, float* logits, int32_t* idx, float* w, double* key,
