@@ -30,8 +30,8 @@ PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 # Oracle sample (tokens whose outputs the CPU oracle computes) per workload,
 # sized for roughly 10-30 s of host work; routing always covers every token.
-CPU_SAMPLE = {"tiny_f32": 256, "switch_top1": 256, "mixtral_prefill": 24, "decode": 32,
-              "fine_grained": 256}
+CPU_SAMPLE = {"tiny_f32": 256, "switch_top1": 8192, "mixtral_prefill": 4096, "decode": 32,
+              "fine_grained": 16384}
 DEFAULT_FLAGS = {"switch_top1": "split", "fine_grained": "split"}
 
 
@@ -114,13 +114,14 @@ def cpu_baseline(w, inp, sample):
         pass
     if not threads:
         threads = len(os.sched_getaffinity(0))
+    what = (f"all {w.T} tokens" if len(toks) == w.T else
+            f"{len(toks)} evenly spaced tokens (routing and capacity still over all {w.T})")
     return {
         "value": len(toks) / dt,
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: routing and capacity for all {w.T} tokens, expert FFN and "
-                   f"combine for {len(toks)} evenly spaced tokens; {dt:.1f} s wall"),
+        "sample": f"fp64 numpy oracle, one layer forward over {what}; {dt:.1f} s wall",
     }
 
 
@@ -132,6 +133,9 @@ def main():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--flags", default=None, help="'split' for the bf16 hi+lo hidden layer, 'plain' for bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (the "
+                         "reference dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -191,6 +195,16 @@ def main():
     ev.close()
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (events {ev_total:.3f}); per kernel "
         + ", ".join(f"{n} {v * 1e3:.1f}us" for n, v in per.items()))
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 18  # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
+        del src, dst
 
     # routing statistics of the timed input (read back after timing)
     _, ex = moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"],
