@@ -112,11 +112,12 @@ size_t moe_workspace_bytes(int T, int d, int d_ff, int N, int k, double capacity
  *        topk_w   [T,k] fp32, renormalised softmax scores, sum_j = 1
  *        topk_key [T,k] fp64, log softmax probability L[t,e] - logsumexp_t(L)
  *                 computed in fp64 from the fp32 logits (the capacity rank)
- * Needs no workspace. */
+ * Needs workspace for bf16 (a transposed copy of W_g; moe_workspace_bytes is
+ * enough); fp32 needs none (workspace may be NULL). */
 int moe_route(const void* x, const void* W_g, const float* logit_bias,
               int T, int d, int N, int k, int dtype,
               float* logits, int32_t* topk_idx, float* topk_w, double* topk_key,
-              void* stream);
+              void* workspace, size_t ws_bytes, void* stream);
 
 /* Steps 4-5 (wiki page, steps 4-5 and the capacity-constrained dispatch of
  * its pseudocode; worked example with N=4, k=2, T=5, C=2).

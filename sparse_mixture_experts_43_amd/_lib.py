@@ -47,7 +47,7 @@ def _load() -> ctypes.CDLL:
         "moe_last_hip_error": (_c_int, []),
         "moe_capacity": (_c_int, [_c_int, _c_int, _c_int, _c_double]),
         "moe_workspace_bytes": (_c_size, [_c_int] * 5 + [_c_double, _c_int]),
-        "moe_route": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_vp]),
+        "moe_route": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_vp, _c_size, _vp]),
         "moe_dispatch": (_c_int, [_vp] * 3 + [_c_int] * 3 + [_c_double] + [_vp] * 7
                          + [_vp, _c_size, _vp]),
         "moe_expert_ffn": (_c_int, [_vp] * 8 + [_c_int] * 5 + [_c_double, _c_int, _c_int]
@@ -132,7 +132,8 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     return ws
 
 
-def moe_route(x: torch.Tensor, W_g: torch.Tensor, logit_bias: Optional[torch.Tensor], k: int):
+def moe_route(x: torch.Tensor, W_g: torch.Tensor, logit_bias: Optional[torch.Tensor], k: int,
+              workspace: Optional[torch.Tensor] = None):
     """Steps 1-3. Returns (logits fp32 [T,N], topk_idx int32 [T,k], topk_w fp32 [T,k], topk_key fp64 [T,k])."""
     dev = x.device
     T, d = x.shape
@@ -144,8 +145,11 @@ def moe_route(x: torch.Tensor, W_g: torch.Tensor, logit_bias: Optional[torch.Ten
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     key = torch.empty((T, k), dtype=torch.float64, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(moe_workspace_bytes(T, d, 8, N, k, 0.0, x.dtype), dev)
     st = _lib.moe_route(_ptr(x), _ptr(W_g), _ptr(logit_bias), T, d, N, k, _dtype_code(x.dtype),
-                        _ptr(logits), _ptr(idx), _ptr(w), _ptr(key), _stream(dev))
+                        _ptr(logits), _ptr(idx), _ptr(w), _ptr(key), _ptr(workspace),
+                        workspace.numel(), _stream(dev))
     _raise(st, "moe_route")
     return logits, idx, w, key
 

@@ -27,6 +27,7 @@
 // of each hidden activation and GEMM2 runs a second MFMA on it, so GEMM2 sees
 // the hidden layer to about 16 significant bits instead of 8 (twice GEMM2's
 // MFMA work; used where the weight stream, not MFMA, bounds the time).
+#include "gemm_ring.h"
 #include "moe_common.h"
 
 namespace moe {
@@ -267,240 +268,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_bf16_kerne
   }
 }
 
-// ---------------------------------------------------------------- tiled bf16, LDS-DMA ring
-// Fast path for K % 32 == 0. Tiles stream into a 4-slot LDS ring with
-// global_load_lds_dwordx4 (each lane's 16 bytes land at base + 16 * lane, so a
-// wave instruction fills 16 rows x 64 bytes); no VGPR staging and no ds_write.
-// Rows are 64 bytes (32 bf16 of K); the 16-byte chunk c of row r sits at
-// position c ^ ((r >> 2) & 3), which keeps the b128 fragment reads of 16
-// consecutive rows on distinct banks. Stage kt+3 is requested while stage kt
-// is multiplied; one wave barrier per stage, taken mid-stage so that the next
-// stage's first fragments are read while the current stage's last MFMAs run.
-constexpr int kRK = 32;       // K per ring stage
-constexpr int kRing = 4;      // ring slots
-constexpr int kRowB = kRK * 2;  // bytes per tile row per stage
-
-#define MOE_LDS __attribute__((address_space(3)))
-
-// s_waitcnt vmcnt(N) with expcnt/lgkmcnt unconstrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void vm_wait_n() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// 16 bytes per lane, global -> LDS (lane i lands at dst + 16 * i).
-__device__ __forceinline__ void dma16(const unsigned char* src, MOE_LDS unsigned char* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
-
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int BM, int BN, int WM, int WN, bool G1, bool SPLIT>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ A_lo, const int32_t* __restrict__ perm,
-    int kpairs, const bf16* __restrict__ W, const bf16* __restrict__ bias,
-    const float* __restrict__ gate, const int4* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles_p, int K, int Nout, void* __restrict__ out,
-    bf16* __restrict__ out_lo) {
-  constexpr int NW = (BM / WM) * (BN / WN);
-  constexpr int MT = WM / 32, NTW = WN / 32;
-  constexpr bool ALO = SPLIT && !G1;
-  constexpr int AI = BM / (NW * 16);  // A wave-loads per stage
-  constexpr int BI = BN / (NW * 16);
-  constexpr int LPS = AI + BI + (ALO ? AI : 0);  // loads per wave per stage
-  constexpr int A_OFF = 0;
-  constexpr int B_OFF = BM * kRowB;
-  constexpr int L_OFF = B_OFF + BN * kRowB;
-  constexpr int STAGE = L_OFF + (ALO ? BM * kRowB : 0);
-  static_assert(AI >= 1 && BI >= 1, "tile too small for the wave count");
-  static_assert(2 * LPS < 64, "vmcnt range");
-
-  extern __shared__ __align__(16) unsigned char smem[];
-
-  const int ntiles = *ntiles_p;
-  const int b = blockIdx.x;
-  const int chunk = (ntiles + 7) >> 3;
-  const int jx = b >> 3;
-  const int tile = (b & 7) * chunk + jx;
-  if (jx >= chunk || tile >= ntiles) return;
-  const int4 te = tiles[tile];
-  const int e = te.x, m0 = te.y, mcount = te.z, n0 = te.w * BN;
-
-  const int l = lane_id();
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wm0 = (wv / (BN / WN)) * WM;
-  const int wn0 = (wv % (BN / WN)) * WN;
-
-  // DMA source pointers: wave-load i covers tile rows (i*NW + wv)*16 .. +16;
-  // lane l fills row +l/4, position l%4, which holds chunk (l%4) ^ ((l>>4)&3).
-  const int csw = ((l & 3) ^ ((l >> 4) & 3)) * 16;  // byte offset of the chunk
-  const unsigned char* pa[AI];
-  const unsigned char* pl[ALO ? AI : 1];
-  const unsigned char* pb[BI];
-#pragma unroll
-  for (int i = 0; i < AI; ++i) {
-    const int r = (i * NW + wv) * 16 + (l >> 2);
-    const int rr = r < mcount ? r : mcount - 1;
-    const int slot = m0 + rr;
-    const size_t row = G1 ? (size_t)(perm[slot] / kpairs) : (size_t)slot;
-    pa[i] = (const unsigned char*)(A + row * K) + csw;
-    if constexpr (ALO) pl[i] = (const unsigned char*)(A_lo + row * K) + csw;
-  }
-  const bf16* We = W + (size_t)e * Nout * K;
-#pragma unroll
-  for (int i = 0; i < BI; ++i) {
-    const int r = (i * NW + wv) * 16 + (l >> 2);
-    const int n = n0 + r < Nout ? n0 + r : Nout - 1;
-    pb[i] = (const unsigned char*)(We + (size_t)n * K) + csw;
-  }
-  MOE_LDS unsigned char* lds = (MOE_LDS unsigned char*)smem;
-  auto issue_stage = [&](int slot, int kt) {
-    MOE_LDS unsigned char* st = lds + (slot & (kRing - 1)) * STAGE;
-    const int kb = kt * kRowB;
-#pragma unroll
-    for (int i = 0; i < AI; ++i)
-      dma16(pa[i] + kb, st + A_OFF + (i * NW + wv) * 1024);
-#pragma unroll
-    for (int i = 0; i < BI; ++i)
-      dma16(pb[i] + kb, st + B_OFF + (i * NW + wv) * 1024);
-    if constexpr (ALO) {
-#pragma unroll
-      for (int i = 0; i < AI; ++i)
-        dma16(pl[i] + kb, st + L_OFF + (i * NW + wv) * 1024);
-    }
-  };
-
-  // Fragment reads: row R, 16-byte chunk c (= 2*ks + l/32) at position c ^ ((R>>2)&3).
-  const int lr = l & 31;
-  const int half = l >> 5;
-  int aoffs[MT], boffs[NTW];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) aoffs[i] = (wm0 + i * 32 + lr) * kRowB;
-#pragma unroll
-  for (int j = 0; j < NTW; ++j) boffs[j] = (wn0 + j * 32 + lr) * kRowB;
-  const int sw = (lr >> 2) & 3;  // (R >> 2) & 3 with R = 32*x + lr
-  const int pos0 = ((0 + half) ^ sw) * 16;  // ks = 0
-  const int pos1 = ((2 + half) ^ sw) * 16;  // ks = 1
-
-  bf16x8 af[2][MT], bfr[2][NTW], alf[ALO ? 2 : 1][ALO ? MT : 1];
-  auto read_frags = [&](int kt, int ks, int set) {
-    const unsigned char* st = smem + (kt & (kRing - 1)) * STAGE;
-    const int pos = ks ? pos1 : pos0;
-#pragma unroll
-    for (int i = 0; i < MT; ++i) af[set][i] = *(const bf16x8*)(st + A_OFF + aoffs[i] + pos);
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) bfr[set][j] = *(const bf16x8*)(st + B_OFF + boffs[j] + pos);
-    if constexpr (ALO) {
-#pragma unroll
-      for (int i = 0; i < MT; ++i) alf[set][i] = *(const bf16x8*)(st + L_OFF + aoffs[i] + pos);
-    }
-  };
-
-  f32x16 acc[MT][NTW];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NTW; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-  auto mma = [&](int set) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
-    if constexpr (ALO) {
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alf[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  const int nk = K / kRK;
-  // Every ring step issues exactly LPS loads per wave: stage min(s, nk-1) into
-  // slot s % 4 (past the last stage the copies land in slots nobody reads), so
-  // "stage s+1 has landed" is always vmcnt <= LPS at the wait below.
-  issue_stage(0, 0);
-  issue_stage(1, nk > 1 ? 1 : nk - 1);
-  issue_stage(2, nk > 2 ? 2 : nk - 1);
-  vm_wait_n<2 * LPS>();
-  wg_barrier();
-  read_frags(0, 0, 0);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // fragments (kt, ks=0) are in set 0
-    read_frags(kt, 1, 1);
-    mma(0);
-    // issue the (kt, ks=1) fragment reads between the first MFMAs
-#pragma unroll
-    for (int q = 0; q < MT + NTW + (ALO ? MT : 0); ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // stage kt+1 has landed (only stage kt+2's loads may still fly) and no
-    // wave still reads the slot of stage kt-1
-    lgkm_wait0();
-    vm_wait_n<LPS>();
-    wg_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_stage(kt + 3, kt + 3 < nk ? kt + 3 : nk - 1);
-    read_frags(kt + 1, 0, 0);  // past the last stage: reads a dead slot, never used
-    mma(1);
-    // interleave: one MFMA, one DMA issue (x LPS), then one MFMA, one fragment read
-#pragma unroll
-    for (int q = 0; q < LPS; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < MT + NTW + (ALO ? MT : 0); ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  vm_wait_n<0>();  // no LDS DMA may outlive the workgroup
-
-  // Epilogue. Lane holds column l%32 and rows 8*jj + 4*(l/32) + r of each 32x32 tile.
-#pragma unroll
-  for (int j = 0; j < NTW; ++j) {
-    const int col = n0 + wn0 + j * 32 + lr;
-    if (col >= Nout) continue;
-    const float bv = bias != nullptr ? (float)bias[(size_t)e * Nout + col] : 0.f;
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = wm0 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
-        if (r < mcount) {
-          const int slot = m0 + r;
-          const float v = acc[i][j][q] + bv;
-          const size_t o = (size_t)slot * Nout + col;
-          if constexpr (G1) {
-            const float h = gelu_erf(v);
-            const bf16 hi = (bf16)h;
-            ((bf16*)out)[o] = hi;
-            if constexpr (SPLIT) out_lo[o] = (bf16)(h - (float)hi);
-          } else {
-            ((float*)out)[o] = v * gate[slot];
-          }
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- decode bf16
 // Block = 4 waves = 64 weight rows of one expert; each wave 16 rows x all K.
 constexpr int kDecRows = 64;
@@ -622,6 +389,214 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- decode bf16, LDS-DMA stream
+// Weight streaming for small per-expert batches (<= 64 slots), K % 128 == 0.
+// A block (4 waves) owns 64 weight rows of one expert and a K range; weights
+// and the expert's slot rows stream through a ring of LDS slots with
+// global_load_lds_dwordx4, every wave instruction one contiguous 1 KB run
+// (4 rows x 256 bytes), so HBM sees long sequential reads. Row r keeps its
+// 16-byte chunk c at position c ^ (r & 15): the 16-row fragment reads are
+// bank-conflict free. Each wave multiplies its 16 weight rows against the
+// slot groups with v_mfma_f32_16x16x32_bf16. With split-K the blocks write
+// fp32 partial sums and a reduce kernel applies bias and the epilogue.
+constexpr int kDKC = 128;             // K per chunk
+constexpr int kDRowB = kDKC * 2;      // 256 bytes per row per chunk
+constexpr int kDWRows = 64;           // weight rows per block
+
+template <bool G1, bool SPLIT>
+struct DecodeGeom {
+  static constexpr bool XLO = SPLIT && !G1;
+  static constexpr int RING = XLO ? 3 : 4;
+  static constexpr int W_OFF = 0;
+  static constexpr int X_OFF = kDWRows * kDRowB;           // 16 KB
+  static constexpr int L_OFF = X_OFF + 64 * kDRowB;        // 32 KB
+  static constexpr int SLOT = L_OFF + (XLO ? 64 * kDRowB : 0);
+  static constexpr size_t LDS = (size_t)RING * SLOT;
+};
+
+template <bool G1, bool SPLIT, int NG>
+__device__ __forceinline__ void decode_dma_body(
+    const bf16* __restrict__ X, const bf16* __restrict__ X_lo, const int32_t* __restrict__ perm,
+    int kpairs, const bf16* __restrict__ W, const bf16* __restrict__ bias,
+    const float* __restrict__ gate, int K, int Nout, int e, int n0, int m0, int mcount,
+    int kbeg, int nch, void* __restrict__ out, bf16* __restrict__ out_lo,
+    float* __restrict__ part, int S_cap, int ks) {
+  using Geo = DecodeGeom<G1, SPLIT>;
+  constexpr bool XLO = Geo::XLO;
+  constexpr int RING = Geo::RING;
+  constexpr int LPS = 4 + NG * (XLO ? 2 : 1);  // DMA instructions per wave per chunk
+  extern __shared__ __align__(16) unsigned char smem[];
+  MOE_LDS unsigned char* lds = (MOE_LDS unsigned char*)smem;
+  const int l = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+  // DMA sources: wave-load i covers rows 4*(4i + wv) .. +4; lane l fills row
+  // +l/16, position l%16, which holds chunk (l%16) ^ (row & 15).
+  const int rsub = l >> 4;
+  const unsigned char* pw[4];
+  const unsigned char* px[NG];
+  const unsigned char* pxl[XLO ? NG : 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * (4 * i + wv) + rsub;
+    const int c = (l & 15) ^ (r & 15);
+    const int n = min(n0 + r, Nout - 1);
+    pw[i] = (const unsigned char*)(W + ((size_t)e * Nout + n) * K + kbeg) + 16 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int r = 4 * (4 * i + wv) + rsub;
+    const int c = (l & 15) ^ (r & 15);
+    const int slot = m0 + min(r, mcount - 1);
+    const size_t row = G1 ? (size_t)(perm[slot] / kpairs) : (size_t)slot;
+    px[i] = (const unsigned char*)(X + row * K + kbeg) + 16 * c;
+    if constexpr (XLO) pxl[i] = (const unsigned char*)(X_lo + row * K + kbeg) + 16 * c;
+  }
+  auto issue = [&](int slot_i, int chunk) {
+    MOE_LDS unsigned char* st = lds + (slot_i % RING) * Geo::SLOT;
+    const int kb = chunk * kDRowB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(pw[i] + kb, st + Geo::W_OFF + (4 * i + wv) * 1024);
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      dma16(px[i] + kb, st + Geo::X_OFF + (4 * i + wv) * 1024);
+      if constexpr (XLO) dma16(pxl[i] + kb, st + Geo::L_OFF + (4 * i + wv) * 1024);
+    }
+  };
+
+  f32x4 acc[NG];
+#pragma unroll
+  for (int sg = 0; sg < NG; ++sg) acc[sg] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int R = 16 * wv + (l & 15);  // weight row of this lane's fragment
+  const int Rs = R & 15;
+  const int S = l & 15;              // slot row within a group (group base is a multiple of 16)
+
+#pragma unroll
+  for (int q = 0; q < RING - 1; ++q) issue(q, q < nch ? q : nch - 1);
+  for (int c = 0; c < nch; ++c) {
+    vm_wait_n<(RING - 2) * LPS>();
+    wg_barrier();
+    issue(c + RING - 1, c + RING - 1 < nch ? c + RING - 1 : nch - 1);
+    const unsigned char* st = smem + (c % RING) * Geo::SLOT;
+#pragma unroll
+    for (int kq = 0; kq < kDKC / 32; ++kq) {
+      const int ch = 4 * kq + (l >> 4);
+      const bf16x8 wf = *(const bf16x8*)(st + Geo::W_OFF + R * kDRowB + 16 * (ch ^ Rs));
+#pragma unroll
+      for (int sg = 0; sg < NG; ++sg) {
+        const int xo = (16 * sg + S) * kDRowB + 16 * (ch ^ S);
+        const bf16x8 xf = *(const bf16x8*)(st + Geo::X_OFF + xo);
+        acc[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf, acc[sg], 0, 0, 0);
+        if constexpr (XLO) {
+          const bf16x8 xl = *(const bf16x8*)(st + Geo::L_OFF + xo);
+          acc[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xl, acc[sg], 0, 0, 0);
+        }
+      }
+    }
+  }
+  vm_wait_n<0>();  // no LDS DMA may outlive the workgroup
+
+  // D[row][slot]: lane holds slot column l%16 of each group, rows 4*(l/16) + i.
+  const int gq = l >> 4;
+#pragma unroll
+  for (int sg = 0; sg < NG; ++sg) {
+    const int sl = 16 * sg + (l & 15);
+    if (sl >= mcount) continue;
+    const int slot = m0 + sl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 16 * wv + 4 * gq + i;
+      if (n >= Nout) continue;
+      if (part != nullptr) {
+        part[((size_t)ks * S_cap + slot) * Nout + n] = acc[sg][i];
+        continue;
+      }
+      const float v = acc[sg][i] + (bias != nullptr ? (float)bias[(size_t)e * Nout + n] : 0.f);
+      const size_t o = (size_t)slot * Nout + n;
+      if constexpr (G1) {
+        const float h = gelu_erf(v);
+        const bf16 hi = (bf16)h;
+        ((bf16*)out)[o] = hi;
+        if constexpr (SPLIT) out_lo[o] = (bf16)(h - (float)hi);
+      } else {
+        ((float*)out)[o] = v * gate[slot];
+      }
+    }
+  }
+}
+
+template <bool G1, bool SPLIT>
+__global__ __launch_bounds__(256) void decode_dma_kernel(
+    const bf16* __restrict__ X, const bf16* __restrict__ X_lo, const int32_t* __restrict__ perm,
+    int kpairs, const int32_t* __restrict__ off, const bf16* __restrict__ W,
+    const bf16* __restrict__ bias, const float* __restrict__ gate, int K, int Nout, int nblk_n,
+    int nsplit, void* __restrict__ out, bf16* __restrict__ out_lo, float* __restrict__ part,
+    int S_cap) {
+  const int ks = blockIdx.x % nsplit;
+  const int rest = blockIdx.x / nsplit;
+  const int e = rest / nblk_n;
+  const int nb = rest - e * nblk_n;
+  const int m0 = off[e];
+  const int mcount = off[e + 1] - m0;
+  if (mcount <= 0) return;  // untouched expert: its weights are never read
+  const int nch_all = K / kDKC;
+  const int per = (nch_all + nsplit - 1) / nsplit;
+  const int c0 = ks * per;
+  const int nch = min(nch_all, c0 + per) - c0;
+  if (nch <= 0) return;
+  const int n0 = nb * kDWRows;
+  float* pp = nsplit > 1 ? part : nullptr;
+  switch ((mcount + 15) / 16) {
+    case 1:
+      decode_dma_body<G1, SPLIT, 1>(X, X_lo, perm, kpairs, W, bias, gate, K, Nout, e, n0, m0,
+                                    mcount, c0 * kDKC, nch, out, out_lo, pp, S_cap, ks);
+      break;
+    case 2:
+      decode_dma_body<G1, SPLIT, 2>(X, X_lo, perm, kpairs, W, bias, gate, K, Nout, e, n0, m0,
+                                    mcount, c0 * kDKC, nch, out, out_lo, pp, S_cap, ks);
+      break;
+    case 3:
+      decode_dma_body<G1, SPLIT, 3>(X, X_lo, perm, kpairs, W, bias, gate, K, Nout, e, n0, m0,
+                                    mcount, c0 * kDKC, nch, out, out_lo, pp, S_cap, ks);
+      break;
+    default:
+      decode_dma_body<G1, SPLIT, 4>(X, X_lo, perm, kpairs, W, bias, gate, K, Nout, e, n0, m0,
+                                    mcount, c0 * kDKC, nch, out, out_lo, pp, S_cap, ks);
+      break;
+  }
+}
+
+// Split-K reduce: fixed-order sum of the partials, bias and epilogue. One
+// block per (expert, 64-row block), threads over (slot, row).
+template <bool G1, bool SPLIT>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(
+    const float* __restrict__ part, int nsplit, int S_cap, const int32_t* __restrict__ off,
+    const bf16* __restrict__ bias, const float* __restrict__ gate, int Nout, int nblk_n,
+    void* __restrict__ out, bf16* __restrict__ out_lo) {
+  const int e = blockIdx.x / nblk_n;
+  const int nb = blockIdx.x - e * nblk_n;
+  const int m0 = off[e];
+  const int mcount = off[e + 1] - m0;
+  const int n0 = nb * kDWRows;
+  for (int i = threadIdx.x; i < mcount * kDWRows; i += 256) {
+    const int sl = i / kDWRows, n = n0 + i % kDWRows;
+    if (n >= Nout) continue;
+    const int slot = m0 + sl;
+    float v = 0.f;
+    for (int q = 0; q < nsplit; ++q) v += part[((size_t)q * S_cap + slot) * Nout + n];
+    v += bias != nullptr ? (float)bias[(size_t)e * Nout + n] : 0.f;
+    const size_t o = (size_t)slot * Nout + n;
+    if constexpr (G1) {
+      const float h = gelu_erf(v);
+      const bf16 hi = (bf16)h;
+      ((bf16*)out)[o] = hi;
+      if constexpr (SPLIT) out_lo[o] = (bf16)(h - (float)hi);
+    } else {
+      ((float*)out)[o] = v * gate[slot];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32
 template <bool G1>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
@@ -692,10 +667,22 @@ struct Plan {
   int BM, BN1, BN2;
   int max1, max2;  // tile-table capacities
   bool split;
+  int ks1, ks2;    // decode split-K factors (1 = none)
+  bool dma1, dma2; // decode GEMMs on the LDS-DMA stream kernel
 };
+
+// Split-K factor for a decode GEMM: enough blocks to cover the CUs a few times.
+int decode_splits(int N, int Nout, int K) {
+  const int blocks = N * cdiv(Nout, kDWRows);
+  const int nch = K / kDKC;
+  int s = 1;
+  while (blocks * s < 1024 && s < 8 && nch / (2 * s) >= 8) s *= 2;
+  return s;
+}
 
 Plan make_plan(int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype, int flags) {
   Plan p{};
+  p.ks1 = p.ks2 = 1;
   const int Ccap = C < T ? C : T;
   p.split = dtype == kBF16 && (flags & kFlagHiddenSplit);
   if (dtype == kF32) {
@@ -704,6 +691,10 @@ Plan make_plan(int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype
   } else if (Ccap <= 64) {
     p.path = kPathDecode;
     p.BM = 64; p.BN1 = p.BN2 = kDecRows;
+    p.dma1 = d % kDKC == 0;
+    p.dma2 = d_ff % kDKC == 0;
+    p.ks1 = p.dma1 ? decode_splits(N, d_ff, d) : 1;
+    p.ks2 = p.dma2 ? decode_splits(N, d, d_ff) : 1;
   } else if (!p.split && Ccap >= 1024 && S_max / N >= 512) {
     p.path = kPathTiledL;
     p.BM = 256; p.BN1 = p.BN2 = 256;
@@ -720,16 +711,7 @@ Plan make_plan(int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype
   return p;
 }
 
-// once per call site (idempotent; a race between threads only repeats the call)
-#define MOE_SET_LDS_ONCE(kern, lds)                                                        \
-  do {                                                                                     \
-    static bool done_ = false;                                                             \
-    if (!done_) {                                                                          \
-      hipFuncSetAttribute((const void*)(kern), hipFuncAttributeMaxDynamicSharedMemorySize, \
-                          (int)(lds));                                                     \
-      done_ = true;                                                                        \
-    }                                                                                      \
-  } while (0)
+
 
 // One grouped GEMM launch: the LDS-DMA ring kernel when K % 32 == 0, else the
 // register-staged kernel (any K % 8 == 0).
@@ -740,10 +722,11 @@ void launch_gemm(const bf16* A, const bf16* A_lo, const int32_t* perm, int k, co
   constexpr int NTH = (BM / WM) * (BN / WN) * kWave;
   constexpr bool ALO = SPLIT && !G1;
   if (K % kRK == 0) {
+    constexpr int MODE = G1 ? kEpiGelu : kEpiGate;
     const size_t lds = (size_t)kRing * (BM + BN + (ALO ? BM : 0)) * kRowB;
-    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, WM, WN, G1, SPLIT>), lds);
-    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, G1, SPLIT>), dim3(grid), dim3(NTH), lds,
-                       st, A, A_lo, perm, k, W, bias, gate, tl, cnt, K, Nout, out, out_lo);
+    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT>), lds);
+    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT>), dim3(grid), dim3(NTH), lds,
+                       st, A, A_lo, perm, k, W, bias, gate, tl, cnt, K, Nout, out, out_lo, 0, 0);
   } else {
     const size_t lds = (size_t)2 * (BM + BN + (ALO ? BM : 0)) * kLdsRow * sizeof(bf16);
     MOE_SET_LDS_ONCE((gemm_bf16_kernel<BM, BN, WM, WN, G1, SPLIT>), lds);
@@ -771,20 +754,43 @@ hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, c
   return hipGetLastError();
 }
 
+// One decode GEMM: LDS-DMA stream kernel (+ split-K reduce) when K % 128 == 0,
+// else the direct-load kernel.
+template <bool G1, bool SPLIT>
+void launch_decode_gemm(bool dma, int nsplit, const bf16* X, const bf16* X_lo,
+                        const int32_t* perm, int k, const int32_t* off, const bf16* W,
+                        const bf16* bias, const float* gate, int K, int Nout, int N, void* out,
+                        bf16* out_lo, float* part, int S_cap, hipStream_t st) {
+  if (dma) {
+    using Geo = DecodeGeom<G1, SPLIT>;
+    const int nb = cdiv(Nout, kDWRows);
+    MOE_SET_LDS_ONCE((decode_dma_kernel<G1, SPLIT>), Geo::LDS);
+    hipLaunchKernelGGL((decode_dma_kernel<G1, SPLIT>), dim3(N * nb * nsplit), dim3(256), Geo::LDS,
+                       st, X, X_lo, perm, k, off, W, bias, gate, K, Nout, nb, nsplit, out, out_lo,
+                       part, S_cap);
+    if (nsplit > 1)
+      hipLaunchKernelGGL((decode_reduce_kernel<G1, SPLIT>), dim3(N * nb), dim3(256), 0, st, part,
+                         nsplit, S_cap, off, bias, gate, Nout, nb, out, out_lo);
+    return;
+  }
+  const int nb = cdiv(Nout, kDecRows);
+  hipLaunchKernelGGL((decode_bf16_kernel<G1, SPLIT>), dim3(N * nb), dim3(256), 0, st, X, X_lo,
+                     perm, k, off, W, bias, gate, K, Nout, nb, out, out_lo);
+}
+
 template <bool SPLIT>
 hipError_t launch_decode(const void* x, const int32_t* perm, const int32_t* off, const float* gate,
                          const void* W1, const void* b1, const void* W2, const void* b2, int d,
-                         int d_ff, int N, int k, void* hid, bf16* hid_lo, void* slot_out,
-                         hipStream_t st) {
-  const int nb1 = cdiv(d_ff, kDecRows), nb2 = cdiv(d, kDecRows);
+                         int d_ff, int N, int k, const Plan& pl, int S_cap, void* hid,
+                         bf16* hid_lo, float* part, void* slot_out, hipStream_t st) {
   profile_mark(3, st);
-  hipLaunchKernelGGL((decode_bf16_kernel<true, SPLIT>), dim3(N * nb1), dim3(256), 0, st,
-                     (const bf16*)x, nullptr, perm, k, off, (const bf16*)W1, (const bf16*)b1,
-                     nullptr, d, d_ff, nb1, hid, hid_lo);
+  launch_decode_gemm<true, SPLIT>(pl.dma1, pl.ks1, (const bf16*)x, nullptr, perm, k, off,
+                                  (const bf16*)W1, (const bf16*)b1, nullptr, d, d_ff, N, hid,
+                                  hid_lo, part, S_cap, st);
   profile_mark(4, st);
-  hipLaunchKernelGGL((decode_bf16_kernel<false, SPLIT>), dim3(N * nb2), dim3(256), 0, st,
-                     (const bf16*)hid, (const bf16*)hid_lo, perm, k, off, (const bf16*)W2,
-                     (const bf16*)b2, gate, d_ff, d, nb2, slot_out, nullptr);
+  launch_decode_gemm<false, SPLIT>(pl.dma2, pl.ks2, (const bf16*)hid, hid_lo, perm, k, off,
+                                   (const bf16*)W2, (const bf16*)b2, gate, d_ff, d, N, slot_out,
+                                   nullptr, part, S_cap, st);
   profile_mark(5, st);
   return hipGetLastError();
 }
@@ -800,6 +806,9 @@ void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max
   s->hidden_lo = pl.split ? (void*)c.take<bf16>(rows * d_ff) : nullptr;
   s->tiles = (int32_t*)c.take<int4>((size_t)(pl.max1 > 0 ? pl.max1 : 1) + (pl.max2 > 0 ? pl.max2 : 1));
   s->counts = c.take<int32_t>(4);
+  const size_t p1 = pl.ks1 > 1 ? (size_t)pl.ks1 * rows * d_ff : 0;
+  const size_t p2 = pl.ks2 > 1 ? (size_t)pl.ks2 * rows * d : 0;
+  s->part = (p1 | p2) ? c.take<float>(p1 > p2 ? p1 : p2) : nullptr;
 }
 
 hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* off,
@@ -814,10 +823,10 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
   bf16* lo = (bf16*)s.hidden_lo;
   if (pl.path == kPathDecode) {
     if (pl.split)
-      return launch_decode<true>(x, perm, off, gate, W1, b1, W2, b2, d, d_ff, N, k, s.hidden, lo,
-                                 slot_out, st);
-    return launch_decode<false>(x, perm, off, gate, W1, b1, W2, b2, d, d_ff, N, k, s.hidden,
-                                nullptr, slot_out, st);
+      return launch_decode<true>(x, perm, off, gate, W1, b1, W2, b2, d, d_ff, N, k, pl, S_max,
+                                 s.hidden, lo, s.part, slot_out, st);
+    return launch_decode<false>(x, perm, off, gate, W1, b1, W2, b2, d, d_ff, N, k, pl, S_max,
+                                s.hidden, nullptr, s.part, slot_out, st);
   }
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, off, N, pl.BM,
                      cdiv(d_ff, pl.BN1), cdiv(d, pl.BN2), pl.max1, pl.max2, t1, t2, s.counts);

@@ -55,6 +55,7 @@ struct ForwardWs {
   int32_t *perm, *inv;
   float* gate;
   void* slot_out;
+  void* wgt;  // transposed router weight
   DispatchScratch ds;
   FfnScratch fs;
   size_t bytes;
@@ -77,6 +78,7 @@ static void carve_forward(void* base, int T, int d, int d_ff, int N, int k, int 
   f->inv = c.take<int32_t>(P);
   f->gate = c.take<float>(P);
   f->slot_out = c.take<float>((size_t)(S_max > 0 ? S_max : 1) * d);
+  f->wgt = c.take<unsigned char>(route_scratch_bytes(d, N, dtype));
   carve_dispatch(c, T * k, N, &f->ds);
   carve_ffn(c, T, d, d_ff, N, k, C, S_max, dtype, flags, &f->fs);
   f->bytes = align_up(c.off, 256);
@@ -141,7 +143,7 @@ size_t moe_workspace_bytes(int T, int d, int d_ff, int N, int k, double capacity
 
 int moe_route(const void* x, const void* W_g, const float* logit_bias, int T, int d, int N, int k,
               int dtype, float* logits, int32_t* topk_idx, float* topk_w, double* topk_key,
-              void* stream) {
+              void* workspace, size_t ws_bytes, void* stream) {
   int st = check_shape(T, d, 8, N, k, dtype, false);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -149,8 +151,11 @@ int moe_route(const void* x, const void* W_g, const float* logit_bias, int T, in
   if (!aligned(x, 16) || !aligned(W_g, 16) || !aligned(logits, 4) || !aligned(topk_idx, 4) ||
       !aligned(topk_w, 4) || !aligned(topk_key, 8) || (logit_bias && !aligned(logit_bias, 4)))
     return MOE_ERR_UNSUPPORTED;
+  const size_t need = route_scratch_bytes(d, N, dtype);
+  if (need > 0 && (!workspace || !aligned(workspace, 256) || ws_bytes < need))
+    return MOE_ERR_WORKSPACE;
   return hip_status(launch_route(x, W_g, logit_bias, T, d, N, k, dtype, logits, topk_idx, topk_w,
-                                 topk_key, (hipStream_t)stream));
+                                 topk_key, workspace, (hipStream_t)stream));
 }
 
 int moe_dispatch(const int32_t* topk_idx, const float* topk_w, const double* topk_key, int T,
@@ -245,7 +250,8 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
   const int S_max = (int)((long long)T * k < (long long)N * C ? (long long)T * k : (long long)N * C);
   hipStream_t s = (hipStream_t)stream;
   profile_mark(0, s);
-  hipError_t e = launch_route(x, W_g, logit_bias, T, d, N, k, dtype, f.logits, f.idx, f.w, f.key, s);
+  hipError_t e =
+      launch_route(x, W_g, logit_bias, T, d, N, k, dtype, f.logits, f.idx, f.w, f.key, f.wgt, s);
   if (e != hipSuccess) return hip_status(e);
   profile_mark(1, s);
   e = launch_dispatch(f.idx, f.w, f.key, T, N, k, C, f.req, f.cnt, f.off, f.perm, f.inv, f.gate,

@@ -69,6 +69,25 @@ __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) 
 __host__ __device__ __forceinline__ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- host side
+// Raise a kernel's dynamic-LDS limit to all the LDS a workgroup may have
+// (160 KB on gfx950) minus its static LDS. Once per call site (idempotent; a
+// race between threads only repeats the call).
+inline void allow_max_dynamic_lds(const void* func) {
+  hipFuncAttributes a{};
+  if (hipFuncGetAttributes(&a, func) != hipSuccess) return;
+  const int limit = 160 * 1024 - (int)a.sharedSizeBytes;
+  (void)hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, limit);
+}
+#define MOE_SET_LDS_ONCE(kern, lds)                    \
+  do {                                                 \
+    static bool done_ = false;                         \
+    if (!done_) {                                      \
+      allow_max_dynamic_lds((const void*)(kern));      \
+      done_ = true;                                    \
+    }                                                  \
+    (void)(lds);                                       \
+  } while (0)
+
 // Capacity per the documented formula (moe.h).
 int capacity_host(int T, int N, int k, double cf);
 
@@ -103,6 +122,7 @@ struct FfnScratch {
   void* hidden_lo;    // [S_max, d_ff] bf16 residual of the hidden layer (split mode) or null
   int32_t* tiles;     // GEMM tile tables (int4 entries) for both GEMMs
   int32_t* counts;    // [4] tile counts written by the schedule kernel
+  float* part;        // split-K partial sums of the decode GEMMs, or null
 };
 constexpr int kFlagHiddenSplit = 1;  // MOE_FLAG_HIDDEN_SPLIT
 constexpr int kFlagYF32 = 2;         // MOE_FLAG_Y_F32
@@ -116,9 +136,10 @@ void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max
 void profile_mark(int slot, hipStream_t st);
 
 // Launchers (return hipError_t of the last launch).
+size_t route_scratch_bytes(int d, int N, int dtype);  // transposed router weight
 hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T, int d, int N,
                         int k, int dtype, float* logits, int32_t* idx, float* w, double* key,
-                        hipStream_t st);
+                        void* scratch, hipStream_t st);
 hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key, int T, int N,
                            int k, int C, int32_t* req, int32_t* cnt, int32_t* off, int32_t* perm,
                            int32_t* inv, float* gate, int32_t* n_dropped,

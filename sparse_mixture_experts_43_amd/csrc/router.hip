@@ -17,6 +17,7 @@
 // Phase 2: the block's logits sit in LDS (reusing the W_g staging space); one
 // wave per token row does k rounds of (value desc, index asc) argmax with
 // cross-lane butterflies, then the fp64 log-sum-exp and the gates.
+#include "gemm_ring.h"
 #include "moe_common.h"
 
 namespace moe {
@@ -27,7 +28,8 @@ constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- phase 2
 // Row r of the block's logits tile (LDS, row stride ls_stride floats).
-__device__ void topk_row(const float* __restrict__ Lrow, int N, int k, int t, float* __restrict__ logits,
+// `logits` may be null (the row is already in global memory).
+__device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, int k, int t, float* __restrict__ logits,
                          int32_t* __restrict__ idx, float* __restrict__ w, double* __restrict__ key) {
   const int l = lane_id();
   float v[kMaxN / kWave];
@@ -38,7 +40,7 @@ __device__ void topk_row(const float* __restrict__ Lrow, int N, int k, int t, fl
     v[i] = (n < N) ? Lrow[n] : -INFINITY;
     if (n < N) {
       m = fmaxf(m, v[i]);
-      logits[(size_t)t * N + n] = v[i];
+      if (logits != nullptr) logits[(size_t)t * N + n] = v[i];
     }
   }
   m = wave_max_f32(m);
@@ -54,54 +56,146 @@ __device__ void topk_row(const float* __restrict__ Lrow, int N, int k, int t, fl
   s = wave_sum_f64(s);
   const double lse = md + log(s);
 
-  // k rounds of argmax: larger value wins, equal values -> lower index.
+  // k rounds of argmax: larger value wins, equal values -> lower index. Lane j
+  // keeps pick j (value, expert, unnormalised probability); no local arrays,
+  // so nothing lands in scratch memory.
   unsigned taken = 0u;
-  float sel_v[kMaxK];
-  int sel_n[kMaxK];
+  float my_v = 0.f;
+  int my_n = 0;
+  double my_p = 0.0, psum = 0.0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bn = 0x7fffffff;
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k) {
-      float bv = -INFINITY;
-      int bn = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < kMaxN / kWave; ++i) {
-        const int n = l + kWave * i;
-        if (n < N && !((taken >> i) & 1u) && (v[i] > bv || bn == 0x7fffffff)) {
-          bv = v[i];
-          bn = n;
-        }
+    for (int i = 0; i < kMaxN / kWave; ++i) {
+      const int n = l + kWave * i;
+      if (n < N && !((taken >> i) & 1u) && (v[i] > bv || bn == 0x7fffffff)) {
+        bv = v[i];
+        bn = n;
       }
+    }
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = wave_shfl_xor(bv, o);
-        const int on = wave_shfl_xor(bn, o);
-        if (ov > bv || (ov == bv && on < bn)) {
-          bv = ov;
-          bn = on;
-        }
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = wave_shfl_xor(bv, o);
+      const int on = wave_shfl_xor(bn, o);
+      if (ov > bv || (ov == bv && on < bn)) {
+        bv = ov;
+        bn = on;
       }
-      if ((bn & (kWave - 1)) == l) taken |= 1u << (bn / kWave);
-      sel_v[j] = bv;
-      sel_n[j] = bn;
+    }
+    if ((bn & (kWave - 1)) == l) taken |= 1u << (bn / kWave);
+    const double pj = exp((double)bv - md);
+    psum += pj;
+    if (l == j) {
+      my_v = bv;
+      my_n = bn;
+      my_p = pj;
     }
   }
-  double psum = 0.0;
-  double p[kMaxK];
+  if (l < k) {
+    idx[(size_t)t * k + l] = my_n;
+    w[(size_t)t * k + l] = (float)(my_p / psum);
+    key[(size_t)t * k + l] = (double)my_v - lse;
+  }
+}
+
+
+// ---------------------------------------------------------------- W_g transpose
+// W_g [d, N] (N-contiguous) -> WgT [NP, d] (K-contiguous, rows n >= N zero), the
+// layout the MFMA B operand wants: 8 consecutive k of one expert per lane.
+__global__ __launch_bounds__(256) void transpose_wg_kernel(const bf16* __restrict__ Wg, int d, int N,
+                                                           int NP, bf16* __restrict__ WgT) {
+  __shared__ bf16 tile[64][66];
+  const int k0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int kk = i / 64, nn = i % 64;
+    const int kg = k0 + kk, ng = n0 + nn;
+    tile[kk][nn] = (kg < d && ng < N) ? Wg[(size_t)kg * N + ng] : (bf16)0.0f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int nn = i / 64, kk = i % 64;
+    const int kg = k0 + kk, ng = n0 + nn;
+    if (kg < d && ng < NP) WgT[(size_t)ng * d + kg] = tile[kk][nn];
+  }
+}
+
+// ---------------------------------------------------------------- skinny router
+// N <= 64 (at most 4 MFMA column tiles): one block = 16 tokens, its WAVES
+// waves split K; x rows and W_g^T rows stream straight from global memory
+// (W_g^T stays in L1/L2), four 32-wide K steps of loads in flight per wave.
+// Partial logits are summed across waves in a fixed order in LDS, then each
+// wave runs the top-k of some of the 16 rows.
+template <int WAVES, int NT>
+__global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ WgT, const float* __restrict__ bias,
+    int T, int d, int N, int k, float* __restrict__ logits, int32_t* __restrict__ idx,
+    float* __restrict__ w, double* __restrict__ key) {
+  constexpr int U = WAVES >= 16 ? 2 : 4;
+  constexpr int NP = NT * 16;
+  __shared__ float part[WAVES][16][NP];
+  __shared__ float Ls[16][NP + 4];
+  const int l = lane_id();
+  const int wv = threadIdx.x / kWave;
+  const int g = l >> 4, c16 = l & 15;
+  const int t0 = blockIdx.x * 16;
+  const int row = t0 + c16;
+  const bool rok = row < T;
+  const bf16* xr = x + (size_t)(rok ? row : 0) * d;
+  const int nsteps = cdiv(d, 32);
+  const int spw = cdiv(nsteps, WAVES);
+  const int s_begin = wv * spw, s_end = min(nsteps, s_begin + spw);
+  f32x4 acc[NT];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k) {
-      p[j] = exp((double)sel_v[j] - md);
-      psum += p[j];
-    }
-  }
+  for (int j = 0; j < NT; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  bf16x8 z;
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k && l == j) {
-      idx[(size_t)t * k + j] = sel_n[j];
-      w[(size_t)t * k + j] = (float)(p[j] / psum);
-      key[(size_t)t * k + j] = (double)sel_v[j] - lse;
+  for (int q = 0; q < 8; ++q) z[q] = (bf16)0.f;
+  for (int s0 = s_begin; s0 < s_end; s0 += U) {
+    bf16x8 a[U], b[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = (s0 + u) * 32 + 8 * g;
+      const bool ok = (s0 + u) < s_end && kk < d;
+      a[u] = (ok && rok) ? *(const bf16x8*)(xr + kk) : z;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        b[u][j] = ok ? *(const bf16x8*)(WgT + (size_t)(16 * j + c16) * d + kk) : z;
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][j], acc[j], 0, 0, 0);
   }
+  // D layout: lane holds column 16j + l%16, rows 4g + i
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[wv][4 * g + i][16 * j + c16] = acc[j][i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * NP; i += WAVES * 64) {
+    const int r = i / NP, n = i - r * NP;
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < WAVES; ++q) sum += part[q][r][n];
+    Ls[r][n] = sum + ((bias != nullptr && n < N) ? bias[n] : 0.f);
+  }
+  __syncthreads();
+  for (int r = wv; r < 16; r += WAVES) {
+    const int t = t0 + r;
+    if (t < T) topk_row(&Ls[r][0], N, k, t, logits, idx, w, key);
+  }
+}
+
+// ---------------------------------------------------------------- top-k over logits rows
+// One wave per token; the logits are already in global memory.
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int N, int k,
+                                                   int32_t* __restrict__ idx, float* __restrict__ w,
+                                                   double* __restrict__ key) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  topk_row(logits + (size_t)t * N, N, k, t, nullptr, idx, w, key);
 }
 
 // ---------------------------------------------------------------- bf16
@@ -267,38 +361,73 @@ hipError_t launch_bf16(const void* x, const void* W_g, const float* bias, int T,
   const size_t lds_w = (size_t)NP * (KC + 8) * sizeof(bf16);
   const size_t lds_l = (size_t)RT * (NP + 4) * sizeof(float);
   const size_t lds = lds_w > lds_l ? lds_w : lds_l;
-  static bool attr = false;
-  if (!attr) {
-    hipFuncSetAttribute((const void*)router_bf16_kernel<RT, KC>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr = true;
-  }
+  MOE_SET_LDS_ONCE((router_bf16_kernel<RT, KC>), 160 * 1024);
   hipLaunchKernelGGL((router_bf16_kernel<RT, KC>), dim3(cdiv(T, RT)), dim3(kThreads), lds, st,
                      (const bf16*)x, (const bf16*)W_g, bias, T, d, N, k, logits, idx, w, key);
   return hipGetLastError();
 }
 
+template <int NT>
+void launch_skinny(bool wide, const void* x, const bf16* WgT, const float* bias, int T, int d,
+                   int N, int k, float* logits, int32_t* idx, float* w, double* key,
+                   hipStream_t st) {
+  if (wide)
+    hipLaunchKernelGGL((router_skinny_kernel<16, NT>), dim3(cdiv(T, 16)), dim3(1024), 0, st,
+                       (const bf16*)x, WgT, bias, T, d, N, k, logits, idx, w, key);
+  else
+    hipLaunchKernelGGL((router_skinny_kernel<4, NT>), dim3(cdiv(T, 16)), dim3(256), 0, st,
+                       (const bf16*)x, WgT, bias, T, d, N, k, logits, idx, w, key);
+}
+
 }  // namespace
+
+size_t route_scratch_bytes(int d, int N, int dtype) {
+  if (dtype != kBF16) return 0;
+  const int NP = cdiv(N, 16) * 16;
+  return align_up((size_t)NP * d * sizeof(bf16), 256);
+}
 
 hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T, int d, int N,
                         int k, int dtype, float* logits, int32_t* idx, float* w, double* key,
-                        hipStream_t st) {
+                        void* scratch, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (dtype == kF32) {
     const int NP = cdiv(N, 16) * 16;
     const size_t lds = (16 * 32 + 32 * 256 + 16 * (NP + 4)) * sizeof(float);
-    static bool attr = false;
-    if (!attr) {
-      hipFuncSetAttribute((const void*)router_f32_kernel,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      attr = true;
-    }
+    MOE_SET_LDS_ONCE(router_f32_kernel, 160 * 1024);
     hipLaunchKernelGGL(router_f32_kernel, dim3(cdiv(T, 16)), dim3(kThreads), lds, st,
                        (const float*)x, (const float*)W_g, bias, T, d, N, k, logits, idx, w, key);
     return hipGetLastError();
   }
-  // Token rows per block: as many as the expert count allows (each wave holds
-  // at most 256 expert columns), fewer when that would leave CUs idle.
+  const int NP = cdiv(N, 16) * 16;
+  bf16* WgT = (bf16*)scratch;
+  hipLaunchKernelGGL(transpose_wg_kernel, dim3(cdiv(d, 64), cdiv(NP, 64)), dim3(256), 0, st,
+                     (const bf16*)W_g, d, N, NP, WgT);
+  if (NP <= 64) {
+    // few experts: K split over the waves of a block; more waves when T is small
+    const bool wide = T < 16 * 256;
+    switch (NP / 16) {
+      case 1: launch_skinny<1>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
+      case 2: launch_skinny<2>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
+      case 3: launch_skinny<3>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
+      default: launch_skinny<4>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
+    }
+    return hipGetLastError();
+  }
+  if (d % kRK == 0) {
+    // many experts: logits as a plain GEMM on the LDS-DMA ring, then top-k rows
+    constexpr int BM = 128, BN = 128;
+    const size_t lds = (size_t)kRing * (BM + BN) * kRowB;
+    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false>), lds);
+    const int grid = cdiv(T, BM) * cdiv(NP, BN);
+    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false>), dim3(grid), dim3(256),
+                       lds, st, (const bf16*)x, nullptr, nullptr, 1, WgT, (const bf16*)bias,
+                       nullptr, nullptr, nullptr, d, NP, (void*)logits, nullptr, T, N);
+    hipLaunchKernelGGL(topk_kernel, dim3(cdiv(T, 4)), dim3(256), 0, st, logits, T, N, k, idx, w,
+                       key);
+    return hipGetLastError();
+  }
+  // d not a multiple of 32: LDS-transposing kernel with fused top-k
   if (N <= 256 && T >= 64 * 256) return launch_bf16<64, 64>(x, W_g, bias, T, d, N, k, logits, idx, w, key, st);
   if (N <= 512 && T >= 32 * 256) return launch_bf16<32, 64>(x, W_g, bias, T, d, N, k, logits, idx, w, key, st);
   if (N <= 512) return launch_bf16<16, 64>(x, W_g, bias, T, d, N, k, logits, idx, w, key, st);

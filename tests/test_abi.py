@@ -73,21 +73,23 @@ def test_argument_checks_return_before_launch():
     p = ctypes.c_void_p(4096)  # never dereferenced: every call below is rejected first
     nul = None
     # k > N
-    assert raw.moe_route(p, p, nul, 4, 64, 4, 5, 1, p, p, p, p, nul) == -1
+    assert raw.moe_route(p, p, nul, 4, 64, 4, 5, 1, p, p, p, p, p, 1 << 20, nul) == -1
     # k > 16
-    assert raw.moe_route(p, p, nul, 4, 64, 32, 17, 1, p, p, p, p, nul) == -1
+    assert raw.moe_route(p, p, nul, 4, 64, 32, 17, 1, p, p, p, p, p, 1 << 20, nul) == -1
     # N > 1024
-    assert raw.moe_route(p, p, nul, 4, 64, 1025, 2, 1, p, p, p, p, nul) == -1
+    assert raw.moe_route(p, p, nul, 4, 64, 1025, 2, 1, p, p, p, p, p, 1 << 20, nul) == -1
     # d not a multiple of 8
-    assert raw.moe_route(p, p, nul, 4, 60, 8, 2, 1, p, p, p, p, nul) == -2
+    assert raw.moe_route(p, p, nul, 4, 60, 8, 2, 1, p, p, p, p, p, 1 << 20, nul) == -2
     # bad dtype
-    assert raw.moe_route(p, p, nul, 4, 64, 8, 2, 7, p, p, p, p, nul) == -2
+    assert raw.moe_route(p, p, nul, 4, 64, 8, 2, 7, p, p, p, p, p, 1 << 20, nul) == -2
     # null required pointer
-    assert raw.moe_route(nul, p, nul, 4, 64, 8, 2, 1, p, p, p, p, nul) == -1
+    assert raw.moe_route(nul, p, nul, 4, 64, 8, 2, 1, p, p, p, p, p, 1 << 20, nul) == -1
     # misaligned x
-    assert raw.moe_route(ctypes.c_void_p(4098), p, nul, 4, 64, 8, 2, 1, p, p, p, p, nul) == -2
+    assert raw.moe_route(ctypes.c_void_p(4098), p, nul, 4, 64, 8, 2, 1, p, p, p, p, p, 1 << 20, nul) == -2
     # T = 0 is a no-op success
-    assert raw.moe_route(nul, nul, nul, 0, 64, 8, 2, 1, nul, nul, nul, nul, nul) == 0
+    assert raw.moe_route(nul, nul, nul, 0, 64, 8, 2, 1, nul, nul, nul, nul, nul, 0, nul) == 0
+    # bf16 route without workspace
+    assert raw.moe_route(p, p, nul, 4, 64, 8, 2, 1, p, p, p, p, nul, 0, nul) == -3
     # workspace missing / too small / misaligned
     args = [p, p, p, 16, 8, 2, 1.0, p, p, p, p, p, p, p]
     assert raw.moe_dispatch(*args, nul, 0, nul) == -3

@@ -32,6 +32,10 @@ CASES = [
     ("decode_small", 32, 256, 384, 8, 2, 0.0, "bf16", False, "none", 0),
     ("decode_bias_ktail", 40, 200, 136, 8, 2, 0.0, "bf16", True, "none", 0),
     ("decode_split", 40, 200, 136, 8, 2, 0.0, "bf16", True, "none", SPLIT),
+    ("decode_splitk", 24, 512, 4096, 4, 2, 0.0, "bf16", True, "none", 0),
+    ("decode_splitk_hilo", 24, 512, 4096, 4, 2, 0.0, "bf16", True, "none", SPLIT),
+    ("decode_64_slots", 64, 256, 512, 2, 2, 0.0, "bf16", False, "none", 0),
+    ("decode_64_slots_hilo", 64, 256, 512, 2, 2, 0.0, "bf16", True, "normal0.5", SPLIT),
     ("tiledM_ragged", 600, 256, 320, 4, 2, 1.0, "bf16", False, "none", 0),
     ("tiledM_bias_ktail", 500, 200, 136, 3, 1, 0.0, "bf16", True, "none", 0),
     ("tiledM_split", 600, 256, 320, 4, 2, 1.0, "bf16", True, "none", SPLIT),
