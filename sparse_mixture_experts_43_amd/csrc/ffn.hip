@@ -724,9 +724,12 @@ void launch_gemm(const bf16* A, const bf16* A_lo, const int32_t* perm, int k, co
   if (K % kRK == 0) {
     constexpr int MODE = G1 ? kEpiGelu : kEpiGate;
     const size_t lds = (size_t)kRing * (BM + BN + (ALO ? BM : 0)) * kRowB;
-    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT>), lds);
-    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT>), dim3(grid), dim3(NTH), lds,
-                       st, A, A_lo, perm, k, W, bias, gate, tl, cnt, K, Nout, out, out_lo, 0, 0);
+    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, kRing>), lds);
+    const int pgrid = ring_grid((const void*)gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, kRing>,
+                                NTH, lds, grid);
+    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, kRing>), dim3(pgrid),
+                       dim3(NTH), lds, st, A, A_lo, perm, k, W, (const void*)bias, gate, tl, cnt, K,
+                       Nout, out, out_lo, 0, 0);
   } else {
     const size_t lds = (size_t)2 * (BM + BN + (ALO ? BM : 0)) * kLdsRow * sizeof(bf16);
     MOE_SET_LDS_ONCE((gemm_bf16_kernel<BM, BN, WM, WN, G1, SPLIT>), lds);

@@ -418,11 +418,13 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
     // many experts: logits as a plain GEMM on the LDS-DMA ring, then top-k rows
     constexpr int BM = 128, BN = 128;
     const size_t lds = (size_t)kRing * (BM + BN) * kRowB;
-    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false>), lds);
-    const int grid = cdiv(T, BM) * cdiv(NP, BN);
-    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false>), dim3(grid), dim3(256),
-                       lds, st, (const bf16*)x, nullptr, nullptr, 1, WgT, (const bf16*)bias,
-                       nullptr, nullptr, nullptr, d, NP, (void*)logits, nullptr, T, N);
+    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false, kRing>), lds);
+    const int grid = ring_grid((const void*)gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false, kRing>,
+                               256, lds, cdiv(T, BM) * cdiv(NP, BN));
+    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false, kRing>), dim3(grid),
+                       dim3(256), lds, st, (const bf16*)x, nullptr, nullptr, 1, WgT,
+                       (const void*)bias, nullptr, nullptr, nullptr, d, NP, (void*)logits, nullptr,
+                       T, N);
     hipLaunchKernelGGL(topk_kernel, dim3(cdiv(T, 4)), dim3(256), 0, st, logits, T, N, k, idx, w,
                        key);
     return hipGetLastError();
