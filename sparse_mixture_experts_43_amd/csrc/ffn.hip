@@ -713,23 +713,49 @@ Plan make_plan(int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype
 
 
 
-// One grouped GEMM launch: the LDS-DMA ring kernel when K % 32 == 0, else the
-// register-staged kernel (any K % 8 == 0).
+// Largest persistent grid a ring GEMM of this shape is launched with (and the
+// split-tail partial buffer is sized for): the workgroups that fit in LDS on
+// 256 CUs, at most one per tile, a multiple of 8.
+constexpr int kRingCUs = 256;
+int ring_grid_bound(int BM, int BN, bool alo, int max_tiles) {
+  const int lds = kRing * (BM + BN + (alo ? BM : 0)) * kRowB;
+  int occ = (160 * 1024) / lds;
+  occ = occ < 1 ? 1 : occ;
+  const int g = cdiv(max_tiles > 0 ? max_tiles : 1, 8) * 8;
+  return g < kRingCUs * occ ? g : kRingCUs * occ;
+}
+
+// fp32 partial tiles of a ring GEMM's split tail (2 per workgroup)
+size_t ring_part_floats(int BM, int BN, bool alo, int max_tiles) {
+  return (size_t)ring_grid_bound(BM, BN, alo, max_tiles) * 2 * BM * BN;
+}
+
+// One grouped GEMM launch: the LDS-DMA ring kernel (+ the reduction of its
+// split tail) when K % 32 == 0, else the register-staged kernel (any K % 8 == 0).
 template <int BM, int BN, int WM, int WN, bool G1, bool SPLIT>
 void launch_gemm(const bf16* A, const bf16* A_lo, const int32_t* perm, int k, const bf16* W,
                  const bf16* bias, const float* gate, const int4* tl, const int32_t* cnt, int K,
-                 int Nout, int grid, void* out, bf16* out_lo, hipStream_t st) {
+                 int Nout, int grid, void* out, bf16* out_lo, float* part, hipStream_t st) {
   constexpr int NTH = (BM / WM) * (BN / WN) * kWave;
   constexpr bool ALO = SPLIT && !G1;
   if (K % kRK == 0) {
     constexpr int MODE = G1 ? kEpiGelu : kEpiGate;
     const size_t lds = (size_t)kRing * (BM + BN + (ALO ? BM : 0)) * kRowB;
     MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, kRing>), lds);
-    const int pgrid = ring_grid((const void*)gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, kRing>,
-                                NTH, lds, grid);
+    int pgrid = ring_grid((const void*)gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, kRing>, NTH,
+                          lds, grid);
+    const int bound = ring_grid_bound(BM, BN, ALO, grid);
+    pgrid = pgrid < bound ? pgrid : bound;
     hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, kRing>), dim3(pgrid),
                        dim3(NTH), lds, st, A, A_lo, perm, k, W, (const void*)bias, gate, tl, cnt, K,
-                       Nout, out, out_lo, 0, 0);
+                       Nout, out, out_lo, 0, 0, part);
+    if (part != nullptr) {
+      // at most per-1 tail tiles per XCD, BM*BN/4/256 group blocks each
+      const int work = 8 * (pgrid / 8) * (BM * BN / 4 / kReduceThreads);
+      hipLaunchKernelGGL((ring_reduce_kernel<BM, BN, WM, WN, MODE, SPLIT>),
+                         dim3(work < 4096 ? work : 4096), dim3(kReduceThreads), 0, st, part, pgrid,
+                         (const void*)bias, gate, tl, cnt, K, Nout, out, out_lo);
+    }
   } else {
     const size_t lds = (size_t)2 * (BM + BN + (ALO ? BM : 0)) * kLdsRow * sizeof(bf16);
     MOE_SET_LDS_ONCE((gemm_bf16_kernel<BM, BN, WM, WN, G1, SPLIT>), lds);
@@ -742,17 +768,17 @@ template <int BM, int BN, int WM, int WN, bool SPLIT>
 hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, const void* W1,
                         const void* b1, const void* W2, const void* b2, int d, int d_ff, int k,
                         const Plan& pl, void* hid, bf16* hid_lo, const int4* t1, const int4* t2,
-                        const int32_t* cnts, void* slot_out, hipStream_t st) {
+                        const int32_t* cnts, void* slot_out, float* part, hipStream_t st) {
   const int g1 = cdiv(pl.max1 > 0 ? pl.max1 : 1, 8) * 8;
   const int g2 = cdiv(pl.max2 > 0 ? pl.max2 : 1, 8) * 8;
   profile_mark(3, st);
   launch_gemm<BM, BN, WM, WN, true, SPLIT>((const bf16*)x, nullptr, perm, k, (const bf16*)W1,
                                            (const bf16*)b1, nullptr, t1, cnts + 0, d, d_ff, g1,
-                                           hid, hid_lo, st);
+                                           hid, hid_lo, part, st);
   profile_mark(4, st);
   launch_gemm<BM, BN, WM, WN, false, SPLIT>((const bf16*)hid, hid_lo, nullptr, k,
                                             (const bf16*)W2, (const bf16*)b2, gate, t2, cnts + 1,
-                                            d_ff, d, g2, slot_out, nullptr, st);
+                                            d_ff, d, g2, slot_out, nullptr, part, st);
   profile_mark(5, st);
   return hipGetLastError();
 }
@@ -809,9 +835,17 @@ void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max
   s->hidden_lo = pl.split ? (void*)c.take<bf16>(rows * d_ff) : nullptr;
   s->tiles = (int32_t*)c.take<int4>((size_t)(pl.max1 > 0 ? pl.max1 : 1) + (pl.max2 > 0 ? pl.max2 : 1));
   s->counts = c.take<int32_t>(4);
-  const size_t p1 = pl.ks1 > 1 ? (size_t)pl.ks1 * rows * d_ff : 0;
-  const size_t p2 = pl.ks2 > 1 ? (size_t)pl.ks2 * rows * d : 0;
-  s->part = (p1 | p2) ? c.take<float>(p1 > p2 ? p1 : p2) : nullptr;
+  // decode: split-K partials; tiled bf16 on the ring: split-tail partial tiles
+  size_t pn = 0;
+  if (pl.path == kPathDecode) {
+    const size_t p1 = pl.ks1 > 1 ? (size_t)pl.ks1 * rows * d_ff : 0;
+    const size_t p2 = pl.ks2 > 1 ? (size_t)pl.ks2 * rows * d : 0;
+    pn = p1 > p2 ? p1 : p2;
+  } else if (pl.path == kPathTiledL || pl.path == kPathTiledM) {
+    const int mx = pl.max1 > pl.max2 ? pl.max1 : pl.max2;
+    pn = ring_part_floats(pl.BM, pl.BN1, false, mx);
+  }
+  s->part = pn ? c.take<float>(pn) : nullptr;
 }
 
 hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* off,
@@ -848,12 +882,14 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
   if (pl.path == kPathTiledL)
     return launch_tiled<256, 256, 128, 128, false>(x, perm, gate, W1, b1, W2, b2, d, d_ff, k, pl,
                                                     s.hidden, nullptr, t1, t2, s.counts, slot_out,
-                                                    st);
+                                                    s.part, st);
   if (pl.split)
     return launch_tiled<128, 128, 64, 64, true>(x, perm, gate, W1, b1, W2, b2, d, d_ff, k, pl,
-                                                 s.hidden, lo, t1, t2, s.counts, slot_out, st);
+                                                 s.hidden, lo, t1, t2, s.counts, slot_out, s.part,
+                                                 st);
   return launch_tiled<128, 128, 64, 64, false>(x, perm, gate, W1, b1, W2, b2, d, d_ff, k, pl,
-                                                s.hidden, nullptr, t1, t2, s.counts, slot_out, st);
+                                                s.hidden, nullptr, t1, t2, s.counts, slot_out,
+                                                s.part, st);
 }
 
 }  // namespace moe

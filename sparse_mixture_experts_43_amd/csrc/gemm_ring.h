@@ -104,15 +104,128 @@ inline int ring_grid(const void* kernel, int threads, size_t lds, int max_tiles)
   return (int)((g + 7) / 8 * 8);
 }
 
+// Work split of a persistent launch. XCD x (workgroups b with b % 8 == x)
+// owns the tiles [x*chunk, x*chunk + cx) of the list; its `per` workgroups
+// take them in whole rounds (workgroup j: tiles j, j+per, ...), and when a
+// last partial round of L < per tiles remains and split partials are enabled,
+// its L*nk stage units are cut into `per` equal contiguous ranges (one per
+// workgroup, each touching at most two tiles), whose fp32 partial tiles
+// ring_reduce_kernel sums in a fixed order: every tile still costs at most
+// one round plus one share of the tail.
+struct RingSplit {
+  int chunk, cx, per, rounds, tail;
+  __device__ __forceinline__ RingSplit(int ntiles, int xcd, int grid, bool split_tail) {
+    per = grid >> 3;
+    chunk = (ntiles + 7) >> 3;
+    cx = ntiles - xcd * chunk;
+    cx = cx < 0 ? 0 : (cx > chunk ? chunk : cx);
+    rounds = cx / per;
+    tail = cx - rounds * per;
+    // split only a short tail: a tail of more than half a round costs about a
+    // round anyway once its partials are written and reduced
+    if (tail > 0 && (!split_tail || 2 * tail > per)) {
+      rounds += 1;  // whole tiles only: the last round is partly idle
+      tail = 0;
+    }
+  }
+  // first stage unit of workgroup j's share of the split tail (32-bit math:
+  // j <= per <= 128, tail < per and nk <= 2048 keep the product below 2^25)
+  __device__ __forceinline__ int lo(int j, int nk) const {
+    return (int)((unsigned)(j * tail * nk) / (unsigned)per);
+  }
+};
+
+// Epilogue of one tile from the accumulators (lane: token row lr of block i,
+// output columns 8q + 4*half + r of block j).
+template <int BM, int BN, int WM, int WN, int MODE, bool SPLIT>
+__device__ __forceinline__ void ring_epilogue(const f32x16 (&acc)[WM / 32][WN / 32], int e,
+                                              int m0, int mcount, int n0, int wr, int wn0,
+                                              int lr, int half, const void* __restrict__ bias,
+                                              const float* __restrict__ gate, int Nout,
+                                              void* __restrict__ out, bf16* __restrict__ out_lo,
+                                              int ldo) {
+  constexpr bool G1 = MODE == kEpiGelu;
+  constexpr int MT = WM / 32, NTW = WN / 32;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int r = (2 * i + wr) * 32 + lr;  // token blocks alternate between the wave rows
+    if (r >= mcount) continue;
+    const int slot = m0 + r;
+    float g = 1.f;
+    if constexpr (MODE == kEpiGate) g = gate[slot];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn0 + j * 32 + 8 * q + 4 * half;
+        float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+        float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        if constexpr (MODE == kEpiLogit) {
+          const float* bf = (const float*)bias;
+          float* o = (float*)out + (size_t)slot * ldo;
+          if (col + 0 < ldo) o[col + 0] = v0 + (bf ? bf[col + 0] : 0.f);
+          if (col + 1 < ldo) o[col + 1] = v1 + (bf ? bf[col + 1] : 0.f);
+          if (col + 2 < ldo) o[col + 2] = v2 + (bf ? bf[col + 2] : 0.f);
+          if (col + 3 < ldo) o[col + 3] = v3 + (bf ? bf[col + 3] : 0.f);
+          continue;
+        }
+        if (col >= Nout) continue;  // Nout % 4 == 0: a group is all in or all out
+        if (bias != nullptr) {
+          const uint2 bb = *(const uint2*)((const bf16*)bias + (size_t)e * Nout + col);
+          v0 += __builtin_bit_cast(float, bb.x << 16);
+          v1 += __builtin_bit_cast(float, bb.x & 0xFFFF0000u);
+          v2 += __builtin_bit_cast(float, bb.y << 16);
+          v3 += __builtin_bit_cast(float, bb.y & 0xFFFF0000u);
+        }
+        const size_t o = (size_t)slot * Nout + col;
+        if constexpr (G1) {
+          const float h0 = gelu_as(v0), h1 = gelu_as(v1), h2 = gelu_as(v2), h3 = gelu_as(v3);
+          const uint2 hi = make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
+          *(uint2*)((bf16*)out + o) = hi;
+          if constexpr (SPLIT) {
+            const float r0 = h0 - __builtin_bit_cast(float, hi.x << 16);
+            const float r1 = h1 - __builtin_bit_cast(float, hi.x & 0xFFFF0000u);
+            const float r2 = h2 - __builtin_bit_cast(float, hi.y << 16);
+            const float r3 = h3 - __builtin_bit_cast(float, hi.y & 0xFFFF0000u);
+            *(uint2*)(out_lo + o) = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
+          }
+        } else {
+          *(f32x4*)((float*)out + o) = f32x4{v0 * g, v1 * g, v2 * g, v3 * g};
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, int BM, int BN>
+__device__ __forceinline__ void ring_decode_tile(int tile, const int4* __restrict__ tiles,
+                                                 int M_total, int Nout, int& e, int& m0,
+                                                 int& mcount, int& n0) {
+  if constexpr (MODE == kEpiLogit) {
+    const int ntn = (Nout + BN - 1) / BN;  // n-tiles fastest
+    const int mt = tile / ntn;
+    e = 0;
+    m0 = mt * BM;
+    mcount = min(BM, M_total - m0);
+    n0 = (tile - mt * ntn) * BN;
+  } else {
+    const int4 te = tiles[tile];
+    e = te.x; m0 = te.y; mcount = te.z; n0 = te.w * BN;
+  }
+}
+
+// part: fp32 partial tiles of the split tail (2 per workgroup, BM*BN each) or
+// NULL (whole tiles only).
 template <int BM, int BN, int WM, int WN, int MODE, bool SPLIT, int RING>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ A_lo, const int32_t* __restrict__ perm,
     int kpairs, const bf16* __restrict__ W, const void* __restrict__ bias,
     const float* __restrict__ gate, const int4* __restrict__ tiles,
     const int32_t* __restrict__ ntiles_p, int K, int Nout, void* __restrict__ out,
-    bf16* __restrict__ out_lo, int M_total, int ldo) {
+    bf16* __restrict__ out_lo, int M_total, int ldo, float* __restrict__ part) {
   constexpr bool G1 = MODE == kEpiGelu;
   constexpr int NW = (BM / WM) * (BN / WN);
+  constexpr int NTH = NW * kWave;
   constexpr int MT = WM / 32, NTW = WN / 32;
   constexpr bool ALO = SPLIT && !G1;
   constexpr int AI = BM / (NW * 16);  // A wave-loads per stage
@@ -124,39 +237,55 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   constexpr int STAGE = L_OFF + (ALO ? BM * kRowB : 0);
   static_assert(AI >= 1 && BI >= 1, "tile too small for the wave count");
   static_assert(RING >= 3 && (RING - 2) * LPS < 64, "ring depth / vmcnt range");
+  static_assert(BM / WM == 2, "two wave rows (token blocks alternate between them)");
 
   extern __shared__ __align__(16) unsigned char smem[];
 
-  // ---- this workgroup's share of the tile list
+  // ---- this workgroup's items: whole tiles, then at most two tail segments
   int ntiles;
   if constexpr (MODE == kEpiLogit) {
     ntiles = ((M_total + BM - 1) / BM) * ((Nout + BN - 1) / BN);
   } else {
     ntiles = *ntiles_p;
   }
+  const int nk = K / kRK;
   const int xcd = blockIdx.x & 7;
-  const int per = gridDim.x >> 3;
-  const int chunk = (ntiles + 7) >> 3;
-  int jt = blockIdx.x >> 3;
-  if (jt >= chunk || xcd * chunk + jt >= ntiles) return;
-
-  auto decode = [&](int tile, int& e, int& m0, int& mcount, int& n0) {
-    if constexpr (MODE == kEpiLogit) {
-      const int ntn = (Nout + BN - 1) / BN;  // n-tiles fastest
-      const int mt = tile / ntn;
-      e = 0;
-      m0 = mt * BM;
-      mcount = min(BM, M_total - m0);
-      n0 = (tile - mt * ntn) * BN;
+  const int jw = blockIdx.x >> 3;
+  const RingSplit sp(ntiles, xcd, gridDim.x, part != nullptr);
+  int n_whole = sp.rounds;  // whole tiles jw + r*per that exist
+  if (n_whole > 0 && jw + (n_whole - 1) * sp.per >= sp.cx) n_whole -= 1;
+  int t_lo = 0, t_hi = 0;
+  int seg0 = 0, n_seg = 0;
+  if (sp.tail > 0) {
+    t_lo = sp.lo(jw, nk);
+    t_hi = sp.lo(jw + 1, nk);
+    if (t_hi > t_lo) {
+      seg0 = t_lo / nk;
+      n_seg = (t_hi - 1) / nk - seg0 + 1;
+    }
+  }
+  const int n_items = n_whole + n_seg;
+  if (n_items == 0) return;
+  const int base_tile = xcd * sp.chunk;
+  // item it -> tile, stage range [kb, ke), partial slot (-1: whole tile)
+  auto item = [&](int it, int& tile, int& kb, int& ke, int& ps) {
+    if (it < n_whole) {
+      tile = base_tile + jw + it * sp.per;
+      kb = 0; ke = nk; ps = -1;
     } else {
-      const int4 te = tiles[tile];
-      e = te.x; m0 = te.y; mcount = te.z; n0 = te.w * BN;
+      const int q = it - n_whole;
+      const int tau = seg0 + q;
+      tile = base_tile + sp.rounds * sp.per + tau;
+      const int u0 = tau * nk;
+      kb = (t_lo > u0 ? t_lo : u0) - u0;
+      ke = (t_hi < u0 + nk ? t_hi : u0 + nk) - u0;
+      ps = (int)blockIdx.x * 2 + q;
     }
   };
 
   const int l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wm0 = (wv / (BN / WN)) * WM;
+  const int wr = wv / (BN / WN);  // wave row: token blocks wr, wr+2, wr+4, ... of the tile
   const int wn0 = (wv % (BN / WN)) * WN;
 
   // DMA source pointers: wave-load i covers tile rows (i*NW + wv)*16 .. +16;
@@ -184,31 +313,31 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
     }
   };
   MOE_LDS unsigned char* lds = (MOE_LDS unsigned char*)smem;
-  const int nk = K / kRK;
+  int kb = 0, nks = 0;  // stage range of the current item: [kb, kb + nks)
   // A stage's copies go out in two parts: part 0 (token rows, and their
   // residual rows) right after the mid-stage barrier, part 1 (weight rows) in
   // the first half of the next ring step, so the vector-memory issue is spread
   // over the whole step instead of bursting.
-  auto issue_part = [&](int kt, int part) {
-    const int src_kt = kt < nk ? kt : nk - 1;  // past the last stage: a dead copy
+  auto issue_part = [&](int kt, int prt) {
+    const int src_kt = kb + (kt < nks ? kt : nks - 1);  // past the last stage: a dead copy
     MOE_LDS unsigned char* st = lds + (kt % RING) * STAGE;
-    const int kb = src_kt * kRowB;
-    if (part == 0) {
+    const int kbyte = src_kt * kRowB;
+    if (prt == 0) {
 #pragma unroll
       for (int i = 0; i < AI; ++i)
-        dma16(pa[i] + kb, st + A_OFF + (i * NW + wv) * 1024);
+        dma16(pa[i] + kbyte, st + A_OFF + (i * NW + wv) * 1024);
       if constexpr (ALO) {
 #pragma unroll
         for (int i = 0; i < AI; ++i)
-          dma16(pl[i] + kb, st + L_OFF + (i * NW + wv) * 1024);
+          dma16(pl[i] + kbyte, st + L_OFF + (i * NW + wv) * 1024);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < BI; ++i)
-        dma16(pb[i] + kb, st + B_OFF + (i * NW + wv) * 1024);
+        dma16(pb[i] + kbyte, st + B_OFF + (i * NW + wv) * 1024);
     }
   };
-  // prologue of a tile: stages 0 .. RING-3 whole, stage RING-2 part 0
+  // prologue of an item: stages 0 .. RING-3 whole, stage RING-2 part 0
   auto issue_prologue = [&]() {
 #pragma unroll
     for (int q = 0; q < RING - 2; ++q) {
@@ -223,7 +352,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   const int half = l >> 5;
   int aoffs[MT], boffs[NTW];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) aoffs[i] = (wm0 + i * 32 + lr) * kRowB;
+  for (int i = 0; i < MT; ++i) aoffs[i] = ((2 * i + wr) * 32 + lr) * kRowB;
 #pragma unroll
   for (int j = 0; j < NTW; ++j) boffs[j] = (wn0 + j * 32 + lr) * kRowB;
   const int sw = (lr >> 2) & 3;  // (R >> 2) & 3 with R = 32*x + lr
@@ -231,50 +360,97 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   const int pos1 = ((2 + half) ^ sw) * 16;  // ks = 1
 
   bf16x8 af[2][MT], bfr[2][NTW], alf[ALO ? 2 : 1][ALO ? MT : 1];
-  // RAG: a partly filled tile; token blocks i >= na (rows past mcount) are
-  // neither read nor multiplied (na is uniform per wave).
-  int na = MT;
-  auto read_frags = [&](int kt, int ks, int set, auto rag) {
-    constexpr bool RAG = decltype(rag)::value;
+  // NA: token blocks of this wave that hold rows of the tile (a partly filled
+  // tile skips the fragment reads and MFMAs of the empty ones)
+  auto read_frags = [&](int kt, int ks, int set, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
     const unsigned char* st = smem + (kt % RING) * STAGE;
     const int pos = ks ? pos1 : pos0;
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-      if (!RAG || i < na) af[set][i] = *(const bf16x8*)(st + A_OFF + aoffs[i] + pos);
+    for (int i = 0; i < NA; ++i) af[set][i] = *(const bf16x8*)(st + A_OFF + aoffs[i] + pos);
 #pragma unroll
     for (int j = 0; j < NTW; ++j) bfr[set][j] = *(const bf16x8*)(st + B_OFF + boffs[j] + pos);
     if constexpr (ALO) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        if (!RAG || i < na) alf[set][i] = *(const bf16x8*)(st + L_OFF + aoffs[i] + pos);
+      for (int i = 0; i < NA; ++i) alf[set][i] = *(const bf16x8*)(st + L_OFF + aoffs[i] + pos);
     }
   };
 
   // acc[i][j]: token block i x weight block j; lane holds token row lr and
   // output columns 8*q + 4*half + r (r = 0..3) at acc[i][j][4*q + r].
   f32x16 acc[MT][NTW];
-  auto mma = [&](int set, auto rag) {
-    constexpr bool RAG = decltype(rag)::value;
+  auto mma = [&](int set, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-      if (!RAG || i < na) {
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
-      }
+      for (int j = 0; j < NTW; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
     if constexpr (ALO) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        if (!RAG || i < na) {
+      for (int i = 0; i < NA; ++i)
 #pragma unroll
-          for (int j = 0; j < NTW; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], alf[set][i], acc[i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < NTW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], alf[set][i], acc[i][j], 0, 0, 0);
     }
   };
 
-  int e, m0, mcount, n0;
-  decode(xcd * chunk + jt, e, m0, mcount, n0);
+  // the ring steps of one item, for NA active token blocks
+  auto kloop = [&](auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
+    constexpr int NR = NA + NTW + (ALO ? NA : 0);  // fragment reads per half step
+    read_frags(0, 0, 0, na_c);
+    for (int kt = 0; kt < nks; ++kt) {
+      // fragments (kt, ks=0) are in set 0
+      read_frags(kt, 1, 1, na_c);
+      issue_part(kt + RING - 2, 1);
+      mma(0, na_c);
+      // the (kt, ks=1) fragment reads between the first MFMAs, then the
+      // weight-row copies of stage kt+RING-2
+      if constexpr (NA > 0) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < BI; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // stage kt+1 has landed (only the stages issued after it may still fly)
+      // and no wave still reads the slot of stage kt-1
+      lgkm_wait0();
+      vm_wait_n<(RING - 3) * LPS>();
+      wg_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(kt + 1, 0, 0, na_c);  // past the last stage: reads a dead slot, never used
+      issue_part(kt + RING - 1, 0);
+      mma(1, na_c);
+      // one MFMA, one fragment read of the next stage (so the reads land long
+      // before the next step needs them), then one MFMA, one token-row copy
+      if constexpr (NA > 0) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < LPS - BI; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  int tile, ke, ps, e, m0, mcount, n0;
+  item(0, tile, kb, ke, ps);
+  nks = ke - kb;
+  ring_decode_tile<MODE, BM, BN>(tile, tiles, M_total, Nout, e, m0, mcount, n0);
   set_ptrs(e, m0, mcount, n0);
   // Every ring step issues exactly LPS loads per wave (part 1 of stage
   // kt+RING-2, then part 0 of stage kt+RING-1; past the last stage the copies
@@ -283,8 +459,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   // means stage kt+1 has landed.
   issue_prologue();
 
-  while (true) {
-    vm_wait_n<0>();  // this tile's first stages (and the last tile's stores)
+  for (int it = 0;;) {
+    vm_wait_n<0>();  // this item's first stages (and the last item's stores)
     wg_barrier();
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -292,121 +468,141 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
       for (int j = 0; j < NTW; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-    auto kloop = [&](auto rag) {
-      constexpr bool RAG = decltype(rag)::value;
-      read_frags(0, 0, 0, rag);
-      for (int kt = 0; kt < nk; ++kt) {
-        // fragments (kt, ks=0) are in set 0
-        read_frags(kt, 1, 1, rag);
-        issue_part(kt + RING - 2, 1);
-        mma(0, rag);
-        if constexpr (!RAG) {
-          // issue the (kt, ks=1) fragment reads between the first MFMAs, then
-          // the weight-row copies of stage kt+RING-2
-#pragma unroll
-          for (int q = 0; q < MT + NTW + (ALO ? MT : 0); ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-#pragma unroll
-          for (int q = 0; q < BI; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          }
+    {
+      // token blocks of this wave row with rows below mcount
+      const int nb = (mcount + 31) / 32;
+      int na = (nb - wr + 1) / 2;
+      na = __builtin_amdgcn_readfirstlane(na < 0 ? 0 : (na > MT ? MT : na));
+      if (na >= MT) {
+        kloop(std::integral_constant<int, MT>{});
+      } else if constexpr (MT == 4) {
+        switch (na) {
+          case 3: kloop(std::integral_constant<int, 3>{}); break;
+          case 2: kloop(std::integral_constant<int, 2>{}); break;
+          case 1: kloop(std::integral_constant<int, 1>{}); break;
+          default: kloop(std::integral_constant<int, 0>{}); break;
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // stage kt+1 has landed (only the stages issued after it may still fly)
-        // and no wave still reads the slot of stage kt-1
-        lgkm_wait0();
-        vm_wait_n<(RING - 3) * LPS>();
-        wg_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(kt + 1, 0, 0, rag);  // past the last stage: reads a dead slot, never used
-        issue_part(kt + RING - 1, 0);
-        mma(1, rag);
-        if constexpr (!RAG) {
-          // interleave: one MFMA, one fragment read of the next stage (so the
-          // reads land long before the next iteration needs them), then one
-          // MFMA, one token-row copy of stage kt+RING-1
-#pragma unroll
-          for (int q = 0; q < MT + NTW + (ALO ? MT : 0); ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-#pragma unroll
-          for (int q = 0; q < LPS - BI; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      } else if constexpr (MT == 2) {
+        if (na == 1) kloop(std::integral_constant<int, 1>{});
+        else kloop(std::integral_constant<int, 0>{});
+      } else {
+        kloop(std::integral_constant<int, MT>{});
       }
-    };
-    kloop(std::false_type{});
-    // all copies (the dead ones too) have landed: the ring is free for the next tile
+    }
+    // all copies (the dead ones too) have landed: the ring is free
     vm_wait_n<0>();
 
-    // ---- next tile: request its first stages before this tile's epilogue
-    const int ce = e, cm0 = m0, cmcount = mcount, cn0 = n0;
-    jt += per;
-    const bool more = jt < chunk && xcd * chunk + jt < ntiles;
+    // ---- next item: request its first stages before this item's epilogue
+    const int ce = e, cm0 = m0, cmcount = mcount, cn0 = n0, cps = ps;
+    ++it;
+    const bool more = it < n_items;
     if (more) {
-      decode(xcd * chunk + jt, e, m0, mcount, n0);
+      item(it, tile, kb, ke, ps);
+      nks = ke - kb;
+      ring_decode_tile<MODE, BM, BN>(tile, tiles, M_total, Nout, e, m0, mcount, n0);
       set_ptrs(e, m0, mcount, n0);
       issue_prologue();
     }
 
-    // ---- epilogue of the tile just finished
+    if (cps < 0) {
+      ring_epilogue<BM, BN, WM, WN, MODE, SPLIT>(acc, ce, cm0, cmcount, cn0, wr, wn0, lr, half,
+                                                 bias, gate, Nout, out, out_lo, ldo);
+    } else {
+      // raw partial accumulators as float4 groups (4 consecutive output
+      // columns of one lane), lane-major so every store is one contiguous 1 KB
+      f32x4* pp = (f32x4*)(part + (size_t)cps * (BM * BN)) + threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int r = wm0 + i * 32 + lr;
-      if (r >= cmcount) continue;
-      const int slot = cm0 + r;
-      float g = 1.f;
-      if constexpr (MODE == kEpiGate) g = gate[slot];
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) {
+        for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = cn0 + wn0 + j * 32 + 8 * q + 4 * half;
-          float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-          float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-          if constexpr (MODE == kEpiLogit) {
-            const float* bf = (const float*)bias;
-            float* o = (float*)out + (size_t)slot * ldo;
-            if (col + 0 < ldo) o[col + 0] = v0 + (bf ? bf[col + 0] : 0.f);
-            if (col + 1 < ldo) o[col + 1] = v1 + (bf ? bf[col + 1] : 0.f);
-            if (col + 2 < ldo) o[col + 2] = v2 + (bf ? bf[col + 2] : 0.f);
-            if (col + 3 < ldo) o[col + 3] = v3 + (bf ? bf[col + 3] : 0.f);
-            continue;
-          }
-          if (col >= Nout) continue;  // Nout % 4 == 0: a group is all in or all out
-          if (bias != nullptr) {
-            const uint2 bb = *(const uint2*)((const bf16*)bias + (size_t)ce * Nout + col);
-            v0 += __builtin_bit_cast(float, bb.x << 16);
-            v1 += __builtin_bit_cast(float, bb.x & 0xFFFF0000u);
-            v2 += __builtin_bit_cast(float, bb.y << 16);
-            v3 += __builtin_bit_cast(float, bb.y & 0xFFFF0000u);
-          }
-          const size_t o = (size_t)slot * Nout + col;
-          if constexpr (G1) {
-            const float h0 = gelu_as(v0), h1 = gelu_as(v1), h2 = gelu_as(v2), h3 = gelu_as(v3);
-            const uint2 hi = make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
-            *(uint2*)((bf16*)out + o) = hi;
-            if constexpr (SPLIT) {
-              const float r0 = h0 - __builtin_bit_cast(float, hi.x << 16);
-              const float r1 = h1 - __builtin_bit_cast(float, hi.x & 0xFFFF0000u);
-              const float r2 = h2 - __builtin_bit_cast(float, hi.y << 16);
-              const float r3 = h3 - __builtin_bit_cast(float, hi.y & 0xFFFF0000u);
-              *(uint2*)(out_lo + o) = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
-            }
-          } else {
-            *(f32x4*)((float*)out + o) = f32x4{v0 * g, v1 * g, v2 * g, v3 * g};
-          }
-        }
-      }
+          for (int q = 0; q < 4; ++q)
+            pp[((i * NTW + j) * 4 + q) * NTH] =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     }
     if (!more) break;
+  }
+}
+
+// Sums the split-tail partials of each tail tile in workgroup order and
+// applies the tile's epilogue. One thread per float4 group of a partial tile
+// (4 consecutive output columns of one GEMM lane); the grid strides over
+// (XCD, tail tile, group block) with tail tiles that do not exist skipped.
+// `grid` is the GEMM launch's grid.
+constexpr int kReduceThreads = 256;
+template <int BM, int BN, int WM, int WN, int MODE, bool SPLIT>
+__global__ __launch_bounds__(kReduceThreads) void ring_reduce_kernel(
+    const float* __restrict__ part, int grid, const void* __restrict__ bias,
+    const float* __restrict__ gate, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ ntiles_p, int K, int Nout, void* __restrict__ out,
+    bf16* __restrict__ out_lo) {
+  constexpr bool G1 = MODE == kEpiGelu;
+  constexpr int NW = (BM / WM) * (BN / WN);
+  constexpr int NTH = NW * kWave;
+  constexpr int NTW = WN / 32;
+  constexpr int GROUPS = BM * BN / 4;               // float4 groups per tile
+  constexpr int GB = GROUPS / kReduceThreads;       // group blocks per tile
+  const int nk = K / kRK;
+  const int ntiles = *ntiles_p;
+  const int per = grid >> 3;
+  const int nwork = 8 * per * GB;
+  for (int w = blockIdx.x; w < nwork; w += gridDim.x) {
+    const int xcd = w & 7;
+    const int tau = (w >> 3) / GB;
+    const int gb = (w >> 3) - tau * GB;
+    const RingSplit sp(ntiles, xcd, grid, true);
+    if (tau >= sp.tail) continue;
+    const int tile = xcd * sp.chunk + sp.rounds * sp.per + tau;
+    int e, m0, mcount, n0;
+    ring_decode_tile<MODE, BM, BN>(tile, tiles, 0, Nout, e, m0, mcount, n0);
+    // group index g = ((i*NTW + j)*4 + q)*NTH + tid of the GEMM lane layout
+    const int g = gb * kReduceThreads + threadIdx.x;
+    const int tid = g % NTH;
+    const int ijq = g / NTH;
+    const int q = ijq & 3, j = (ijq >> 2) % NTW, i = (ijq >> 2) / NTW;
+    const int wv = tid / kWave, lane = tid % kWave;
+    const int row = (2 * i + wv / (BN / WN)) * 32 + (lane & 31);
+    const int col = n0 + (wv % (BN / WN)) * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    // workgroups whose share holds unit u: lo(j) <= u < lo(j+1), i.e. the
+    // largest j with j*U < (u+1)*per (U = tail*nk units in the tail)
+    const int U = sp.tail * nk;
+    const int u0 = tau * nk, u1 = u0 + nk;
+    const int j1 = (int)(((unsigned)(u0 + 1) * per + U - 1) / (unsigned)U) - 1;
+    const int j2 = (int)(((unsigned)u1 * per + U - 1) / (unsigned)U) - 1;
+    for (int jw = j1; jw <= j2; ++jw) {
+      const int lo = sp.lo(jw, nk), hi = sp.lo(jw + 1, nk);
+      if (hi <= u0 || lo >= u1 || hi <= lo) continue;
+      const int sq = tau - lo / nk;
+      const int b = jw * 8 + xcd;
+      v += ((const f32x4*)(part + (size_t)(b * 2 + sq) * (BM * BN)))[g];
+    }
+    if (row >= mcount || col >= Nout) continue;
+    const int slot = m0 + row;
+    float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+    if (bias != nullptr) {
+      const uint2 bb = *(const uint2*)((const bf16*)bias + (size_t)e * Nout + col);
+      v0 += __builtin_bit_cast(float, bb.x << 16);
+      v1 += __builtin_bit_cast(float, bb.x & 0xFFFF0000u);
+      v2 += __builtin_bit_cast(float, bb.y << 16);
+      v3 += __builtin_bit_cast(float, bb.y & 0xFFFF0000u);
+    }
+    const size_t o = (size_t)slot * Nout + col;
+    if constexpr (G1) {
+      const float h0 = gelu_as(v0), h1 = gelu_as(v1), h2 = gelu_as(v2), h3 = gelu_as(v3);
+      const uint2 hi = make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
+      *(uint2*)((bf16*)out + o) = hi;
+      if constexpr (SPLIT) {
+        const float r0 = h0 - __builtin_bit_cast(float, hi.x << 16);
+        const float r1 = h1 - __builtin_bit_cast(float, hi.x & 0xFFFF0000u);
+        const float r2 = h2 - __builtin_bit_cast(float, hi.y << 16);
+        const float r3 = h3 - __builtin_bit_cast(float, hi.y & 0xFFFF0000u);
+        *(uint2*)(out_lo + o) = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
+      }
+    } else {
+      const float gg = gate[slot];
+      *(f32x4*)((float*)out + o) = f32x4{v0 * gg, v1 * gg, v2 * gg, v3 * gg};
+    }
   }
 }
 

@@ -134,11 +134,13 @@ int moe_capacity(int T, int N, int k, double capacity_factor) {
 size_t moe_workspace_bytes(int T, int d, int d_ff, int N, int k, double capacity_factor,
                            int dtype) {
   if (check_shape(T, d, d_ff, N, k, dtype, true) != MOE_OK || isnan(capacity_factor)) return 0;
-  // enough for every flag combination: the split plan needs the most
-  ForwardWs f;
-  carve_forward(nullptr, T, d, d_ff, N, k, capacity_host(T, N, k, capacity_factor), dtype,
-                MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32, &f);
-  return f.bytes;
+  // enough for every flag combination (the plans with and without the split
+  // hidden layer differ in tiling and scratch)
+  const int C = capacity_host(T, N, k, capacity_factor);
+  ForwardWs f, g;
+  carve_forward(nullptr, T, d, d_ff, N, k, C, dtype, MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32, &f);
+  carve_forward(nullptr, T, d, d_ff, N, k, C, dtype, MOE_FLAG_Y_F32, &g);
+  return f.bytes > g.bytes ? f.bytes : g.bytes;
 }
 
 int moe_route(const void* x, const void* W_g, const float* logit_bias, int T, int d, int N, int k,
