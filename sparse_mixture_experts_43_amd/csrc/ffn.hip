@@ -27,6 +27,7 @@
 // of each hidden activation and GEMM2 runs a second MFMA on it, so GEMM2 sees
 // the hidden layer to about 16 significant bits instead of 8 (twice GEMM2's
 // MFMA work; used where the weight stream, not MFMA, bounds the time).
+#include "gemm_decode.h"
 #include "gemm_ring.h"
 #include "moe_common.h"
 
@@ -389,214 +390,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
   }
 }
 
-// ---------------------------------------------------------------- decode bf16, LDS-DMA stream
-// Weight streaming for small per-expert batches (<= 64 slots), K % 128 == 0.
-// A block (4 waves) owns 64 weight rows of one expert and a K range; weights
-// and the expert's slot rows stream through a ring of LDS slots with
-// global_load_lds_dwordx4, every wave instruction one contiguous 1 KB run
-// (4 rows x 256 bytes), so HBM sees long sequential reads. Row r keeps its
-// 16-byte chunk c at position c ^ (r & 15): the 16-row fragment reads are
-// bank-conflict free. Each wave multiplies its 16 weight rows against the
-// slot groups with v_mfma_f32_16x16x32_bf16. With split-K the blocks write
-// fp32 partial sums and a reduce kernel applies bias and the epilogue.
-constexpr int kDKC = 128;             // K per chunk
-constexpr int kDRowB = kDKC * 2;      // 256 bytes per row per chunk
-constexpr int kDWRows = 64;           // weight rows per block
-
-template <bool G1, bool SPLIT>
-struct DecodeGeom {
-  static constexpr bool XLO = SPLIT && !G1;
-  static constexpr int RING = XLO ? 3 : 4;
-  static constexpr int W_OFF = 0;
-  static constexpr int X_OFF = kDWRows * kDRowB;           // 16 KB
-  static constexpr int L_OFF = X_OFF + 64 * kDRowB;        // 32 KB
-  static constexpr int SLOT = L_OFF + (XLO ? 64 * kDRowB : 0);
-  static constexpr size_t LDS = (size_t)RING * SLOT;
-};
-
-template <bool G1, bool SPLIT, int NG>
-__device__ __forceinline__ void decode_dma_body(
-    const bf16* __restrict__ X, const bf16* __restrict__ X_lo, const int32_t* __restrict__ perm,
-    int kpairs, const bf16* __restrict__ W, const bf16* __restrict__ bias,
-    const float* __restrict__ gate, int K, int Nout, int e, int n0, int m0, int mcount,
-    int kbeg, int nch, void* __restrict__ out, bf16* __restrict__ out_lo,
-    float* __restrict__ part, int S_cap, int ks) {
-  using Geo = DecodeGeom<G1, SPLIT>;
-  constexpr bool XLO = Geo::XLO;
-  constexpr int RING = Geo::RING;
-  constexpr int LPS = 4 + NG * (XLO ? 2 : 1);  // DMA instructions per wave per chunk
-  extern __shared__ __align__(16) unsigned char smem[];
-  MOE_LDS unsigned char* lds = (MOE_LDS unsigned char*)smem;
-  const int l = lane_id();
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-
-  // DMA sources: wave-load i covers rows 4*(4i + wv) .. +4; lane l fills row
-  // +l/16, position l%16, which holds chunk (l%16) ^ (row & 15).
-  const int rsub = l >> 4;
-  const unsigned char* pw[4];
-  const unsigned char* px[NG];
-  const unsigned char* pxl[XLO ? NG : 1];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * (4 * i + wv) + rsub;
-    const int c = (l & 15) ^ (r & 15);
-    const int n = min(n0 + r, Nout - 1);
-    pw[i] = (const unsigned char*)(W + ((size_t)e * Nout + n) * K + kbeg) + 16 * c;
-  }
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    const int r = 4 * (4 * i + wv) + rsub;
-    const int c = (l & 15) ^ (r & 15);
-    const int slot = m0 + min(r, mcount - 1);
-    const size_t row = G1 ? (size_t)(perm[slot] / kpairs) : (size_t)slot;
-    px[i] = (const unsigned char*)(X + row * K + kbeg) + 16 * c;
-    if constexpr (XLO) pxl[i] = (const unsigned char*)(X_lo + row * K + kbeg) + 16 * c;
-  }
-  auto issue = [&](int slot_i, int chunk) {
-    MOE_LDS unsigned char* st = lds + (slot_i % RING) * Geo::SLOT;
-    const int kb = chunk * kDRowB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(pw[i] + kb, st + Geo::W_OFF + (4 * i + wv) * 1024);
-#pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      dma16(px[i] + kb, st + Geo::X_OFF + (4 * i + wv) * 1024);
-      if constexpr (XLO) dma16(pxl[i] + kb, st + Geo::L_OFF + (4 * i + wv) * 1024);
-    }
-  };
-
-  f32x4 acc[NG];
-#pragma unroll
-  for (int sg = 0; sg < NG; ++sg) acc[sg] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const int R = 16 * wv + (l & 15);  // weight row of this lane's fragment
-  const int Rs = R & 15;
-  const int S = l & 15;              // slot row within a group (group base is a multiple of 16)
-
-#pragma unroll
-  for (int q = 0; q < RING - 1; ++q) issue(q, q < nch ? q : nch - 1);
-  for (int c = 0; c < nch; ++c) {
-    vm_wait_n<(RING - 2) * LPS>();
-    wg_barrier();
-    issue(c + RING - 1, c + RING - 1 < nch ? c + RING - 1 : nch - 1);
-    const unsigned char* st = smem + (c % RING) * Geo::SLOT;
-#pragma unroll
-    for (int kq = 0; kq < kDKC / 32; ++kq) {
-      const int ch = 4 * kq + (l >> 4);
-      const bf16x8 wf = *(const bf16x8*)(st + Geo::W_OFF + R * kDRowB + 16 * (ch ^ Rs));
-#pragma unroll
-      for (int sg = 0; sg < NG; ++sg) {
-        const int xo = (16 * sg + S) * kDRowB + 16 * (ch ^ S);
-        const bf16x8 xf = *(const bf16x8*)(st + Geo::X_OFF + xo);
-        acc[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf, acc[sg], 0, 0, 0);
-        if constexpr (XLO) {
-          const bf16x8 xl = *(const bf16x8*)(st + Geo::L_OFF + xo);
-          acc[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xl, acc[sg], 0, 0, 0);
-        }
-      }
-    }
-  }
-  vm_wait_n<0>();  // no LDS DMA may outlive the workgroup
-
-  // D[row][slot]: lane holds slot column l%16 of each group, rows 4*(l/16) + i.
-  const int gq = l >> 4;
-#pragma unroll
-  for (int sg = 0; sg < NG; ++sg) {
-    const int sl = 16 * sg + (l & 15);
-    if (sl >= mcount) continue;
-    const int slot = m0 + sl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + 16 * wv + 4 * gq + i;
-      if (n >= Nout) continue;
-      if (part != nullptr) {
-        part[((size_t)ks * S_cap + slot) * Nout + n] = acc[sg][i];
-        continue;
-      }
-      const float v = acc[sg][i] + (bias != nullptr ? (float)bias[(size_t)e * Nout + n] : 0.f);
-      const size_t o = (size_t)slot * Nout + n;
-      if constexpr (G1) {
-        const float h = gelu_erf(v);
-        const bf16 hi = (bf16)h;
-        ((bf16*)out)[o] = hi;
-        if constexpr (SPLIT) out_lo[o] = (bf16)(h - (float)hi);
-      } else {
-        ((float*)out)[o] = v * gate[slot];
-      }
-    }
-  }
-}
-
-template <bool G1, bool SPLIT>
-__global__ __launch_bounds__(256) void decode_dma_kernel(
-    const bf16* __restrict__ X, const bf16* __restrict__ X_lo, const int32_t* __restrict__ perm,
-    int kpairs, const int32_t* __restrict__ off, const bf16* __restrict__ W,
-    const bf16* __restrict__ bias, const float* __restrict__ gate, int K, int Nout, int nblk_n,
-    int nsplit, void* __restrict__ out, bf16* __restrict__ out_lo, float* __restrict__ part,
-    int S_cap) {
-  const int ks = blockIdx.x % nsplit;
-  const int rest = blockIdx.x / nsplit;
-  const int e = rest / nblk_n;
-  const int nb = rest - e * nblk_n;
-  const int m0 = off[e];
-  const int mcount = off[e + 1] - m0;
-  if (mcount <= 0) return;  // untouched expert: its weights are never read
-  const int nch_all = K / kDKC;
-  const int per = (nch_all + nsplit - 1) / nsplit;
-  const int c0 = ks * per;
-  const int nch = min(nch_all, c0 + per) - c0;
-  if (nch <= 0) return;
-  const int n0 = nb * kDWRows;
-  float* pp = nsplit > 1 ? part : nullptr;
-  switch ((mcount + 15) / 16) {
-    case 1:
-      decode_dma_body<G1, SPLIT, 1>(X, X_lo, perm, kpairs, W, bias, gate, K, Nout, e, n0, m0,
-                                    mcount, c0 * kDKC, nch, out, out_lo, pp, S_cap, ks);
-      break;
-    case 2:
-      decode_dma_body<G1, SPLIT, 2>(X, X_lo, perm, kpairs, W, bias, gate, K, Nout, e, n0, m0,
-                                    mcount, c0 * kDKC, nch, out, out_lo, pp, S_cap, ks);
-      break;
-    case 3:
-      decode_dma_body<G1, SPLIT, 3>(X, X_lo, perm, kpairs, W, bias, gate, K, Nout, e, n0, m0,
-                                    mcount, c0 * kDKC, nch, out, out_lo, pp, S_cap, ks);
-      break;
-    default:
-      decode_dma_body<G1, SPLIT, 4>(X, X_lo, perm, kpairs, W, bias, gate, K, Nout, e, n0, m0,
-                                    mcount, c0 * kDKC, nch, out, out_lo, pp, S_cap, ks);
-      break;
-  }
-}
-
-// Split-K reduce: fixed-order sum of the partials, bias and epilogue. One
-// block per (expert, 64-row block), threads over (slot, row).
-template <bool G1, bool SPLIT>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(
-    const float* __restrict__ part, int nsplit, int S_cap, const int32_t* __restrict__ off,
-    const bf16* __restrict__ bias, const float* __restrict__ gate, int Nout, int nblk_n,
-    void* __restrict__ out, bf16* __restrict__ out_lo) {
-  const int e = blockIdx.x / nblk_n;
-  const int nb = blockIdx.x - e * nblk_n;
-  const int m0 = off[e];
-  const int mcount = off[e + 1] - m0;
-  const int n0 = nb * kDWRows;
-  for (int i = threadIdx.x; i < mcount * kDWRows; i += 256) {
-    const int sl = i / kDWRows, n = n0 + i % kDWRows;
-    if (n >= Nout) continue;
-    const int slot = m0 + sl;
-    float v = 0.f;
-    for (int q = 0; q < nsplit; ++q) v += part[((size_t)q * S_cap + slot) * Nout + n];
-    v += bias != nullptr ? (float)bias[(size_t)e * Nout + n] : 0.f;
-    const size_t o = (size_t)slot * Nout + n;
-    if constexpr (G1) {
-      const float h = gelu_erf(v);
-      const bf16 hi = (bf16)h;
-      ((bf16*)out)[o] = hi;
-      if constexpr (SPLIT) out_lo[o] = (bf16)(h - (float)hi);
-    } else {
-      ((float*)out)[o] = v * gate[slot];
-    }
-  }
-}
-
 // ---------------------------------------------------------------- fp32
 template <bool G1>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
@@ -669,14 +462,21 @@ struct Plan {
   bool split;
   int ks1, ks2;    // decode split-K factors (1 = none)
   bool dma1, dma2; // decode GEMMs on the LDS-DMA stream kernel
+  int xg;          // decode: 16-slot groups an expert can hold (capacity / 16, rounded up to 1, 2, 4)
 };
 
 // Split-K factor for a decode GEMM: enough blocks to cover the CUs a few times.
-int decode_splits(int N, int Nout, int K) {
-  const int blocks = N * cdiv(Nout, kDWRows);
+// Split-K factor for a decode GEMM: double it (keeping at least 8 chunks of
+// K per share) while there are fewer than 1024 items; measured on the
+// Mixtral-shaped decode layer, more items per workgroup stream better than
+// splits chosen to fill whole rounds.
+int decode_splits(int N, int Nout, int K, int xg, bool xlo) {
+  (void)xg;
+  (void)xlo;
+  const int items = N * cdiv(Nout, kDWRows);
   const int nch = K / kDKC;
   int s = 1;
-  while (blocks * s < 1024 && s < 8 && nch / (2 * s) >= 8) s *= 2;
+  while (items * s < 1024 && s < 8 && nch / (2 * s) >= 8) s *= 2;
   return s;
 }
 
@@ -691,10 +491,11 @@ Plan make_plan(int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype
   } else if (Ccap <= 64) {
     p.path = kPathDecode;
     p.BM = 64; p.BN1 = p.BN2 = kDecRows;
+    p.xg = Ccap <= 16 ? 1 : (Ccap <= 32 ? 2 : 4);
     p.dma1 = d % kDKC == 0;
     p.dma2 = d_ff % kDKC == 0;
-    p.ks1 = p.dma1 ? decode_splits(N, d_ff, d) : 1;
-    p.ks2 = p.dma2 ? decode_splits(N, d, d_ff) : 1;
+    p.ks1 = p.dma1 ? decode_splits(N, d_ff, d, p.xg, false) : 1;
+    p.ks2 = p.dma2 ? decode_splits(N, d, d_ff, p.xg, p.split) : 1;
   } else if (!p.split && Ccap >= 1024 && S_max / N >= 512) {
     p.path = kPathTiledL;
     p.BM = 256; p.BN1 = p.BN2 = 256;
@@ -783,23 +584,42 @@ hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, c
   return hipGetLastError();
 }
 
+template <bool G1, bool SPLIT, int XG>
+void launch_decode_dma(int nsplit, const bf16* X, const bf16* X_lo, const int32_t* perm, int k,
+                       const int32_t* off, const bf16* W, const bf16* bias, const float* gate,
+                       int K, int Nout, int N, void* out, bf16* out_lo, float* part, int S_cap,
+                       hipStream_t st) {
+  constexpr int RING = decode_ring(XG, SPLIT && !G1);
+  using Geo = DecodeGeom<G1, SPLIT, XG, RING>;
+  const int nb = cdiv(Nout, kDWRows);
+  MOE_SET_LDS_ONCE((decode_dma_kernel<G1, SPLIT, XG, RING>), Geo::LDS);
+  const int grid = ring_grid((const void*)decode_dma_kernel<G1, SPLIT, XG, RING>, 256, Geo::LDS,
+                             N * nb * nsplit);
+  hipLaunchKernelGGL((decode_dma_kernel<G1, SPLIT, XG, RING>), dim3(grid), dim3(256), Geo::LDS,
+                     st, X, X_lo, perm, k, off, W, bias, gate, K, Nout, nb, nsplit, out, out_lo,
+                     part, S_cap, N);
+  if (nsplit > 1)
+    hipLaunchKernelGGL((decode_reduce_kernel<G1, SPLIT>), dim3(N * nb), dim3(256), 0, st, part,
+                       nsplit, S_cap, off, bias, gate, Nout, nb, out, out_lo);
+}
+
 // One decode GEMM: LDS-DMA stream kernel (+ split-K reduce) when K % 128 == 0,
-// else the direct-load kernel.
+// else the direct-load kernel. xg: 16-slot groups per expert (<= 4).
 template <bool G1, bool SPLIT>
-void launch_decode_gemm(bool dma, int nsplit, const bf16* X, const bf16* X_lo,
+void launch_decode_gemm(bool dma, int nsplit, int xg, const bf16* X, const bf16* X_lo,
                         const int32_t* perm, int k, const int32_t* off, const bf16* W,
                         const bf16* bias, const float* gate, int K, int Nout, int N, void* out,
                         bf16* out_lo, float* part, int S_cap, hipStream_t st) {
   if (dma) {
-    using Geo = DecodeGeom<G1, SPLIT>;
-    const int nb = cdiv(Nout, kDWRows);
-    MOE_SET_LDS_ONCE((decode_dma_kernel<G1, SPLIT>), Geo::LDS);
-    hipLaunchKernelGGL((decode_dma_kernel<G1, SPLIT>), dim3(N * nb * nsplit), dim3(256), Geo::LDS,
-                       st, X, X_lo, perm, k, off, W, bias, gate, K, Nout, nb, nsplit, out, out_lo,
-                       part, S_cap);
-    if (nsplit > 1)
-      hipLaunchKernelGGL((decode_reduce_kernel<G1, SPLIT>), dim3(N * nb), dim3(256), 0, st, part,
-                         nsplit, S_cap, off, bias, gate, Nout, nb, out, out_lo);
+    if (xg <= 1)
+      launch_decode_dma<G1, SPLIT, 1>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout, N,
+                                      out, out_lo, part, S_cap, st);
+    else if (xg == 2)
+      launch_decode_dma<G1, SPLIT, 2>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout, N,
+                                      out, out_lo, part, S_cap, st);
+    else
+      launch_decode_dma<G1, SPLIT, 4>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout, N,
+                                      out, out_lo, part, S_cap, st);
     return;
   }
   const int nb = cdiv(Nout, kDecRows);
@@ -813,11 +633,11 @@ hipError_t launch_decode(const void* x, const int32_t* perm, const int32_t* off,
                          int d_ff, int N, int k, const Plan& pl, int S_cap, void* hid,
                          bf16* hid_lo, float* part, void* slot_out, hipStream_t st) {
   profile_mark(3, st);
-  launch_decode_gemm<true, SPLIT>(pl.dma1, pl.ks1, (const bf16*)x, nullptr, perm, k, off,
+  launch_decode_gemm<true, SPLIT>(pl.dma1, pl.ks1, pl.xg, (const bf16*)x, nullptr, perm, k, off,
                                   (const bf16*)W1, (const bf16*)b1, nullptr, d, d_ff, N, hid,
                                   hid_lo, part, S_cap, st);
   profile_mark(4, st);
-  launch_decode_gemm<false, SPLIT>(pl.dma2, pl.ks2, (const bf16*)hid, hid_lo, perm, k, off,
+  launch_decode_gemm<false, SPLIT>(pl.dma2, pl.ks2, pl.xg, (const bf16*)hid, hid_lo, perm, k, off,
                                    (const bf16*)W2, (const bf16*)b2, gate, d_ff, d, N, slot_out,
                                    nullptr, part, S_cap, st);
   profile_mark(5, st);

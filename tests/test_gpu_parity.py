@@ -34,6 +34,8 @@ CASES = [
     ("decode_split", 40, 200, 136, 8, 2, 0.0, "bf16", True, "none", SPLIT),
     ("decode_splitk", 24, 512, 4096, 4, 2, 0.0, "bf16", True, "none", 0),
     ("decode_splitk_hilo", 24, 512, 4096, 4, 2, 0.0, "bf16", True, "none", SPLIT),
+    ("decode_splitk_tail", 24, 2048, 6400, 6, 2, 0.0, "bf16", True, "normal0.5", 0),
+    ("decode_splitk_tail_hilo", 20, 2048, 6400, 6, 2, 0.0, "bf16", False, "none", SPLIT),
     ("decode_64_slots", 64, 256, 512, 2, 2, 0.0, "bf16", False, "none", 0),
     ("decode_64_slots_hilo", 64, 256, 512, 2, 2, 0.0, "bf16", True, "normal0.5", SPLIT),
     ("tiledM_ragged", 600, 256, 320, 4, 2, 1.0, "bf16", False, "none", 0),
