@@ -584,18 +584,18 @@ hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, c
   return hipGetLastError();
 }
 
-template <bool G1, bool SPLIT, int XG>
+template <bool G1, bool SPLIT, int XG, int KC>
 void launch_decode_dma(int nsplit, const bf16* X, const bf16* X_lo, const int32_t* perm, int k,
                        const int32_t* off, const bf16* W, const bf16* bias, const float* gate,
                        int K, int Nout, int N, void* out, bf16* out_lo, float* part, int S_cap,
                        hipStream_t st) {
-  constexpr int RING = decode_ring(XG, SPLIT && !G1);
-  using Geo = DecodeGeom<G1, SPLIT, XG, RING>;
+  constexpr int RING = decode_ring(XG, SPLIT && !G1, KC);
+  using Geo = DecodeGeom<G1, SPLIT, XG, RING, KC>;
   const int nb = cdiv(Nout, kDWRows);
-  MOE_SET_LDS_ONCE((decode_dma_kernel<G1, SPLIT, XG, RING>), Geo::LDS);
-  const int grid = ring_grid((const void*)decode_dma_kernel<G1, SPLIT, XG, RING>, 256, Geo::LDS,
-                             N * nb * nsplit);
-  hipLaunchKernelGGL((decode_dma_kernel<G1, SPLIT, XG, RING>), dim3(grid), dim3(256), Geo::LDS,
+  MOE_SET_LDS_ONCE((decode_dma_kernel<G1, SPLIT, XG, RING, KC>), Geo::LDS);
+  const int grid = ring_grid((const void*)decode_dma_kernel<G1, SPLIT, XG, RING, KC>, 256,
+                             Geo::LDS, N * nb * nsplit);
+  hipLaunchKernelGGL((decode_dma_kernel<G1, SPLIT, XG, RING, KC>), dim3(grid), dim3(256), Geo::LDS,
                      st, X, X_lo, perm, k, off, W, bias, gate, K, Nout, nb, nsplit, out, out_lo,
                      part, S_cap, N);
   if (nsplit > 1)
@@ -611,15 +611,25 @@ void launch_decode_gemm(bool dma, int nsplit, int xg, const bf16* X, const bf16*
                         const bf16* bias, const float* gate, int K, int Nout, int N, void* out,
                         bf16* out_lo, float* part, int S_cap, hipStream_t st) {
   if (dma) {
-    if (xg <= 1)
-      launch_decode_dma<G1, SPLIT, 1>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout, N,
-                                      out, out_lo, part, S_cap, st);
-    else if (xg == 2)
-      launch_decode_dma<G1, SPLIT, 2>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout, N,
-                                      out, out_lo, part, S_cap, st);
-    else
-      launch_decode_dma<G1, SPLIT, 4>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout, N,
-                                      out, out_lo, part, S_cap, st);
+    // the first GEMM (shorter K) streams better in 512-byte row chunks, one
+    // workgroup per CU; the second in 256-byte chunks, two per CU (measured)
+    if (G1 && K % 256 == 0 && xg <= 2) {
+      if (xg <= 1)
+        launch_decode_dma<G1, SPLIT, 1, 256>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K,
+                                             Nout, N, out, out_lo, part, S_cap, st);
+      else
+        launch_decode_dma<G1, SPLIT, 2, 256>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K,
+                                             Nout, N, out, out_lo, part, S_cap, st);
+    } else if (xg <= 1) {
+      launch_decode_dma<G1, SPLIT, 1, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
+                                           N, out, out_lo, part, S_cap, st);
+    } else if (xg == 2) {
+      launch_decode_dma<G1, SPLIT, 2, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
+                                           N, out, out_lo, part, S_cap, st);
+    } else {
+      launch_decode_dma<G1, SPLIT, 4, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
+                                           N, out, out_lo, part, S_cap, st);
+    }
     return;
   }
   const int nb = cdiv(Nout, kDecRows);

@@ -18,50 +18,57 @@ namespace {
 // bank-conflict free. Each wave multiplies its 16 weight rows against the
 // slot groups with v_mfma_f32_16x16x32_bf16. With split-K the blocks write
 // fp32 partial sums and a reduce kernel applies bias and the epilogue.
-constexpr int kDKC = 128;             // K per chunk
+constexpr int kDKC = 128;             // K per chunk (default)
 constexpr int kDRowB = kDKC * 2;      // 256 bytes per row per chunk
 constexpr int kDWRows = 64;           // weight rows per block
 
 // Ring depth of the decode stream kernel: as deep as fits two workgroups per
 // CU in LDS (80 KB each), at least 3 slots.
-constexpr int decode_ring(int xg, bool xlo) {
-  const int slot = kDWRows * kDRowB + 16 * xg * kDRowB * (xlo ? 2 : 1);
+constexpr int decode_ring(int xg, bool xlo, int kc = kDKC) {
+  const int slot = kDWRows * 2 * kc + 16 * xg * 2 * kc * (xlo ? 2 : 1);
   const int r = (80 * 1024) / slot;
   return r < 3 ? 3 : (r > 6 ? 6 : r);
 }
 
 // XG: slot groups of 16 an LDS slot holds (the expert's kept slots, <= 16*XG);
-// RING: slots in the ring.
-template <bool G1, bool SPLIT, int XG, int RING_>
+// RING: slots in the ring; KC: K per chunk (rows of 2*KC bytes).
+template <bool G1, bool SPLIT, int XG, int RING_, int KC = kDKC>
 struct DecodeGeom {
   static constexpr bool XLO = SPLIT && !G1;
   static constexpr int RING = RING_;
+  static constexpr int ROWB = 2 * KC;
+  static constexpr int CPR = KC / 8;        // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;      // rows per wave DMA instruction
+  static constexpr int WLD = 16 / RPI;      // weight DMA instructions per wave per chunk
+  static constexpr int XLD = 4 / RPI;       // slot-row DMA instructions per wave per 16-slot group
   static constexpr int W_OFF = 0;
-  static constexpr int X_OFF = kDWRows * kDRowB;                 // 16 KB of weight rows
-  static constexpr int L_OFF = X_OFF + 16 * XG * kDRowB;
-  static constexpr int SLOT = L_OFF + (XLO ? 16 * XG * kDRowB : 0);
+  static constexpr int X_OFF = kDWRows * ROWB;
+  static constexpr int L_OFF = X_OFF + 16 * XG * ROWB;
+  static constexpr int SLOT = L_OFF + (XLO ? 16 * XG * ROWB : 0);
   static constexpr size_t LDS = (size_t)RING * SLOT;
+  static_assert(CPR == 16 || CPR == 32, "128- or 256-wide K chunks");
 };
 
 // Persistent: workgroup b takes items b, b + grid, ... of the (expert, 64-row
 // block, K share) list, skipping experts that received no slot (their weights
 // are never read), and requests the next item's first chunks before the
 // current item's epilogue, so no item pays the stream's start-up latency.
-template <bool G1, bool SPLIT, int XG, int RING>
+template <bool G1, bool SPLIT, int XG, int RING, int KC = kDKC>
 __global__ __launch_bounds__(256) void decode_dma_kernel(
     const bf16* __restrict__ X, const bf16* __restrict__ X_lo, const int32_t* __restrict__ perm,
     int kpairs, const int32_t* __restrict__ off, const bf16* __restrict__ W,
     const bf16* __restrict__ bias, const float* __restrict__ gate, int K, int Nout, int nblk_n,
     int nsplit, void* __restrict__ out, bf16* __restrict__ out_lo, float* __restrict__ part,
     int S_cap, int n_experts) {
-  using Geo = DecodeGeom<G1, SPLIT, XG, RING>;
+  using Geo = DecodeGeom<G1, SPLIT, XG, RING, KC>;
   constexpr bool XLO = Geo::XLO;
+  constexpr int ROWB = Geo::ROWB, CPR = Geo::CPR, RPI = Geo::RPI, WLD = Geo::WLD, XLD = Geo::XLD;
   extern __shared__ __align__(16) unsigned char smem[];
   MOE_LDS unsigned char* lds = (MOE_LDS unsigned char*)smem;
   const int l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int n_items = n_experts * nblk_n * nsplit;
-  const int nch_all = K / kDKC;
+  const int nch_all = K / KC;
   const int per = (nch_all + nsplit - 1) / nsplit;
 
   // item i -> expert, rows, K share; false when the item holds no work
@@ -84,25 +91,25 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
     return n_items;
   };
 
-  // DMA sources: wave-load i covers rows 4*(4i + wv) .. +4; lane l fills row
-  // +l/16, position l%16, which holds chunk (l%16) ^ (row & 15).
-  const int rsub = l >> 4;
-  const unsigned char* pw[4];
-  const unsigned char* px[XG];
-  const unsigned char* pxl[XLO ? XG : 1];
+  // DMA sources: wave-load i covers rows RPI*(4i + wv) .. +RPI; lane l fills
+  // row +l/CPR, position l%CPR, which holds chunk (l%CPR) ^ (row & 15).
+  const int rsub = l / CPR;
+  const unsigned char* pw[WLD];
+  const unsigned char* px[XG * XLD];
+  const unsigned char* pxl[XLO ? XG * XLD : 1];
   auto set_ptrs = [&]() {
-    const int kbeg = c0 * kDKC;
+    const int kbeg = c0 * KC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * (4 * i + wv) + rsub;
-      const int c = (l & 15) ^ (r & 15);
+    for (int i = 0; i < WLD; ++i) {
+      const int r = RPI * (4 * i + wv) + rsub;
+      const int c = (l % CPR) ^ (r & 15);
       const int n = min(n0 + r, Nout - 1);
       pw[i] = (const unsigned char*)(W + ((size_t)e * Nout + n) * K + kbeg) + 16 * c;
     }
 #pragma unroll
-    for (int i = 0; i < XG; ++i) {
-      const int r = 4 * (4 * i + wv) + rsub;
-      const int c = (l & 15) ^ (r & 15);
+    for (int i = 0; i < XG * XLD; ++i) {
+      const int r = RPI * (4 * i + wv) + rsub;
+      const int c = (l % CPR) ^ (r & 15);
       const int slot = m0 + min(r, mcount - 1);
       const size_t row = G1 ? (size_t)(perm[slot] / kpairs) : (size_t)slot;
       px[i] = (const unsigned char*)(X + row * K + kbeg) + 16 * c;
@@ -113,11 +120,11 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
   auto issue = [&](int slot_i, int chunk, auto ng_c) {
     constexpr int NG = decltype(ng_c)::value;
     MOE_LDS unsigned char* st = lds + (slot_i % RING) * Geo::SLOT;
-    const int kb = chunk * kDRowB;
+    const int kb = chunk * ROWB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(pw[i] + kb, st + Geo::W_OFF + (4 * i + wv) * 1024);
+    for (int i = 0; i < WLD; ++i) dma16(pw[i] + kb, st + Geo::W_OFF + (4 * i + wv) * 1024);
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
+    for (int i = 0; i < NG * XLD; ++i) {
       dma16(px[i] + kb, st + Geo::X_OFF + (4 * i + wv) * 1024);
       if constexpr (XLO) dma16(pxl[i] + kb, st + Geo::L_OFF + (4 * i + wv) * 1024);
     }
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
   // item's first chunks, then write this item's outputs
   auto run_item = [&](auto ng_c) -> int {
     constexpr int NG = decltype(ng_c)::value;
-    constexpr int LPS = 4 + NG * (XLO ? 2 : 1);  // DMA instructions per wave per chunk
+    constexpr int LPS = WLD + NG * XLD * (XLO ? 2 : 1);  // DMA instructions per wave per chunk
     f32x4 acc[NG];
 #pragma unroll
     for (int sg = 0; sg < NG; ++sg) acc[sg] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -160,12 +167,12 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
       issue(c + RING - 1, c + RING - 1 < nch ? c + RING - 1 : nch - 1, ng_c);
       const unsigned char* st = smem + (c % RING) * Geo::SLOT;
 #pragma unroll
-      for (int kq = 0; kq < kDKC / 32; ++kq) {
+      for (int kq = 0; kq < KC / 32; ++kq) {
         const int ch = 4 * kq + (l >> 4);
-        const bf16x8 wf = *(const bf16x8*)(st + Geo::W_OFF + R * kDRowB + 16 * (ch ^ Rs));
+        const bf16x8 wf = *(const bf16x8*)(st + Geo::W_OFF + R * ROWB + 16 * (ch ^ Rs));
 #pragma unroll
         for (int sg = 0; sg < NG; ++sg) {
-          const int xo = (16 * sg + S) * kDRowB + 16 * (ch ^ S);
+          const int xo = (16 * sg + S) * ROWB + 16 * (ch ^ S);
           const bf16x8 xf = *(const bf16x8*)(st + Geo::X_OFF + xo);
           acc[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf, acc[sg], 0, 0, 0);
           if constexpr (XLO) {

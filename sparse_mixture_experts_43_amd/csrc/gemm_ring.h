@@ -88,17 +88,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // Resident workgroups for a persistent ring kernel: every workgroup that fits
 // on the device at once, at most one per tile, rounded up to a multiple of 8
 // (one share per XCD).
+// (The device queries are cached per calling thread: they cost microseconds,
+// which a small layer's launch sequence would otherwise expose.)
 inline int ring_grid(const void* kernel, int threads, size_t lds, int max_tiles) {
-  int dev = 0, cus = 0, occ = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, lds) != hipSuccess ||
-      occ < 1)
-    occ = 1;
-  (void)hipGetLastError();
-  long long g = (long long)cus * occ;
+  struct Entry {
+    const void* kernel;
+    int threads, dev;
+    size_t lds;
+    int resident;
+  };
+  thread_local Entry cache[32];
+  thread_local int n_cache = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int resident = 0;
+  for (int i = 0; i < n_cache; ++i)
+    if (cache[i].kernel == kernel && cache[i].threads == threads && cache[i].lds == lds &&
+        cache[i].dev == dev)
+      resident = cache[i].resident;
+  if (resident == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, lds) != hipSuccess ||
+        occ < 1)
+      occ = 1;
+    (void)hipGetLastError();
+    resident = cus * occ;
+    if (n_cache < 32) cache[n_cache++] = Entry{kernel, threads, dev, lds, resident};
+  }
+  long long g = resident;
   const long long mt = max_tiles > 0 ? max_tiles : 1;
   if (g > mt) g = mt;
   return (int)((g + 7) / 8 * 8);
