@@ -26,15 +26,86 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  const int32_t* it = inv + (size_t)t * k;
+  // picks in groups of 4: all slot indices first, then every kept pick's row
+  // load issued before the first add (more loads in flight), then the sums in
+  // fixed pick order
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    int s[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] = j0 + q < k ? it[j0 + q] : -1;
+    f32x4 v[4][V / 4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4* src = (const f32x4*)(slot_out + (size_t)(s[q] < 0 ? 0 : s[q]) * d + c);
+#pragma unroll
+      for (int h = 0; h < V / 4; ++h) v[q][h] = s[q] >= 0 ? src[h] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (s[q] < 0) continue;
+#pragma unroll
+      for (int h = 0; h < V / 4; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[4 * h + i] += v[q][h][i];
+    }
+  }
+  i32x4 outv;
+  T* o = (T*)&outv;
+#pragma unroll
+  for (int i = 0; i < V; ++i) o[i] = from_f32<T>(acc[i]);
+  *(i32x4*)(y + (size_t)t * d + c) = outv;
+}
+
+// The same combine when the second expert GEMM left K-split partials: each
+// kept pick's slot value is finished here as gate * (((0 + p_0) + p_1) + ... +
+// b2), the operations and order of the split-K reduction, then summed over the
+// picks in fixed order, so y is bit-identical to the two-kernel path.
+template <typename T, typename B>
+__global__ __launch_bounds__(256) void combine_splitk_kernel(
+    const float* __restrict__ part, int nsplit, int S_cap, const B* __restrict__ bias,
+    const float* __restrict__ gate, const int32_t* __restrict__ off, int N,
+    const int32_t* __restrict__ inv, int T_, int d, int k, T* __restrict__ y) {
+#pragma clang fp contract(off)
+  constexpr int V = 16 / sizeof(T);
+  const int vpr = d / V;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)T_ * vpr) return;
+  const int t = (int)(gid / vpr);
+  const int c = (int)(gid - (long long)t * vpr) * V;
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
   for (int j = 0; j < k; ++j) {
     const int s = inv[(size_t)t * k + j];
     if (s < 0) continue;
-    const f32x4* src = (const f32x4*)(slot_out + (size_t)s * d + c);
+    float v[V];
 #pragma unroll
-    for (int q = 0; q < V / 4; ++q) {
-      const f32x4 v = src[q];
+    for (int i = 0; i < V; ++i) v[i] = 0.f;
+    for (int q = 0; q < nsplit; ++q) {
+      const f32x4* src = (const f32x4*)(part + ((size_t)q * S_cap + s) * d + c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[4 * q + i] += v[i];
+      for (int h = 0; h < V / 4; ++h) {
+        const f32x4 pv = src[h];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * h + i] += pv[i];
+      }
+    }
+    int e = 0;
+    if (bias != nullptr) {
+      // expert of slot s: the last e with off[e] <= s
+      int lo = 0, hi = N - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= s) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+    }
+    const float g = gate[s];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      v[i] += bias != nullptr ? to_f32(bias[(size_t)e * d + c + i]) : 0.f;
+      acc[i] += v[i] * g;  // rounded product, as the stored slot value (no fma)
     }
   }
   i32x4 outv;
@@ -45,6 +116,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 }  // namespace
+
+hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, int d, int k,
+                                 int dtype, void* y, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  // the split-K path exists for bf16 weights only; y may be fp32 or bf16
+  const bf16* b = (const bf16*)sk.bias;
+  const int V = dtype == kF32 ? 4 : 8;
+  const long long n = (long long)T * (d / V);
+  const int blocks = (int)((n + 255) / 256);
+  if (dtype == kF32)
+    hipLaunchKernelGGL((combine_splitk_kernel<float, bf16>), dim3(blocks), dim3(256), 0, st,
+                       sk.part, sk.nsplit, sk.S_cap, b, sk.gate, sk.off, sk.N, inv, T, d, k,
+                       (float*)y);
+  else
+    hipLaunchKernelGGL((combine_splitk_kernel<bf16, bf16>), dim3(blocks), dim3(256), 0, st,
+                       sk.part, sk.nsplit, sk.S_cap, b, sk.gate, sk.off, sk.N, inv, T, d, k,
+                       (bf16*)y);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d, int k,
                           int dtype, void* y, hipStream_t st) {

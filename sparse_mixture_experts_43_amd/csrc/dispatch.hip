@@ -285,95 +285,285 @@ __global__ __launch_bounds__(256) void bucket_kernel(
 }
 
 // ------------------------------------------------------------ select + scatter
+// One block per expert. An expert within capacity writes its slots in bucket
+// (token) order. Over capacity, the C-th largest U of the order-preserving
+// 64-bit images of the fp64 keys is found by radix selection: the bits above
+// the highest bit in which the expert's keys differ are common (block min/max);
+// 256-bin passes on 8-bit digits from there down each pick the bin holding
+// the C-th largest key, and once the remaining candidates fit in a short LDS
+// list they are compacted into it, so the later passes scan only them. The
+// pairs with key above U and the first (lowest-token) ones equal to U are
+// kept, in token order. Up to kSelLds keys are held in LDS.
+constexpr int kSelLds = 16384;
+constexpr int kSelList = 1024;  // compacted candidates
+
+// Wave-aggregated histogram add: lanes with the same digit add once. The
+// distinct digits of the wave are peeled off one at a time (the high digits of
+// one expert's keys take few values); after 4 rounds the remaining lanes group
+// by bit-wise ballots.
+template <int BITS>
+__device__ __forceinline__ void hist_add(int* hist, int dig, bool cand) {
+  unsigned long long rem = __ballot(cand);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (rem == 0ull) return;
+    const int lead = __builtin_amdgcn_readfirstlane(__ffsll((long long)rem) - 1);
+    const int d0 = __shfl(dig, lead, kWave);
+    const unsigned long long same = __ballot(cand && dig == d0) & rem;
+    if (lane_id() == lead) atomicAdd(&hist[d0], __popcll(same));
+    rem &= ~same;
+  }
+  if (rem == 0ull) return;
+  const bool mine = (rem >> lane_id()) & 1ull;
+  const unsigned long long peers = match_peers<BITS>(dig, mine);
+  if (mine && __popcll(peers & lanemask_lt()) == 0) atomicAdd(&hist[dig], __popcll(peers));
+}
+
+// Threshold digit of a histogram of `bins` (<= 2048) bins: the digit whose
+// suffix count (from the top) first reaches `want`; run by one wave.
+__device__ __forceinline__ void hist_pick(const int* hist, int bins, int want, int* out_dig,
+                                          int* out_want) {
+  const int l = lane_id();
+  const int per = (bins + kWave - 1) / kWave;  // bins per lane, descending from the top
+  int s = 0;
+  for (int q = 0; q < per; ++q) {
+    const int b = bins - 1 - (l * per + q);
+    if (b >= 0) s += hist[b];
+  }
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (l >= o) incl += y;
+  }
+  int above = incl - s;
+  for (int q = 0; q < per; ++q) {
+    const int b = bins - 1 - (l * per + q);
+    if (b < 0) break;
+    const int c = hist[b];
+    if (above < want && above + c >= want) {
+      *out_dig = b;
+      *out_want = want - above;
+    }
+    above += c;
+  }
+}
+
+constexpr int kSelWaves = kScanThreads / kWave;
+struct SelShared {
+  int tmp[17];
+  int hist[256];
+  int whist[kSelWaves][256];  // per-wave sub-histograms
+  unsigned long long list[kSelList];
+  unsigned long long red[2][16];
+  int dig, want, cnt;
+};
+
+template <bool LDSC>
+__device__ __forceinline__ void select_body(
+    const int32_t* __restrict__ bucket, const unsigned long long* __restrict__ codes,
+    const float* __restrict__ w, int n, int base, int o, int C, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, float* __restrict__ gate, unsigned long long* __restrict__ sc,
+    SelShared& shm) {
+  int* tmp = shm.tmp;
+  int* hist = shm.hist;
+  unsigned long long* list = shm.list;
+  auto& red = shm.red;
+  int& sh_dig = shm.dig;
+  int& sh_want = shm.want;
+  int& sh_cnt = shm.cnt;
+  const int tid = threadIdx.x;
+  const int l = lane_id(), wv = tid / kWave;
+  if constexpr (LDSC) {
+    for (int i0 = 0; i0 < n; i0 += 4 * kScanThreads) {
+      unsigned long long v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q * kScanThreads + tid;
+        v[q] = i < n ? codes[base + i] : 0ull;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q * kScanThreads + tid;
+        if (i < n) sc[i] = v[q];
+      }
+    }
+  }
+  auto code = [&](int i) -> unsigned long long { return LDSC ? sc[i] : codes[base + i]; };
+
+  // common prefix of all keys: block min and max
+  unsigned long long mn = ~0ull, mx = 0ull;
+  for (int i = tid; i < n; i += kScanThreads) {
+    const unsigned long long u = code(i);
+    mn = u < mn ? u : mn;
+    mx = u > mx ? u : mx;
+  }
+#pragma unroll
+  for (int off2 = 32; off2 > 0; off2 >>= 1) {
+    const unsigned long long a = __shfl_xor(mn, off2, kWave), b2 = __shfl_xor(mx, off2, kWave);
+    mn = a < mn ? a : mn;
+    mx = b2 > mx ? b2 : mx;
+  }
+  if (l == 0) {
+    red[0][wv] = mn;
+    red[1][wv] = mx;
+  }
+  __syncthreads();
+  mn = red[0][0];
+  mx = red[1][0];
+  for (int q = 1; q < kScanThreads / kWave; ++q) {
+    mn = red[0][q] < mn ? red[0][q] : mn;
+    mx = red[1][q] > mx ? red[1][q] : mx;
+  }
+
+  unsigned long long prefix, pmask;
+  int want = C;
+  if (mn == mx) {
+    prefix = mn;  // every key equal: keep the first C by token
+  } else {
+    // 8-bit digits from the highest differing bit down; each pass scans the
+    // candidates (all keys sharing the prefix so far), from the compacted
+    // list once they fit in it
+    int s_hi = 63 - __clzll((long long)(mn ^ mx));  // highest differing bit
+    pmask = s_hi >= 63 ? 0ull : ~((2ull << s_hi) - 1ull);
+    prefix = mn & pmask;
+    bool compact = false;
+    int lsize = 0;  // keys in the compacted list
+    while (true) {
+      const int sh = s_hi >= 7 ? s_hi - 7 : 0;  // digit = bits [sh, s_hi]
+      const int bins = 1 << (s_hi - sh + 1);
+      const unsigned long long dmask = (unsigned long long)(bins - 1);
+      __syncthreads();  // earlier readers of hist / list are done
+      for (int b2 = tid; b2 < kSelWaves * 256; b2 += kScanThreads) (&shm.whist[0][0])[b2] = 0;
+      __syncthreads();
+      const int nn = compact ? lsize : n;
+      int* hw = shm.whist[wv];  // this wave's sub-histogram: no contention between waves
+      for (int i0 = 0; i0 < nn; i0 += kScanThreads) {
+        const int i = i0 + tid;
+        const unsigned long long u = i < nn ? (compact ? list[i] : code(i)) : 0ull;
+        const bool cand = i < nn && (u & pmask) == prefix;
+        const int dig = (int)((u >> sh) & dmask);
+        // up to 4 distinct digits of the wave are added once each (the high
+        // digits of one expert's keys take few values); the remaining lanes
+        // add to their own wave's bins one by one
+        unsigned long long rem = __ballot(cand);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (rem == 0ull) break;
+          const int lead = __builtin_amdgcn_readfirstlane(__ffsll((long long)rem) - 1);
+          const int d0 = __shfl(dig, lead, kWave);
+          const unsigned long long same = __ballot(cand && dig == d0) & rem;
+          if (l == lead) hw[d0] += __popcll(same);
+          rem &= ~same;
+        }
+        if ((rem >> l) & 1ull) atomicAdd(&hw[dig], 1);
+      }
+      __syncthreads();
+      for (int b2 = tid; b2 < bins; b2 += kScanThreads) {
+        int sum = 0;
+#pragma unroll
+        for (int q = 0; q < kSelWaves; ++q) sum += shm.whist[q][b2];
+        hist[b2] = sum;
+      }
+      __syncthreads();
+      if (tid < kWave) hist_pick(hist, bins, want, &sh_dig, &sh_want);
+      __syncthreads();
+      prefix |= (unsigned long long)sh_dig << sh;
+      pmask |= dmask << sh;
+      want = sh_want;
+      const int m_next = hist[sh_dig];
+      if (sh == 0) break;
+      s_hi = sh - 1;
+      if (!compact && m_next <= kSelList) {
+        // the remaining candidates fit in the list: compact them once
+        if (tid == 0) sh_cnt = 0;
+        __syncthreads();
+        for (int i0 = 0; i0 < n; i0 += kScanThreads) {
+          const int i = i0 + tid;
+          const unsigned long long u = i < n ? code(i) : 0ull;
+          if (i < n && (u & pmask) == prefix) list[atomicAdd(&sh_cnt, 1)] = u;
+        }
+        __syncthreads();
+        compact = true;
+        lsize = m_next;
+      }
+    }
+  }
+  // prefix = threshold code U; keep codes > U, and the first `want` codes == U.
+  // Each wave takes a contiguous segment of the expert's requests (token
+  // order), its lanes consecutive elements, ranks from ballot prefixes.
+  const unsigned long long U = prefix;
+  const int seg = ((n + kSelWaves - 1) / kSelWaves + kWave - 1) / kWave * kWave;
+  const int s_beg = wv * seg, s_end = min(n, s_beg + seg);
+  const unsigned long long lt = lanemask_lt();
+  int n_eq = 0;
+  for (int i0 = s_beg; i0 < s_end; i0 += kWave) {
+    const int i = i0 + l;
+    n_eq += __popcll(__ballot(i < s_end && code(i) == U));
+  }
+  int tot;
+  const int eq_before = block_scan_excl(l == 0 ? n_eq : 0, tmp, &tot);
+  const int eq_w = __shfl(eq_before, 0, kWave);  // equal keys before this wave's segment
+  int n_kept = 0;
+  {
+    int r = eq_w;
+    for (int i0 = s_beg; i0 < s_end; i0 += kWave) {
+      const int i = i0 + l;
+      const unsigned long long u = i < s_end ? code(i) : 0ull;
+      const unsigned long long eqm = __ballot(i < s_end && u == U);
+      const bool keep = i < s_end && (u > U || (u == U && r + __popcll(eqm & lt) < want));
+      n_kept += __popcll(__ballot(keep));
+      r += __popcll(eqm);
+    }
+  }
+  const int kept_before = block_scan_excl(l == 0 ? n_kept : 0, tmp, &tot);
+  {
+    int r = eq_w;
+    int ks = o + __shfl(kept_before, 0, kWave);
+    // the segment's pair ids first (all loads in flight), then the writes
+    constexpr int kPre = kSelLds / kSelWaves / kWave;  // iterations of an LDS-sized segment
+    int pre[kPre];
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) {
+      const int i = s_beg + q * kWave + l;
+      pre[q] = i < s_end ? bucket[base + i] : 0;
+    }
+    for (int i0 = s_beg, q = 0; i0 < s_end; i0 += kWave, ++q) {
+      const int i = i0 + l;
+      const bool in = i < s_end;
+      const unsigned long long u = in ? code(i) : 0ull;
+      const int p = !in ? 0 : (q < kPre ? pre[q < kPre ? q : 0] : bucket[base + i]);
+      const unsigned long long eqm = __ballot(in && u == U);
+      const bool keep = in && (u > U || (u == U && r + __popcll(eqm & lt) < want));
+      const unsigned long long km = __ballot(keep);
+      if (keep) write_slot(perm, inv, gate, w, p, ks + __popcll(km & lt));
+      else if (in) inv[p] = -1;
+      ks += __popcll(km);
+      r += __popcll(eqm);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kScanThreads) void select_kernel(
     const int32_t* __restrict__ bucket, const unsigned long long* __restrict__ codes,
     const float* __restrict__ w, const int32_t* __restrict__ req,
     const int32_t* __restrict__ reqoff, const int32_t* __restrict__ off, int C,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, float* __restrict__ gate) {
-  __shared__ int tmp[17];
-  __shared__ int hist[256];
-  __shared__ unsigned long long sh_prefix;
-  __shared__ int sh_want;
+  extern __shared__ __align__(16) unsigned long long sel_codes[];
   const int e = blockIdx.x;
   const int n = req[e];
   const int base = reqoff[e];
   const int o = off[e];
-  const int tid = threadIdx.x;
   if (n <= C) {
-    for (int i = tid; i < n; i += kScanThreads)
+    for (int i = threadIdx.x; i < n; i += kScanThreads)
       write_slot(perm, inv, gate, w, bucket[base + i], o + i);
     return;
   }
-  // Radix select of the C-th largest code among this expert's n codes.
-  unsigned long long prefix = 0ull, pmask = 0ull;
-  int want = C;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int b = tid; b < 256; b += kScanThreads) hist[b] = 0;
-    __syncthreads();
-    for (int i0 = 0; i0 < n; i0 += kScanThreads) {
-      const int i = i0 + tid;
-      const unsigned long long u = i < n ? codes[base + i] : 0ull;
-      const bool cand = i < n && (u & pmask) == prefix;
-      const int dig = (int)((u >> shift) & 255);
-      // lanes with the same digit add once (high digits are shared by most keys)
-      const unsigned long long peers = match_peers<8>(dig, cand);
-      if (cand && __popcll(peers & lanemask_lt()) == 0) atomicAdd(&hist[dig], __popcll(peers));
-    }
-    __syncthreads();
-    if (tid < kWave) {
-      // lane l owns digits 255-4l .. 252-4l (descending); suffix counts from the top
-      int c[4], s = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c[q] = hist[255 - 4 * tid - q];
-        s += c[q];
-      }
-      int incl = s;
-#pragma unroll
-      for (int off2 = 1; off2 < kWave; off2 <<= 1) {
-        const int y = __shfl_up(incl, off2, kWave);
-        if (tid >= off2) incl += y;
-      }
-      int above = incl - s;  // count of digits strictly above this lane's block
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (above < want && above + c[q] >= want) {
-          sh_prefix = prefix | ((unsigned long long)(255 - 4 * tid - q) << shift);
-          sh_want = want - above;
-        }
-        above += c[q];
-      }
-    }
-    __syncthreads();
-    prefix = sh_prefix;
-    want = sh_want;
-    pmask |= 255ull << shift;
-    __syncthreads();
-  }
-  // prefix = threshold code U; keep codes > U, and the first `want` codes == U.
-  const unsigned long long U = prefix;
-  int run_eq = 0, run_kept = 0;
-  for (int i0 = 0; i0 < n; i0 += kScanThreads) {
-    const int i = i0 + tid;
-    unsigned long long u = 0ull;
-    int p = -1;
-    if (i < n) {
-      u = codes[base + i];
-      p = bucket[base + i];
-    }
-    const int eq = (i < n && u == U) ? 1 : 0;
-    int tot_eq;
-    const int eqr = block_scan_excl(eq, tmp, &tot_eq) + run_eq;
-    const int kept = (i < n && (u > U || (eq && eqr < want))) ? 1 : 0;
-    int tot_k;
-    const int ks = block_scan_excl(kept, tmp, &tot_k) + run_kept;
-    if (i < n) {
-      if (kept) write_slot(perm, inv, gate, w, p, o + ks);
-      else inv[p] = -1;
-    }
-    run_eq += tot_eq;
-    run_kept += tot_k;
-  }
+  __shared__ SelShared shm;
+  if (n <= kSelLds)
+    select_body<true>(bucket, codes, w, n, base, o, C, perm, inv, gate, sel_codes, shm);
+  else
+    select_body<false>(bucket, codes, w, n, base, o, C, perm, inv, gate, nullptr, shm);
 }
 
 }  // namespace
@@ -416,8 +606,14 @@ hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key
                        s.tilebase, s.reqoff, s.bucket, s.codes, inv);
   }
   if (can_drop || !fused)
-    hipLaunchKernelGGL(select_kernel, dim3(N), dim3(kScanThreads), 0, st, s.bucket, s.codes, w,
+  {
+    // LDS for the keys of one expert; at most T requests reach an expert
+    const int nmax = T < kSelLds ? T : kSelLds;
+    const size_t lds = (size_t)nmax * sizeof(unsigned long long);
+    MOE_SET_LDS_ONCE(select_kernel, 160 * 1024);
+    hipLaunchKernelGGL(select_kernel, dim3(N), dim3(kScanThreads), lds, st, s.bucket, s.codes, w,
                        req, s.reqoff, off, C, perm, inv, gate);
+  }
   return hipGetLastError();
 }
 

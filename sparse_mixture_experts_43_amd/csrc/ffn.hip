@@ -588,7 +588,7 @@ template <bool G1, bool SPLIT, int XG, int KC>
 void launch_decode_dma(int nsplit, const bf16* X, const bf16* X_lo, const int32_t* perm, int k,
                        const int32_t* off, const bf16* W, const bf16* bias, const float* gate,
                        int K, int Nout, int N, void* out, bf16* out_lo, float* part, int S_cap,
-                       hipStream_t st) {
+                       hipStream_t st, bool reduce) {
   constexpr int RING = decode_ring(XG, SPLIT && !G1, KC);
   using Geo = DecodeGeom<G1, SPLIT, XG, RING, KC>;
   const int nb = cdiv(Nout, kDWRows);
@@ -598,7 +598,7 @@ void launch_decode_dma(int nsplit, const bf16* X, const bf16* X_lo, const int32_
   hipLaunchKernelGGL((decode_dma_kernel<G1, SPLIT, XG, RING, KC>), dim3(grid), dim3(256), Geo::LDS,
                      st, X, X_lo, perm, k, off, W, bias, gate, K, Nout, nb, nsplit, out, out_lo,
                      part, S_cap, N);
-  if (nsplit > 1)
+  if (nsplit > 1 && reduce)
     hipLaunchKernelGGL((decode_reduce_kernel<G1, SPLIT>), dim3(N * nb), dim3(256), 0, st, part,
                        nsplit, S_cap, off, bias, gate, Nout, nb, out, out_lo);
 }
@@ -609,26 +609,27 @@ template <bool G1, bool SPLIT>
 void launch_decode_gemm(bool dma, int nsplit, int xg, const bf16* X, const bf16* X_lo,
                         const int32_t* perm, int k, const int32_t* off, const bf16* W,
                         const bf16* bias, const float* gate, int K, int Nout, int N, void* out,
-                        bf16* out_lo, float* part, int S_cap, hipStream_t st) {
+                        bf16* out_lo, float* part, int S_cap, hipStream_t st,
+                        bool reduce = true) {
   if (dma) {
     // the first GEMM (shorter K) streams better in 512-byte row chunks, one
     // workgroup per CU; the second in 256-byte chunks, two per CU (measured)
     if (G1 && K % 256 == 0 && xg <= 2) {
       if (xg <= 1)
         launch_decode_dma<G1, SPLIT, 1, 256>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K,
-                                             Nout, N, out, out_lo, part, S_cap, st);
+                                             Nout, N, out, out_lo, part, S_cap, st, reduce);
       else
         launch_decode_dma<G1, SPLIT, 2, 256>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K,
-                                             Nout, N, out, out_lo, part, S_cap, st);
+                                             Nout, N, out, out_lo, part, S_cap, st, reduce);
     } else if (xg <= 1) {
       launch_decode_dma<G1, SPLIT, 1, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
-                                           N, out, out_lo, part, S_cap, st);
+                                           N, out, out_lo, part, S_cap, st, reduce);
     } else if (xg == 2) {
       launch_decode_dma<G1, SPLIT, 2, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
-                                           N, out, out_lo, part, S_cap, st);
+                                           N, out, out_lo, part, S_cap, st, reduce);
     } else {
       launch_decode_dma<G1, SPLIT, 4, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
-                                           N, out, out_lo, part, S_cap, st);
+                                           N, out, out_lo, part, S_cap, st, reduce);
     }
     return;
   }
@@ -641,7 +642,9 @@ template <bool SPLIT>
 hipError_t launch_decode(const void* x, const int32_t* perm, const int32_t* off, const float* gate,
                          const void* W1, const void* b1, const void* W2, const void* b2, int d,
                          int d_ff, int N, int k, const Plan& pl, int S_cap, void* hid,
-                         bf16* hid_lo, float* part, void* slot_out, hipStream_t st) {
+                         bf16* hid_lo, float* part, void* slot_out, hipStream_t st,
+                         SplitK* defer) {
+  const bool defer2 = defer != nullptr && pl.dma2 && pl.ks2 > 1;
   profile_mark(3, st);
   launch_decode_gemm<true, SPLIT>(pl.dma1, pl.ks1, pl.xg, (const bf16*)x, nullptr, perm, k, off,
                                   (const bf16*)W1, (const bf16*)b1, nullptr, d, d_ff, N, hid,
@@ -649,7 +652,16 @@ hipError_t launch_decode(const void* x, const int32_t* perm, const int32_t* off,
   profile_mark(4, st);
   launch_decode_gemm<false, SPLIT>(pl.dma2, pl.ks2, pl.xg, (const bf16*)hid, hid_lo, perm, k, off,
                                    (const bf16*)W2, (const bf16*)b2, gate, d_ff, d, N, slot_out,
-                                   nullptr, part, S_cap, st);
+                                   nullptr, part, S_cap, st, !defer2);
+  if (defer2) {
+    defer->part = part;
+    defer->nsplit = pl.ks2;
+    defer->S_cap = S_cap;
+    defer->bias = b2;
+    defer->gate = gate;
+    defer->off = off;
+    defer->N = N;
+  }
   profile_mark(5, st);
   return hipGetLastError();
 }
@@ -682,7 +694,8 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
                              const float* gate, const void* W1, const void* b1, const void* W2,
                              const void* b2, int T, int d, int d_ff, int N, int k, int C,
                              int S_max, int dtype, int flags, void* slot_out,
-                             const FfnScratch& s, hipStream_t st) {
+                             const FfnScratch& s, hipStream_t st, SplitK* defer) {
+  if (defer != nullptr) defer->nsplit = 1;
   if (T == 0 || S_max == 0) return hipSuccess;
   const Plan pl = make_plan(T, d, d_ff, N, k, C, S_max, dtype, flags);
   int4* t1 = (int4*)s.tiles;
@@ -691,9 +704,9 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
   if (pl.path == kPathDecode) {
     if (pl.split)
       return launch_decode<true>(x, perm, off, gate, W1, b1, W2, b2, d, d_ff, N, k, pl, S_max,
-                                 s.hidden, lo, s.part, slot_out, st);
+                                 s.hidden, lo, s.part, slot_out, st, defer);
     return launch_decode<false>(x, perm, off, gate, W1, b1, W2, b2, d, d_ff, N, k, pl, S_max,
-                                s.hidden, nullptr, s.part, slot_out, st);
+                                s.hidden, nullptr, s.part, slot_out, st, defer);
   }
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, off, N, pl.BM,
                      cdiv(d_ff, pl.BN1), cdiv(d, pl.BN2), pl.max1, pl.max2, t1, t2, s.counts);

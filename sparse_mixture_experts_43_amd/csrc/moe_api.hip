@@ -260,11 +260,13 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
                       f.ndrop, f.ds, s);
   if (e != hipSuccess) return hip_status(e);
   profile_mark(2, s);
+  SplitK sk;  // a K-split second GEMM hands its partials straight to the combine
   e = launch_expert_ffn(x, f.perm, f.off, f.gate, W1, b1, W2, b2, T, d, d_ff, N, k, C, S_max,
-                        dtype, flags, f.slot_out, f.fs, s);
+                        dtype, flags, f.slot_out, f.fs, s, &sk);
   if (e != hipSuccess) return hip_status(e);
   const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
-  e = launch_combine(f.slot_out, f.inv, T, d, k, y_dtype, y, s);
+  e = sk.nsplit > 1 ? launch_combine_splitk(sk, f.inv, T, d, k, y_dtype, y, s)
+                    : launch_combine(f.slot_out, f.inv, T, d, k, y_dtype, y, s);
   profile_mark(6, s);
   return hip_status(e);
 }

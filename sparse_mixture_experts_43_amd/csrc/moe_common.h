@@ -144,12 +144,28 @@ hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key
                            int k, int C, int32_t* req, int32_t* cnt, int32_t* off, int32_t* perm,
                            int32_t* inv, float* gate, int32_t* n_dropped,
                            const DispatchScratch& s, hipStream_t st);
+// Second expert GEMM left as K-split fp32 partials (decode path): the combine
+// finishes the slot outputs, gate * (sum_q part[q] + b2), in the same order of
+// operations as the split-K reduction would.
+struct SplitK {
+  const float* part = nullptr;  // [nsplit][S_cap][d]
+  int nsplit = 1;
+  int S_cap = 0;
+  const void* bias = nullptr;   // b2 [N, d] activation dtype, or null
+  const float* gate = nullptr;  // slot gates
+  const int32_t* off = nullptr; // expert offsets [N+1] (slot -> expert for the bias)
+  int N = 0;
+};
+// defer: when not null and the plan splits the second GEMM's K, its reduction
+// is skipped and described in *defer (nsplit > 1) for launch_combine_splitk.
 hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* off,
                              const float* gate, const void* W1, const void* b1, const void* W2,
                              const void* b2, int T, int d, int d_ff, int N, int k, int C,
                              int S_max, int dtype, int flags, void* slot_out,
-                             const FfnScratch& s, hipStream_t st);
+                             const FfnScratch& s, hipStream_t st, SplitK* defer = nullptr);
 hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d, int k,
                           int dtype, void* y, hipStream_t st);
+hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, int d, int k,
+                                 int dtype, void* y, hipStream_t st);
 
 }  // namespace moe

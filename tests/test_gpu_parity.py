@@ -94,6 +94,22 @@ def test_identical_tokens_tie_break(lib):
     assert res["n_dropped"] > 0
 
 
+def test_few_distinct_tokens_select(lib):
+    """40960 pairs from three distinct token rows: an over-full expert's keys
+    take three values, so the threshold bin of the capacity selection holds
+    thousands of equal keys (the selection falls back from its short candidate
+    list to passes over all keys); equal keys keep the lowest tokens."""
+    from gpu_util import run_and_compare
+    from moe_inputs import make_inputs
+    w = Workload("three_token_rows", T=20480, d=64, d_ff=64, N=4, k=2, capacity_factor=0.7,
+                 dtype="bf16", ffn_bias=False, skew="none")
+    inp = make_inputs(w)
+    rows = inp["x"][:3]
+    inp["x"] = rows[torch.arange(w.T) % 3].contiguous()
+    res = run_and_compare(w, lib, inputs=inp, sample_tokens=64)
+    assert res["n_dropped"] > 0
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name", sorted(FULL))
 def test_parity_full_size(lib, name):
