@@ -126,12 +126,16 @@ __global__ __launch_bounds__(256) void transpose_wg_kernel(const bf16* __restric
 // (W_g^T stays in L1/L2), four 32-wide K steps of loads in flight per wave.
 // Partial logits are summed across waves in a fixed order in LDS, then each
 // wave runs the top-k of some of the 16 rows.
-template <int WAVES, int NT>
+// DIRECT (N <= 16): the weight fragments are gathered straight from W_g [d, N]
+// (8 strided 2-byte loads per lane per 32-wide K step, the rows of W_g sit in
+// L1/L2), so no transposed copy of W_g is made first.
+template <int WAVES, int NT, bool DIRECT = false>
 __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ WgT, const float* __restrict__ bias,
     int T, int d, int N, int k, float* __restrict__ logits, int32_t* __restrict__ idx,
     float* __restrict__ w, double* __restrict__ key) {
-  constexpr int U = WAVES >= 16 ? 2 : 4;
+  static_assert(!DIRECT || NT == 1, "direct W_g reads for N <= 16 only");
+  constexpr int U = NT == 1 ? 8 : (WAVES >= 16 ? 2 : 4);  // 32-wide K steps of loads in flight
   constexpr int NP = NT * 16;
   __shared__ float part[WAVES][16][NP];
   __shared__ float Ls[16][NP + 4];
@@ -158,9 +162,19 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
       const int kk = (s0 + u) * 32 + 8 * g;
       const bool ok = (s0 + u) < s_end && kk < d;
       a[u] = (ok && rok) ? *(const bf16x8*)(xr + kk) : z;
+      if constexpr (DIRECT) {
+        // WgT is W_g [d, N] here
+        bf16x8 v = z;
+        if (ok && c16 < N) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        b[u][j] = ok ? *(const bf16x8*)(WgT + (size_t)(16 * j + c16) * d + kk) : z;
+          for (int i = 0; i < 8; ++i) v[i] = kk + i < d ? WgT[(size_t)(kk + i) * N + c16] : (bf16)0.f;
+        }
+        b[u][0] = v;
+      } else {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          b[u][j] = ok ? *(const bf16x8*)(WgT + (size_t)(16 * j + c16) * d + kk) : z;
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -367,15 +381,15 @@ hipError_t launch_bf16(const void* x, const void* W_g, const float* bias, int T,
   return hipGetLastError();
 }
 
-template <int NT>
+template <int NT, bool DIRECT = false>
 void launch_skinny(bool wide, const void* x, const bf16* WgT, const float* bias, int T, int d,
                    int N, int k, float* logits, int32_t* idx, float* w, double* key,
                    hipStream_t st) {
   if (wide)
-    hipLaunchKernelGGL((router_skinny_kernel<16, NT>), dim3(cdiv(T, 16)), dim3(1024), 0, st,
-                       (const bf16*)x, WgT, bias, T, d, N, k, logits, idx, w, key);
+    hipLaunchKernelGGL((router_skinny_kernel<16, NT, DIRECT>), dim3(cdiv(T, 16)), dim3(1024), 0,
+                       st, (const bf16*)x, WgT, bias, T, d, N, k, logits, idx, w, key);
   else
-    hipLaunchKernelGGL((router_skinny_kernel<4, NT>), dim3(cdiv(T, 16)), dim3(256), 0, st,
+    hipLaunchKernelGGL((router_skinny_kernel<4, NT, DIRECT>), dim3(cdiv(T, 16)), dim3(256), 0, st,
                        (const bf16*)x, WgT, bias, T, d, N, k, logits, idx, w, key);
 }
 
@@ -400,6 +414,11 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
     return hipGetLastError();
   }
   const int NP = cdiv(N, 16) * 16;
+  if (NP == 16 && T < 16 * 256) {
+    // few tokens, at most 16 experts: gather W_g directly (no transposed copy)
+    launch_skinny<1, true>(true, x, (const bf16*)W_g, bias, T, d, N, k, logits, idx, w, key, st);
+    return hipGetLastError();
+  }
   bf16* WgT = (bf16*)scratch;
   hipLaunchKernelGGL(transpose_wg_kernel, dim3(cdiv(d, 64), cdiv(NP, 64)), dim3(256), 0, st,
                      (const bf16*)W_g, d, N, NP, WgT);
