@@ -37,6 +37,15 @@ namespace {
 
 // ---------------------------------------------------------------- schedule
 // Tile entry: {expert, first slot of the m-tile, rows in the m-tile, n-tile}.
+// The grouped GEMMs hand XCD x the x-th contiguous eighth of the list, so the
+// list is written band-residue-major: group r (r = 0..7) holds the weight
+// bands (expert e, n-tile nt) with nt % 8 == r, expert by expert, each band
+// with all its m-tiles (so one XCD's L2 serves the band's weight rows). With
+// NT % 8 == 0 every group holds exactly the same m-tiles, so every XCD sees the
+// same mix of full and partly filled tiles, instead of contiguous runs whose
+// cost depends on where the experts' ragged last m-tiles fall. Group r has
+// c_r = #{nt < NT : nt % 8 == r} bands per expert, i.e. total_mt * c_r tiles,
+// so entry p decodes in closed form.
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ off, int N,
                                                         int BM, int NT1, int NT2, int max1,
                                                         int max2, int4* __restrict__ tiles1,
@@ -46,11 +55,11 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
   __shared__ int tmp[17];
   __shared__ int carry;
   if (threadIdx.x == 0) carry = 0;
+  const int l = lane_id(), wv = threadIdx.x / kWave;
   for (int e0 = 0; e0 < N; e0 += 1024) {
     const int e = e0 + threadIdx.x;
     const int mt = (e < N) ? cdiv(off[e + 1] - off[e], BM) : 0;
     // block exclusive scan
-    const int l = lane_id(), wv = threadIdx.x / kWave;
     int x = mt;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -84,19 +93,28 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
     const int mx = pass == 0 ? max1 : max2;
     int4* tl = pass == 0 ? tiles1 : tiles2;
     const int total = min(total_mt * NTn, mx);
-    for (int i = threadIdx.x; i < total; i += 1024) {
-      // expert e: largest e with mtoff[e] * NTn <= i
-      int lo = 0, hi = N - 1;
+    for (int p = threadIdx.x; p < total; p += 1024) {
+      // residue group r of entry p (groups are never empty where p lands)
+      int r = 0, base = 0, c = 0;
+      for (; r < 8; ++r) {
+        c = NTn / 8 + (r < NTn % 8 ? 1 : 0);
+        if (p < base + total_mt * c) break;
+        base += total_mt * c;
+      }
+      const int q = p - base;
+      int lo = 0, hi = N - 1;  // expert: largest e with mtoff[e] * c <= q
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (mtoff[mid] * NTn <= i) lo = mid; else hi = mid - 1;
+        if (mtoff[mid] * c <= q) lo = mid; else hi = mid - 1;
       }
       const int e = lo;
       const int me = mtoff[e + 1] - mtoff[e];
-      const int local = i - mtoff[e] * NTn;
-      const int nt = local / me, mt = local - nt * me;
+      const int local = q - mtoff[e] * c;
+      const int band = local / me;  // the expert's band-th n-tile of residue r
+      const int mt = local - band * me;
+      const int nt = band * 8 + r;
       const int cnt_e = off[e + 1] - off[e];
-      tl[i] = make_int4(e, off[e] + mt * BM, min(BM, cnt_e - mt * BM), nt);
+      tl[p] = make_int4(e, off[e] + mt * BM, min(BM, cnt_e - mt * BM), nt);
     }
     if (threadIdx.x == 0) counts[pass] = total;
   }
@@ -723,9 +741,9 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
     return hipGetLastError();
   }
   if (pl.path == kPathTiledL)
-    return launch_tiled<256, 256, 128, 128, false>(x, perm, gate, W1, b1, W2, b2, d, d_ff, k, pl,
-                                                    s.hidden, nullptr, t1, t2, s.counts, slot_out,
-                                                    s.part, st);
+    return launch_tiled<256, 256, 128, 64, false>(x, perm, gate, W1, b1, W2, b2, d, d_ff, k, pl,
+                                                   s.hidden, nullptr, t1, t2, s.counts, slot_out,
+                                                   s.part, st);
   if (pl.split)
     return launch_tiled<128, 128, 64, 64, true>(x, perm, gate, W1, b1, W2, b2, d, d_ff, k, pl,
                                                  s.hidden, lo, t1, t2, s.counts, slot_out, s.part,

@@ -1,5 +1,5 @@
 // Grouped / plain bf16 GEMM on an LDS-DMA ring, shared by the expert FFN and
-// the wide router. gfx950: global_load_lds_dwordx4, v_mfma_f32_32x32x16_bf16.
+// the wide router. gfx950: global_load_lds_dwordx4, v_mfma_f32_16x16x32_bf16.
 #pragma once
 
 #include "moe_common.h"
@@ -50,10 +50,12 @@ namespace {
 // next tile's first RING-1 stages are requested before the current tile's
 // epilogue, so their latency hides behind it.
 //
-// MFMA operands: the weight fragment is the matrix-core A operand and the
-// token fragment the B operand, so each lane's accumulator holds one token row
-// and 4 consecutive output columns per 32x32 block: the epilogue writes 8-byte
-// (bf16) or 16-byte (fp32) vectors.
+// MFMA: v_mfma_f32_16x16x32_bf16, one per 16x16 block and stage (it holds
+// the matrix cores at a higher clock under the power limit than the 32x32x16
+// form with live data). The weight fragment is the A operand and the token
+// fragment the B operand, so each lane's accumulator holds one token row and 4
+// consecutive output columns per block: the epilogue writes 8-byte (bf16) or
+// 16-byte (fp32) vectors.
 constexpr int kRK = 32;         // K per ring stage
 constexpr int kRing = 4;        // default ring slots
 constexpr int kRowB = kRK * 2;  // bytes per tile row per stage
@@ -155,63 +157,60 @@ struct RingSplit {
   }
 };
 
-// Epilogue of one tile from the accumulators (lane: token row lr of block i,
-// output columns 8q + 4*half + r of block j).
+// Epilogue of one tile from the accumulators. Lane l holds, for token block i
+// and weight block j, token row (2i + wr)*16 + (l & 15) of the tile and the 4
+// consecutive output columns wn0 + 16j + 4*(l >> 4) + r (r = 0..3).
 template <int BM, int BN, int WM, int WN, int MODE, bool SPLIT>
-__device__ __forceinline__ void ring_epilogue(const f32x16 (&acc)[WM / 32][WN / 32], int e,
-                                              int m0, int mcount, int n0, int wr, int wn0,
-                                              int lr, int half, const void* __restrict__ bias,
+__device__ __forceinline__ void ring_epilogue(const f32x4 (&acc)[WM / 16][WN / 16], int e, int m0,
+                                              int mcount, int n0, int wr, int wn0, int l,
+                                              const void* __restrict__ bias,
                                               const float* __restrict__ gate, int Nout,
                                               void* __restrict__ out, bf16* __restrict__ out_lo,
                                               int ldo) {
   constexpr bool G1 = MODE == kEpiGelu;
-  constexpr int MT = WM / 32, NTW = WN / 32;
+  constexpr int MT = WM / 16, NTW = WN / 16;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    const int r = (2 * i + wr) * 32 + lr;  // token blocks alternate between the wave rows
+    const int r = (2 * i + wr) * 16 + (l & 15);  // token blocks alternate between the wave rows
     if (r >= mcount) continue;
     const int slot = m0 + r;
     float g = 1.f;
     if constexpr (MODE == kEpiGate) g = gate[slot];
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn0 + j * 32 + 8 * q + 4 * half;
-        float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-        float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if constexpr (MODE == kEpiLogit) {
-          const float* bf = (const float*)bias;
-          float* o = (float*)out + (size_t)slot * ldo;
-          if (col + 0 < ldo) o[col + 0] = v0 + (bf ? bf[col + 0] : 0.f);
-          if (col + 1 < ldo) o[col + 1] = v1 + (bf ? bf[col + 1] : 0.f);
-          if (col + 2 < ldo) o[col + 2] = v2 + (bf ? bf[col + 2] : 0.f);
-          if (col + 3 < ldo) o[col + 3] = v3 + (bf ? bf[col + 3] : 0.f);
-          continue;
+      const int col = n0 + wn0 + j * 16 + 4 * (l >> 4);
+      float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
+      if constexpr (MODE == kEpiLogit) {
+        const float* bf = (const float*)bias;
+        float* o = (float*)out + (size_t)slot * ldo;
+        if (col + 0 < ldo) o[col + 0] = v0 + (bf ? bf[col + 0] : 0.f);
+        if (col + 1 < ldo) o[col + 1] = v1 + (bf ? bf[col + 1] : 0.f);
+        if (col + 2 < ldo) o[col + 2] = v2 + (bf ? bf[col + 2] : 0.f);
+        if (col + 3 < ldo) o[col + 3] = v3 + (bf ? bf[col + 3] : 0.f);
+        continue;
+      }
+      if (col >= Nout) continue;  // Nout % 4 == 0: a group is all in or all out
+      if (bias != nullptr) {
+        const uint2 bb = *(const uint2*)((const bf16*)bias + (size_t)e * Nout + col);
+        v0 += __builtin_bit_cast(float, bb.x << 16);
+        v1 += __builtin_bit_cast(float, bb.x & 0xFFFF0000u);
+        v2 += __builtin_bit_cast(float, bb.y << 16);
+        v3 += __builtin_bit_cast(float, bb.y & 0xFFFF0000u);
+      }
+      const size_t o = (size_t)slot * Nout + col;
+      if constexpr (G1) {
+        const float h0 = gelu_as(v0), h1 = gelu_as(v1), h2 = gelu_as(v2), h3 = gelu_as(v3);
+        const uint2 hi = make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
+        *(uint2*)((bf16*)out + o) = hi;
+        if constexpr (SPLIT) {
+          const float r0 = h0 - __builtin_bit_cast(float, hi.x << 16);
+          const float r1 = h1 - __builtin_bit_cast(float, hi.x & 0xFFFF0000u);
+          const float r2 = h2 - __builtin_bit_cast(float, hi.y << 16);
+          const float r3 = h3 - __builtin_bit_cast(float, hi.y & 0xFFFF0000u);
+          *(uint2*)(out_lo + o) = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
         }
-        if (col >= Nout) continue;  // Nout % 4 == 0: a group is all in or all out
-        if (bias != nullptr) {
-          const uint2 bb = *(const uint2*)((const bf16*)bias + (size_t)e * Nout + col);
-          v0 += __builtin_bit_cast(float, bb.x << 16);
-          v1 += __builtin_bit_cast(float, bb.x & 0xFFFF0000u);
-          v2 += __builtin_bit_cast(float, bb.y << 16);
-          v3 += __builtin_bit_cast(float, bb.y & 0xFFFF0000u);
-        }
-        const size_t o = (size_t)slot * Nout + col;
-        if constexpr (G1) {
-          const float h0 = gelu_as(v0), h1 = gelu_as(v1), h2 = gelu_as(v2), h3 = gelu_as(v3);
-          const uint2 hi = make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
-          *(uint2*)((bf16*)out + o) = hi;
-          if constexpr (SPLIT) {
-            const float r0 = h0 - __builtin_bit_cast(float, hi.x << 16);
-            const float r1 = h1 - __builtin_bit_cast(float, hi.x & 0xFFFF0000u);
-            const float r2 = h2 - __builtin_bit_cast(float, hi.y << 16);
-            const float r3 = h3 - __builtin_bit_cast(float, hi.y & 0xFFFF0000u);
-            *(uint2*)(out_lo + o) = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
-          }
-        } else {
-          *(f32x4*)((float*)out + o) = f32x4{v0 * g, v1 * g, v2 * g, v3 * g};
-        }
+      } else {
+        *(f32x4*)((float*)out + o) = f32x4{v0 * g, v1 * g, v2 * g, v3 * g};
       }
     }
   }
@@ -246,7 +245,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   constexpr bool G1 = MODE == kEpiGelu;
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int NTH = NW * kWave;
-  constexpr int MT = WM / 32, NTW = WN / 32;
+  constexpr int MT = WM / 16, NTW = WN / 16;  // 16-row token / weight blocks per wave
   constexpr bool ALO = SPLIT && !G1;
   constexpr int AI = BM / (NW * 16);  // A wave-loads per stage
   constexpr int BI = BN / (NW * 16);
@@ -258,6 +257,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   static_assert(AI >= 1 && BI >= 1, "tile too small for the wave count");
   static_assert(RING >= 3 && (RING - 2) * LPS < 64, "ring depth / vmcnt range");
   static_assert(BM / WM == 2, "two wave rows (token blocks alternate between them)");
+  static_assert(MT % 2 == 0, "token blocks are skipped in pairs");
 
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -367,91 +367,88 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
     issue_part(RING - 2, 0);
   };
 
-  // Fragment reads: row R, 16-byte chunk c (= 2*ks + l/32) at position c ^ ((R>>2)&3).
-  const int lr = l & 31;
-  const int half = l >> 5;
+  // Fragment reads (v_mfma_f32_16x16x32_bf16 operands): lane l reads row
+  // 16*blk + (l & 15), 16-byte chunk l >> 4 (K 8*(l>>4) .. +8), which sits at
+  // position (l >> 4) ^ (((l & 15) >> 2) & 3); the 16 lanes of a quarter-wave
+  // hit all 64 banks once.
+  const int pos = (((l >> 4) ^ ((l >> 2) & 3)) * 16);
   int aoffs[MT], boffs[NTW];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) aoffs[i] = ((2 * i + wr) * 32 + lr) * kRowB;
+  for (int i = 0; i < MT; ++i) aoffs[i] = ((2 * i + wr) * 16 + (l & 15)) * kRowB + pos;
 #pragma unroll
-  for (int j = 0; j < NTW; ++j) boffs[j] = (wn0 + j * 32 + lr) * kRowB;
-  const int sw = (lr >> 2) & 3;  // (R >> 2) & 3 with R = 32*x + lr
-  const int pos0 = ((0 + half) ^ sw) * 16;  // ks = 0
-  const int pos1 = ((2 + half) ^ sw) * 16;  // ks = 1
+  for (int j = 0; j < NTW; ++j) boffs[j] = (wn0 + j * 16 + (l & 15)) * kRowB + pos;
 
   bf16x8 af[2][MT], bfr[2][NTW], alf[ALO ? 2 : 1][ALO ? MT : 1];
   // NA: token blocks of this wave that hold rows of the tile (a partly filled
   // tile skips the fragment reads and MFMAs of the empty ones)
-  auto read_frags = [&](int kt, int ks, int set, auto na_c) {
+  auto read_frags = [&](int kt, int set, auto na_c) {
     constexpr int NA = decltype(na_c)::value;
     const unsigned char* st = smem + (kt % RING) * STAGE;
-    const int pos = ks ? pos1 : pos0;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) af[set][i] = *(const bf16x8*)(st + A_OFF + aoffs[i] + pos);
+    for (int i = 0; i < NA; ++i) af[set][i] = *(const bf16x8*)(st + A_OFF + aoffs[i]);
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) bfr[set][j] = *(const bf16x8*)(st + B_OFF + boffs[j] + pos);
+    for (int j = 0; j < NTW; ++j) bfr[set][j] = *(const bf16x8*)(st + B_OFF + boffs[j]);
     if constexpr (ALO) {
 #pragma unroll
-      for (int i = 0; i < NA; ++i) alf[set][i] = *(const bf16x8*)(st + L_OFF + aoffs[i] + pos);
+      for (int i = 0; i < NA; ++i) alf[set][i] = *(const bf16x8*)(st + L_OFF + aoffs[i]);
     }
   };
 
-  // acc[i][j]: token block i x weight block j; lane holds token row lr and
-  // output columns 8*q + 4*half + r (r = 0..3) at acc[i][j][4*q + r].
-  f32x16 acc[MT][NTW];
-  auto mma = [&](int set, auto na_c) {
-    constexpr int NA = decltype(na_c)::value;
+  // acc[i][j]: token block i x weight block j (weight fragment = A operand,
+  // token fragment = B operand of the 16x16x32 MFMA).
+  f32x4 acc[MT][NTW];
+  auto mma = [&](int set, auto lo_c, auto hi_c) {
+    constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
+    for (int i = LO; i < HI; ++i)
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
     if constexpr (ALO) {
 #pragma unroll
-      for (int i = 0; i < NA; ++i)
+      for (int i = LO; i < HI; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], alf[set][i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[set][j], alf[set][i], acc[i][j], 0, 0, 0);
     }
   };
 
-  // the ring steps of one item, for NA active token blocks
+  // the ring steps of one item, for NA active token blocks: step kt multiplies
+  // stage kt (fragments in register set kt & 1, unrolled by two so that the
+  // set is static) in two halves of token blocks; the barrier between them
+  // makes stage kt+1 visible, and its fragments are read during the second half
   auto kloop = [&](auto na_c) {
     constexpr int NA = decltype(na_c)::value;
-    constexpr int NR = NA + NTW + (ALO ? NA : 0);  // fragment reads per half step
-    read_frags(0, 0, 0, na_c);
-    for (int kt = 0; kt < nks; ++kt) {
-      // fragments (kt, ks=0) are in set 0
-      read_frags(kt, 1, 1, na_c);
+    constexpr int H = NA / 2;
+    constexpr int NR = NA + NTW + (ALO ? NA : 0);  // fragment reads per stage
+    constexpr int M1 = H * NTW * (ALO ? 2 : 1);    // MFMAs per half
+    using lo0 = std::integral_constant<int, 0>;
+    using mid = std::integral_constant<int, H>;
+    using hi1 = std::integral_constant<int, NA>;
+    auto step = [&](int kt, auto set_c) {
+      constexpr int SET = decltype(set_c)::value;
       issue_part(kt + RING - 2, 1);
-      mma(0, na_c);
-      // the (kt, ks=1) fragment reads between the first MFMAs, then the
-      // weight-row copies of stage kt+RING-2
-      if constexpr (NA > 0) {
-#pragma unroll
-        for (int q = 0; q < NR; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+      mma(SET, lo0{}, mid{});
+      if constexpr (M1 > 0) {
+        // the weight-row copies of stage kt+RING-2 spread over the first half
 #pragma unroll
         for (int q = 0; q < BI; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, M1 / BI > 0 ? M1 / BI : 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
       // stage kt+1 has landed (only the stages issued after it may still fly)
       // and no wave still reads the slot of stage kt-1
-      lgkm_wait0();
       vm_wait_n<(RING - 3) * LPS>();
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(kt + 1, 0, 0, na_c);  // past the last stage: reads a dead slot, never used
+      read_frags(kt + 1, SET ^ 1, na_c);  // past the last stage: reads a dead slot, never used
       issue_part(kt + RING - 1, 0);
-      mma(1, na_c);
-      // one MFMA, one fragment read of the next stage (so the reads land long
-      // before the next step needs them), then one MFMA, one token-row copy
-      if constexpr (NA > 0) {
+      mma(SET, mid{}, hi1{});
+      if constexpr (M1 > 0) {
+        // one MFMA, one fragment read of the next stage, ...; then the
+        // token-row copies of stage kt+RING-1
 #pragma unroll
         for (int q = 0; q < NR; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -464,7 +461,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      // the next stage's fragments are complete before the next step's MFMAs
+      // (and before this wave passes the next barrier)
+      lgkm_wait0();
+    };
+    read_frags(0, 0, na_c);
+    int kt = 0;
+    for (; kt + 1 < nks; kt += 2) {
+      step(kt, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
     }
+    if (kt < nks) step(kt, std::integral_constant<int, 0>{});
   };
 
   int tile, ke, ps, e, m0, mcount, n0;
@@ -485,25 +492,25 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+      for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      // token blocks of this wave row with rows below mcount
-      const int nb = (mcount + 31) / 32;
+      // token blocks of this wave row with rows below mcount, rounded up to
+      // an even count
+      const int nb = (mcount + 15) / 16;
       int na = (nb - wr + 1) / 2;
+      na = (na + 1) & ~1;
       na = __builtin_amdgcn_readfirstlane(na < 0 ? 0 : (na > MT ? MT : na));
       if (na >= MT) {
         kloop(std::integral_constant<int, MT>{});
-      } else if constexpr (MT == 4) {
+      } else if constexpr (MT == 8) {
         switch (na) {
-          case 3: kloop(std::integral_constant<int, 3>{}); break;
+          case 6: kloop(std::integral_constant<int, 6>{}); break;
+          case 4: kloop(std::integral_constant<int, 4>{}); break;
           case 2: kloop(std::integral_constant<int, 2>{}); break;
-          case 1: kloop(std::integral_constant<int, 1>{}); break;
           default: kloop(std::integral_constant<int, 0>{}); break;
         }
-      } else if constexpr (MT == 2) {
-        if (na == 1) kloop(std::integral_constant<int, 1>{});
+      } else if constexpr (MT == 4) {
+        if (na == 2) kloop(std::integral_constant<int, 2>{});
         else kloop(std::integral_constant<int, 0>{});
       } else {
         kloop(std::integral_constant<int, MT>{});
@@ -525,20 +532,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
     }
 
     if (cps < 0) {
-      ring_epilogue<BM, BN, WM, WN, MODE, SPLIT>(acc, ce, cm0, cmcount, cn0, wr, wn0, lr, half,
-                                                 bias, gate, Nout, out, out_lo, ldo);
+      ring_epilogue<BM, BN, WM, WN, MODE, SPLIT>(acc, ce, cm0, cmcount, cn0, wr, wn0, l, bias,
+                                                 gate, Nout, out, out_lo, ldo);
     } else {
-      // raw partial accumulators as float4 groups (4 consecutive output
-      // columns of one lane), lane-major so every store is one contiguous 1 KB
+      // raw partial accumulators, one float4 per lane and block, lane-major
+      // so every store is one contiguous 1 KB
       f32x4* pp = (f32x4*)(part + (size_t)cps * (BM * BN)) + threadIdx.x;
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            pp[((i * NTW + j) * 4 + q) * NTH] =
-                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        for (int j = 0; j < NTW; ++j) pp[(i * NTW + j) * NTH] = acc[i][j];
     }
     if (!more) break;
   }
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(kReduceThreads) void ring_reduce_kernel(
   constexpr bool G1 = MODE == kEpiGelu;
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int NTH = NW * kWave;
-  constexpr int NTW = WN / 32;
+  constexpr int NTW = WN / 16;
   constexpr int GROUPS = BM * BN / 4;               // float4 groups per tile
   constexpr int GB = GROUPS / kReduceThreads;       // group blocks per tile
   const int nk = K / kRK;
@@ -575,14 +578,14 @@ __global__ __launch_bounds__(kReduceThreads) void ring_reduce_kernel(
     const int tile = xcd * sp.chunk + sp.rounds * sp.per + tau;
     int e, m0, mcount, n0;
     ring_decode_tile<MODE, BM, BN>(tile, tiles, 0, Nout, e, m0, mcount, n0);
-    // group index g = ((i*NTW + j)*4 + q)*NTH + tid of the GEMM lane layout
+    // group index g = (i*NTW + j)*NTH + tid of the GEMM lane layout
     const int g = gb * kReduceThreads + threadIdx.x;
     const int tid = g % NTH;
-    const int ijq = g / NTH;
-    const int q = ijq & 3, j = (ijq >> 2) % NTW, i = (ijq >> 2) / NTW;
+    const int ij = g / NTH;
+    const int j = ij % NTW, i = ij / NTW;
     const int wv = tid / kWave, lane = tid % kWave;
-    const int row = (2 * i + wv / (BN / WN)) * 32 + (lane & 31);
-    const int col = n0 + (wv % (BN / WN)) * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+    const int row = (2 * i + wv / (BN / WN)) * 16 + (lane & 15);
+    const int col = n0 + (wv % (BN / WN)) * WN + j * 16 + 4 * (lane >> 4);
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     // workgroups whose share holds unit u: lo(j) <= u < lo(j+1), i.e. the
     // largest j with j*U < (u+1)*per (U = tail*nk units in the tail)
