@@ -122,23 +122,37 @@ __global__ __launch_bounds__(256) void transpose_wg_kernel(const bf16* __restric
 
 // ---------------------------------------------------------------- skinny router
 // N <= 64 (at most 4 MFMA column tiles): one block = 16 tokens, its WAVES
-// waves split K; x rows and W_g^T rows stream straight from global memory
-// (W_g^T stays in L1/L2), four 32-wide K steps of loads in flight per wave.
-// Partial logits are summed across waves in a fixed order in LDS, then each
-// wave runs the top-k of some of the 16 rows.
-// DIRECT (N <= 16): the weight fragments are gathered straight from W_g [d, N]
-// (8 strided 2-byte loads per lane per 32-wide K step, the rows of W_g sit in
-// L1/L2), so no transposed copy of W_g is made first.
-template <int WAVES, int NT, bool DIRECT = false>
+// waves split K; x rows stream straight from global memory, several 32-wide K
+// steps of loads in flight per wave. Partial logits are summed across waves in
+// a fixed order in LDS, then each wave runs the top-k of some of the 16 rows.
+// Weight fragments (8 consecutive k of one expert per lane, the layout of the
+// MFMA B operand):
+//   LDSW:  the block first copies W_g [d, N] into LDS transposed (row n holds
+//          expert n's d weights, rows padded by 16 bytes so the fragment reads
+//          of 16 rows hit distinct banks); used where N*d is small, so no
+//          separate transpose launch is needed;
+//   else:  from WgT [NP, d] (the transposed copy made by transpose_wg_kernel,
+//          L1/L2-resident).
+inline int wt_ld(int d) { return d + 8; }
+inline size_t wt_lds_bytes(int d, int N) { return (size_t)N * wt_ld(d) * sizeof(bf16); }
+// LDS left for the staged W_g^T next to the 16-wave kernel's static arrays
+// (part[16][16][NP], Ls[16][NP+4] floats)
+constexpr size_t wt_lds_budget(int NP) {
+  return (size_t)160 * 1024 - (size_t)16 * 16 * NP * 4 - (size_t)16 * (NP + 4) * 4 - 1024;
+}
+
+template <int WAVES, int NT, bool LDSW>
 __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
-    const bf16* __restrict__ x, const bf16* __restrict__ WgT, const float* __restrict__ bias,
+    const bf16* __restrict__ x, const bf16* __restrict__ Wsrc, const float* __restrict__ bias,
     int T, int d, int N, int k, float* __restrict__ logits, int32_t* __restrict__ idx,
     float* __restrict__ w, double* __restrict__ key) {
-  static_assert(!DIRECT || NT == 1, "direct W_g reads for N <= 16 only");
   constexpr int U = NT == 1 ? 8 : (WAVES >= 16 ? 2 : 4);  // 32-wide K steps of loads in flight
   constexpr int NP = NT * 16;
   __shared__ float part[WAVES][16][NP];
   __shared__ float Ls[16][NP + 4];
+  extern __shared__ __align__(16) unsigned char wt_smem[];
+  bf16* wt = (bf16*)wt_smem;  // LDSW: [N][d + 8]
+  const int ldw = d + 8;
   const int l = lane_id();
   const int wv = threadIdx.x / kWave;
   const int g = l >> 4, c16 = l & 15;
@@ -146,6 +160,25 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
   const int row = t0 + c16;
   const bool rok = row < T;
   const bf16* xr = x + (size_t)(rok ? row : 0) * d;
+  if constexpr (LDSW) {
+    // W_g [d, N] -> wt[n][k]: coalesced reads of the row-major matrix (16-byte
+    // groups of 8 experts when N % 8 == 0), scattered 2-byte LDS writes
+    if (N % 8 == 0) {
+      const int groups = d * N / 8;
+      for (int q = threadIdx.x; q < groups; q += WAVES * 64) {
+        const bf16x8 v = *(const bf16x8*)(Wsrc + (size_t)q * 8);
+        const int e0 = q * 8, kk = e0 / N, n0 = e0 - kk * N;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wt[(n0 + i) * ldw + kk] = v[i];
+      }
+    } else {
+      for (int q = threadIdx.x; q < d * N; q += WAVES * 64) {
+        const int kk = q / N, n = q - kk * N;
+        wt[n * ldw + kk] = Wsrc[q];
+      }
+    }
+    __syncthreads();
+  }
   const int nsteps = cdiv(d, 32);
   const int spw = cdiv(nsteps, WAVES);
   const int s_begin = wv * spw, s_end = min(nsteps, s_begin + spw);
@@ -162,18 +195,15 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
       const int kk = (s0 + u) * 32 + 8 * g;
       const bool ok = (s0 + u) < s_end && kk < d;
       a[u] = (ok && rok) ? *(const bf16x8*)(xr + kk) : z;
-      if constexpr (DIRECT) {
-        // WgT is W_g [d, N] here
-        bf16x8 v = z;
-        if (ok && c16 < N) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = kk + i < d ? WgT[(size_t)(kk + i) * N + c16] : (bf16)0.f;
+      for (int j = 0; j < NT; ++j) {
+        if constexpr (LDSW) {
+          // d % 8 == 0: a fragment never straddles the end of a row
+          const int n = 16 * j + c16;
+          b[u][j] = (ok && n < N) ? *(const bf16x8*)(wt + n * ldw + kk) : z;
+        } else {
+          b[u][j] = ok ? *(const bf16x8*)(Wsrc + (size_t)(16 * j + c16) * d + kk) : z;
         }
-        b[u][0] = v;
-      } else {
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          b[u][j] = ok ? *(const bf16x8*)(WgT + (size_t)(16 * j + c16) * d + kk) : z;
       }
     }
 #pragma unroll
@@ -381,16 +411,20 @@ hipError_t launch_bf16(const void* x, const void* W_g, const float* bias, int T,
   return hipGetLastError();
 }
 
-template <int NT, bool DIRECT = false>
-void launch_skinny(bool wide, const void* x, const bf16* WgT, const float* bias, int T, int d,
+template <int NT, bool LDSW>
+void launch_skinny(bool wide, const void* x, const bf16* Wsrc, const float* bias, int T, int d,
                    int N, int k, float* logits, int32_t* idx, float* w, double* key,
                    hipStream_t st) {
-  if (wide)
-    hipLaunchKernelGGL((router_skinny_kernel<16, NT, DIRECT>), dim3(cdiv(T, 16)), dim3(1024), 0,
-                       st, (const bf16*)x, WgT, bias, T, d, N, k, logits, idx, w, key);
+  const size_t lds = LDSW ? wt_lds_bytes(d, N) : 0;
+  if constexpr (LDSW) {
+    MOE_SET_LDS_ONCE((router_skinny_kernel<16, NT, true>), (int)wt_lds_budget(NT * 16));
+  }
+  if (wide || LDSW)
+    hipLaunchKernelGGL((router_skinny_kernel<16, NT, LDSW>), dim3(cdiv(T, 16)), dim3(1024), lds,
+                       st, (const bf16*)x, Wsrc, bias, T, d, N, k, logits, idx, w, key);
   else
-    hipLaunchKernelGGL((router_skinny_kernel<4, NT, DIRECT>), dim3(cdiv(T, 16)), dim3(256), 0, st,
-                       (const bf16*)x, WgT, bias, T, d, N, k, logits, idx, w, key);
+    hipLaunchKernelGGL((router_skinny_kernel<4, NT, false>), dim3(cdiv(T, 16)), dim3(256), 0, st,
+                       (const bf16*)x, Wsrc, bias, T, d, N, k, logits, idx, w, key);
 }
 
 }  // namespace
@@ -414,9 +448,14 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
     return hipGetLastError();
   }
   const int NP = cdiv(N, 16) * 16;
-  if (NP == 16 && T < 16 * 256) {
-    // few tokens, at most 16 experts: gather W_g directly (no transposed copy)
-    launch_skinny<1, true>(true, x, (const bf16*)W_g, bias, T, d, N, k, logits, idx, w, key, st);
+  if (NP <= 64 && d % 8 == 0 && wt_lds_bytes(d, N) <= wt_lds_budget(NP)) {
+    // few experts, small W_g: each block stages W_g^T in LDS (no transpose launch)
+    switch (NP / 16) {
+      case 1: launch_skinny<1, true>(true, x, (const bf16*)W_g, bias, T, d, N, k, logits, idx, w, key, st); break;
+      case 2: launch_skinny<2, true>(true, x, (const bf16*)W_g, bias, T, d, N, k, logits, idx, w, key, st); break;
+      case 3: launch_skinny<3, true>(true, x, (const bf16*)W_g, bias, T, d, N, k, logits, idx, w, key, st); break;
+      default: launch_skinny<4, true>(true, x, (const bf16*)W_g, bias, T, d, N, k, logits, idx, w, key, st); break;
+    }
     return hipGetLastError();
   }
   bf16* WgT = (bf16*)scratch;
@@ -426,10 +465,10 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
     // few experts: K split over the waves of a block; more waves when T is small
     const bool wide = T < 16 * 256;
     switch (NP / 16) {
-      case 1: launch_skinny<1>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
-      case 2: launch_skinny<2>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
-      case 3: launch_skinny<3>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
-      default: launch_skinny<4>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
+      case 1: launch_skinny<1, false>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
+      case 2: launch_skinny<2, false>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
+      case 3: launch_skinny<3, false>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
+      default: launch_skinny<4, false>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
     }
     return hipGetLastError();
   }

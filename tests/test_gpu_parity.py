@@ -46,6 +46,8 @@ CASES = [
     ("switch_small_split", 1024, 128, 256, 16, 1, 1.0, "bf16", False, "normal0.5", SPLIT),
     ("fine_small_zipf", 2048, 128, 64, 64, 8, 1.25, "bf16", False, "zipf1.1", 0),
     ("router_N13", 256, 64, 64, 13, 3, 1.0, "bf16", False, "normal0.5", 0),
+    # N*d too large to stage W_g^T in LDS: the transposed-copy router path
+    ("router_transposed_N64", 256, 768, 64, 64, 2, 1.0, "bf16", False, "normal0.5", 0),
     ("dense_k_eq_N", 128, 64, 128, 4, 4, 0.0, "bf16", False, "none", 0),
     ("single_token", 1, 64, 64, 8, 2, 0.0, "bf16", False, "none", 0),
     ("capacity_one", 64, 64, 64, 8, 2, 0.01, "bf16", False, "zipf1.1", 0),
