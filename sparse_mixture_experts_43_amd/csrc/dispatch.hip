@@ -51,6 +51,21 @@ __device__ __forceinline__ unsigned long long match_peers(int v, bool valid) {
   return peers;
 }
 
+// The same for values below 2^nbits, nbits <= 10 uniform across the wave:
+// expert ids need only ceil(log2 N) bits.
+__device__ __forceinline__ unsigned long long match_peers_n(int v, bool valid, int nbits) {
+  unsigned long long peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (v >> b) & 1;
+    const unsigned long long m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+// bits of an expert id (N <= 1024)
+__device__ __forceinline__ int id_bits(int N) { return N > 1 ? 32 - __clz(N - 1) : 0; }
+
 // Block-wide exclusive scan (blockDim.x multiple of 64, <= 1024). `tmp` holds
 // 17 ints of LDS. Returns the exclusive prefix; *total gets the block sum.
 __device__ int block_scan_excl(int v, int* tmp, int* total) {
@@ -84,16 +99,18 @@ __device__ int block_scan_excl(int v, int* tmp, int* total) {
 // One wave walks pairs [p0, p1) in order, 64 at a time; `cnt` (LDS, per
 // expert) holds running counts that start at the caller's bases. For each pair
 // `emit(p, e, pos)` gets cnt[e] at the pair's turn. Expert ids outside [0, N)
-// are skipped, so bad ids cannot index out of range.
-template <typename Emit>
-__device__ __forceinline__ void walk_pairs(const int32_t* __restrict__ idx, int p0, int p1, int N,
+// are skipped, so bad ids cannot index out of range. `idx` is the global
+// int32 array or an int16 copy in LDS.
+template <typename Id, typename Emit>
+__device__ __forceinline__ void walk_pairs(const Id* __restrict__ idx, int p0, int p1, int N,
                                            int* cnt, Emit emit) {
   const int l = lane_id();
+  const int nbits = id_bits(N);
   for (int c0 = p0; c0 < p1; c0 += kWave) {
     const int p = c0 + l;
     const int e = (p < p1) ? idx[p] : 0;
     const bool valid = p < p1 && (unsigned)e < (unsigned)N;
-    const unsigned long long peers = match_peers<10>(e, valid);  // expert ids < 1024
+    const unsigned long long peers = match_peers_n(e, valid, nbits);
     const int before = __popcll(peers & lanemask_lt());
     int base = 0;
     if (valid) base = cnt[e];
@@ -115,10 +132,14 @@ __device__ __forceinline__ void write_slot(int32_t* perm, int32_t* inv, float* g
 }
 
 // ------------------------------------------------------------ fused (small P)
-// One block of 16 waves; wave v walks a contiguous range of pairs twice:
-// first counting per expert, then (after the block turns counts into bases)
-// placing each pair. With no possible overflow (C >= T) the slot of a pair is
-// its bucket position, so perm / inv / gate are written here directly.
+// One block of 16 waves. The expert ids are first copied into LDS as int16
+// (-1 for ids outside [0, N)); wave v then walks a contiguous range of pairs
+// twice from LDS: first counting per expert, then (after the block turns
+// counts into bases) recording each pair's position in place of its id. A last
+// parallel pass writes the outputs with coalesced reads of w / key: with no
+// possible overflow (C >= T) the slot of a pair is its bucket position, so
+// perm / inv / gate are written directly; otherwise the request-ordered
+// bucket and its keys.
 __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ w, const double* __restrict__ key,
     int P, int N, int C, int direct, int32_t* __restrict__ req, int32_t* __restrict__ cnt,
@@ -126,18 +147,23 @@ __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
     int32_t* __restrict__ bucket, unsigned long long* __restrict__ codes,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, float* __restrict__ gate) {
   constexpr int NWV = kScanThreads / kWave;
-  extern __shared__ int fsm[];  // [NWV][N] counters, then [N] request offsets
+  extern __shared__ int fsm[];  // [NWV][N] counters, [N] request offsets, then int16 ids[P]
   __shared__ int tmp[17];
   __shared__ int carry[2];
   const int wv = threadIdx.x / kWave;
   const int l = lane_id();
   int* my = fsm + wv * N;
   int* sh_reqoff = fsm + NWV * N;
+  int16_t* sid = (int16_t*)(fsm + NWV * N + N);
+  for (int p = threadIdx.x; p < P; p += kScanThreads) {
+    const int e = idx[p];
+    sid[p] = (unsigned)e < (unsigned)N ? (int16_t)e : (int16_t)-1;
+  }
   const int span = cdiv(cdiv(P, NWV), kWave) * kWave;
   const int p0 = min(P, wv * span), p1 = min(P, p0 + span);
   for (int e = l; e < N; e += kWave) my[e] = 0;
-  __builtin_amdgcn_wave_barrier();
-  walk_pairs(idx, p0, p1, N, my, [](int, int, int) {});
+  __syncthreads();
+  walk_pairs(sid, p0, p1, N, my, [](int, int, int) {});
   if (threadIdx.x == 0) carry[0] = carry[1] = 0;
   __syncthreads();
   // per expert: totals, bases across waves, expert offsets
@@ -176,17 +202,20 @@ __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
   }
   for (int e = l; e < N; e += kWave) my[e] += sh_reqoff[e];
   __builtin_amdgcn_wave_barrier();
-  if (direct) {
-    walk_pairs(idx, p0, p1, N, my,
-               [&](int p, int, int pos) { write_slot(perm, inv, gate, w, p, pos); });
-  } else {
-    walk_pairs(idx, p0, p1, N, my, [&](int p, int, int pos) {
-      bucket[pos] = p;
-      codes[pos] = key_code(key[p]);
-    });
+  // positions (< P <= 32768) replace the ids of valid pairs
+  walk_pairs(sid, p0, p1, N, my, [&](int p, int, int pos) { sid[p] = (int16_t)pos; });
+  __syncthreads();
+  for (int p = threadIdx.x; p < P; p += kScanThreads) {
+    const int s = sid[p];
+    if (s < 0) {
+      inv[p] = -1;
+    } else if (direct) {
+      write_slot(perm, inv, gate, w, p, s);
+    } else {
+      bucket[s] = p;
+      codes[s] = key_code(key[p]);
+    }
   }
-  for (int p = p0 + l; p < p1; p += kWave)
-    if ((unsigned)idx[p] >= (unsigned)N) inv[p] = -1;
 }
 
 // ------------------------------------------------------------ large P: hist
@@ -588,7 +617,8 @@ hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key
   const bool can_drop = C < T;
   const bool fused = P <= kFusedMaxPairs;
   if (fused) {
-    const size_t lds = ((size_t)(kScanThreads / kWave) * N + N) * sizeof(int);
+    const size_t lds = ((size_t)(kScanThreads / kWave) * N + N) * sizeof(int) +
+                       (size_t)P * sizeof(int16_t);
     MOE_SET_LDS_ONCE(fused_dispatch_kernel, 160 * 1024);
     hipLaunchKernelGGL(fused_dispatch_kernel, dim3(1), dim3(kScanThreads), lds, st, idx, w, key, P,
                        N, C, can_drop ? 0 : 1, req, cnt, off, s.reqoff, n_dropped, s.bucket,

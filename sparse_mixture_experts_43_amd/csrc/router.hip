@@ -100,6 +100,61 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, 
 }
 
 
+// N <= 16: the same as topk_row with one 16-lane group per token row (lane c
+// of the group holds expert c), so a wave serves 4 rows. The reductions are
+// the xor butterflies of topk_row restricted to the 16 lanes that can hold an
+// expert (the other lanes there only add zeros / lose every comparison), so
+// the results are identical. Every lane of the wave takes part in the
+// shuffles; `active` only gates the stores.
+__device__ __forceinline__ void topk_row16(const float* __restrict__ Lrow, bool active, int N,
+                                           int k, int t, float* __restrict__ logits,
+                                           int32_t* __restrict__ idx, float* __restrict__ w,
+                                           double* __restrict__ key) {
+  const int c = lane_id() & 15;
+  const bool has = c < N;
+  const float v = has ? Lrow[c] : -INFINITY;
+  if (active && has && logits != nullptr) logits[(size_t)t * N + c] = v;
+  float m = v;
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+  const double md = (double)m;
+  double s = has ? exp((double)v - md) : 0.0;
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
+  const double lse = md + log(s);
+  bool taken = false;
+  float my_v = 0.f;
+  int my_n = 0;
+  double my_p = 0.0, psum = 0.0;
+  for (int j = 0; j < k; ++j) {
+    const bool cand = has && !taken;
+    float bv = cand ? v : -INFINITY;
+    int bn = cand ? c : 0x7fffffff;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 16);
+      const int on = __shfl_xor(bn, o, 16);
+      if (ov > bv || (ov == bv && on < bn)) {
+        bv = ov;
+        bn = on;
+      }
+    }
+    if (bn == c) taken = true;
+    const double pj = exp((double)bv - md);
+    psum += pj;
+    if (c == j) {
+      my_v = bv;
+      my_n = bn;
+      my_p = pj;
+    }
+  }
+  if (active && c < k) {
+    idx[(size_t)t * k + c] = my_n;
+    w[(size_t)t * k + c] = (float)(my_p / psum);
+    key[(size_t)t * k + c] = (double)my_v - lse;
+  }
+}
+
 // ---------------------------------------------------------------- W_g transpose
 // W_g [d, N] (N-contiguous) -> WgT [NP, d] (K-contiguous, rows n >= N zero), the
 // layout the MFMA B operand wants: 8 consecutive k of one expert per lane.
@@ -160,16 +215,44 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
   const int row = t0 + c16;
   const bool rok = row < T;
   const bf16* xr = x + (size_t)(rok ? row : 0) * d;
+  const int nsteps = cdiv(d, 32);
+  const int spw = cdiv(nsteps, WAVES);
+  const int s_begin = wv * spw, s_end = min(nsteps, s_begin + spw);
+  bf16x8 z;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) z[q] = (bf16)0.f;
+  bf16x8 a[U];
+  auto load_x = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = (s0 + u) * 32 + 8 * g;
+      const bool ok = (s0 + u) < s_end && kk < d;
+      a[u] = (ok && rok) ? *(const bf16x8*)(xr + kk) : z;
+    }
+  };
+  load_x(s_begin);  // the first x fragments fly while W_g is staged
   if constexpr (LDSW) {
     // W_g [d, N] -> wt[n][k]: coalesced reads of the row-major matrix (16-byte
     // groups of 8 experts when N % 8 == 0), scattered 2-byte LDS writes
     if (N % 8 == 0) {
+      // batches of 8 groups per thread, the batch's loads issued first
       const int groups = d * N / 8;
-      for (int q = threadIdx.x; q < groups; q += WAVES * 64) {
-        const bf16x8 v = *(const bf16x8*)(Wsrc + (size_t)q * 8);
-        const int e0 = q * 8, kk = e0 / N, n0 = e0 - kk * N;
+      for (int q0 = 0; q0 < groups; q0 += 8 * WAVES * 64) {
+        bf16x8 v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wt[(n0 + i) * ldw + kk] = v[i];
+        for (int u = 0; u < 8; ++u) {
+          const int q = q0 + u * WAVES * 64 + (int)threadIdx.x;
+          if (q < groups) v[u] = *(const bf16x8*)(Wsrc + (size_t)q * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int q = q0 + u * WAVES * 64 + (int)threadIdx.x;
+          if (q < groups) {
+            const int e0 = q * 8, kk = e0 / N, n0 = e0 - kk * N;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wt[(n0 + i) * ldw + kk] = v[u][i];
+          }
+        }
       }
     } else {
       for (int q = threadIdx.x; q < d * N; q += WAVES * 64) {
@@ -179,22 +262,16 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
     }
     __syncthreads();
   }
-  const int nsteps = cdiv(d, 32);
-  const int spw = cdiv(nsteps, WAVES);
-  const int s_begin = wv * spw, s_end = min(nsteps, s_begin + spw);
   f32x4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  bf16x8 z;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) z[q] = (bf16)0.f;
   for (int s0 = s_begin; s0 < s_end; s0 += U) {
-    bf16x8 a[U], b[U][NT];
+    if (s0 != s_begin) load_x(s0);
+    bf16x8 b[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kk = (s0 + u) * 32 + 8 * g;
       const bool ok = (s0 + u) < s_end && kk < d;
-      a[u] = (ok && rok) ? *(const bf16x8*)(xr + kk) : z;
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         if constexpr (LDSW) {
@@ -226,9 +303,18 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
     Ls[r][n] = sum + ((bias != nullptr && n < N) ? bias[n] : 0.f);
   }
   __syncthreads();
-  for (int r = wv; r < 16; r += WAVES) {
-    const int t = t0 + r;
-    if (t < T) topk_row(&Ls[r][0], N, k, t, logits, idx, w, key);
+  if constexpr (NT == 1) {
+    // 4 rows per wave in 16-lane groups (waves 0..3)
+    if (wv < 4) {
+      const int r = wv * 4 + (l >> 4);
+      const int t = t0 + r;
+      topk_row16(&Ls[r][0], t < T, N, k, t, logits, idx, w, key);
+    }
+  } else {
+    for (int r = wv; r < 16; r += WAVES) {
+      const int t = t0 + r;
+      if (t < T) topk_row(&Ls[r][0], N, k, t, logits, idx, w, key);
+    }
   }
 }
 
