@@ -7,6 +7,7 @@ does, and the two share no code.
 from .moe_ref import (  # noqa: F401
     Dispatch,
     Routing,
+    RoutingStats,
     capacity,
     capacity_dispatch,
     combine,
@@ -14,7 +15,9 @@ from .moe_ref import (  # noqa: F401
     expert_slots_out,
     gelu,
     moe_forward,
+    renormalise_survivors,
     route_topk,
+    routing_stats,
     router_logits,
     to_f64,
 )

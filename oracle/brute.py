@@ -12,6 +12,12 @@ probability itself (not the log-domain key), one expert at a time, exactly as
 the [Wiki] worked example ranks requests. Expert modules are torch.nn layers in
 float64 (nn.Linear stores weights [out, in]; nn.GELU() is the erf form).
 
+The drop-policy variants are stated the same way: first-come capacity as the
+[Wiki] pseudocode's dispatch loop (tokens in order, each token's picks in
+order, an expert's buffer accepts while it holds fewer than C), survivor
+renormalisation and identity fallback as plain per-token loops. The routing
+statistics are stated with pure-Python sums over tokens and picks.
+
 Only for small T, d, d_ff, N (pure-Python loops over tokens and experts).
 """
 from __future__ import annotations
@@ -51,12 +57,14 @@ def make_experts(W1, b1, W2, b2) -> List[Callable]:
     return experts
 
 
-def brute_moe(x, logits, k: int, C: Optional[int], experts: List[Callable]):
+def brute_moe(x, logits, k: int, C: Optional[int], experts: List[Callable],
+              first_come: bool = False, renorm: bool = False, identity: bool = False):
     """Dense-then-mask MoE forward.
 
     logits: [T, N] router logits (float64 or exactly widened fp32).
     C: per-expert capacity, or None for no limit.
     experts: list of callables mapping a float64 [M, d] tensor to [M, d].
+    first_come / renorm / identity: the drop-policy variants.
     Returns (y [T, d] float64 numpy, kept set {(t, e)}, picks {t: [(e, w)]}).
     """
     X = _f64(x)
@@ -72,17 +80,60 @@ def brute_moe(x, logits, k: int, C: Optional[int], experts: List[Callable]):
         tot = sum(float(probs[t, e]) for e in chosen)
         picks[t] = [(e, float(probs[t, e]) / tot) for e in chosen]
     kept = set()
-    for e in range(N):
-        reqs = [(float(probs[t, e]), t) for t in range(T) if any(pe == e for pe, _ in picks[t])]
-        reqs.sort(key=lambda r: (-r[0], r[1]))  # highest score first, then lower token
-        lim = len(reqs) if C is None else C
-        for _, t in reqs[:lim]:
-            kept.add((t, e))
+    if first_come:
+        buffers = {e: [] for e in range(N)}
+        for t in range(T):
+            for e, _ in picks[t]:
+                if C is None or len(buffers[e]) < C:
+                    buffers[e].append(t)
+                    kept.add((t, e))
+    else:
+        for e in range(N):
+            reqs = [(float(probs[t, e]), t) for t in range(T)
+                    if any(pe == e for pe, _ in picks[t])]
+            reqs.sort(key=lambda r: (-r[0], r[1]))  # highest score first, then lower token
+            lim = len(reqs) if C is None else C
+            for _, t in reqs[:lim]:
+                kept.add((t, e))
+    gates = {}
+    for t in range(T):
+        survivors = [(e, w) for e, w in picks[t] if (t, e) in kept]
+        scale = 1.0
+        if renorm and survivors and len(survivors) < len(picks[t]):
+            scale = 1.0 / sum(w for _, w in survivors)
+        for e, w in survivors:
+            gates[(t, e)] = w * scale
     dense = [experts[e](X).detach() for e in range(N)]  # every expert on every token
     y = torch.zeros_like(X)
     for e in range(N):
         mask = torch.tensor([(t, e) in kept for t in range(T)], dtype=torch.bool)
-        gate = torch.tensor([next((w for pe, w in picks[t] if pe == e), 0.0) for t in range(T)],
-                            dtype=torch.float64)
+        gate = torch.tensor([gates.get((t, e), 0.0) for t in range(T)], dtype=torch.float64)
         y += (mask.to(torch.float64) * gate)[:, None] * dense[e]
+    if identity:
+        for t in range(T):
+            if not any((t, e) in kept for e, _ in picks[t]):
+                y[t] = X[t]
     return y.numpy(), kept, picks
+
+
+def brute_routing_stats(logits, k: int):
+    """(f, P, aux, z) with pure-Python loops: f_e = picks of e / (T*k), P_e =
+    mean softmax probability, aux = N * sum f_e P_e, z = mean lse^2."""
+    L = _f64(logits)
+    T, N = L.shape
+    counts = [0] * N
+    psum = [0.0] * N
+    zsum = 0.0
+    for t in range(T):
+        row = [float(L[t, e]) for e in range(N)]
+        m = max(row)
+        lse = m + math.log(sum(math.exp(v - m) for v in row))
+        zsum += lse * lse
+        for e in range(N):
+            psum[e] += math.exp(row[e] - lse)
+        order = sorted(range(N), key=lambda e: (-row[e], e))
+        for e in order[:k]:
+            counts[e] += 1
+    f = [c / (T * k) for c in counts]
+    P = [s / T for s in psum]
+    return f, P, N * sum(a * b for a, b in zip(f, P)), zsum / T

@@ -40,6 +40,18 @@ reason in the design notes of the repository):
   R6 GELU is the exact erf form (nn.GELU default in [Arch] and [Rise]).
   R7 slots are ordered by expert ascending, tokens ascending inside an expert
      (the append order of the [Wiki] pseudocode).
+  R8 routing statistics: f_e = share of the T*k top-k picks (before capacity)
+     that chose expert e, so sum_e f_e = 1 ([Wiki] normalisation; the code of
+     [Scaling] and [Rise] averages the k-hot mask over tokens, which is k*f_e);
+     P_e = mean over tokens of the full softmax probability; aux = N * sum_e
+     f_e P_e without the training coefficient (1 at uniform routing); z = mean
+     over tokens of lse_t^2 without its coefficient.
+  R9 drop-policy variants, each off by default: (a) first-come capacity keeps
+     each expert's first C requests in token order (the arrival order of the
+     [Wiki] pseudocode's dispatch loop); (b) survivor renormalisation divides a
+     token's kept weights by their sum when it lost a pick ([Wiki] worked
+     example: weight 1.0 on E2's output for x4); (c) identity fallback gives a
+     token that lost every pick y[t] = x[t] (the [Wiki] pseudocode's fallback).
 
 Every function here is pinned by tests under tests/ against facts the pages
 or the mathematics fix (see tests/test_oracle_pins.py). The bf16 rounding of
@@ -68,6 +80,9 @@ __all__ = [
     "moe_forward",
     "Routing",
     "Dispatch",
+    "RoutingStats",
+    "routing_stats",
+    "renormalise_survivors",
 ]
 
 
@@ -133,6 +148,34 @@ def route_topk(L, k: int) -> Routing:
 
 
 # --------------------------------------------------------------------------
+# Forward routing statistics: [Wiki] step 8 and "The load-balancing auxiliary
+# loss" (f_e, P_e, N * sum f_e P_e, minimum 1 when f = P = 1/N); [Arch]
+# "Auxiliary Load Balancing Loss" and "Importance Loss and Z-Loss" (z-loss over
+# the tokens' log-sum-exp); [Scaling] "Training Dynamics and Stability" (z-loss
+# as the batch mean of the squared log-sum-exp).  Reading R8.
+# --------------------------------------------------------------------------
+@dataclass
+class RoutingStats:
+    f: np.ndarray  # [N] share of the T*k top-k picks that chose each expert (sum 1)
+    P: np.ndarray  # [N] mean softmax probability of each expert over the tokens (sum 1)
+    aux: float  # N * sum_e f_e * P_e
+    z: float  # mean over tokens of lse_t^2
+
+
+def routing_stats(L, idx) -> RoutingStats:
+    L = np.asarray(L, dtype=np.float64)
+    idx = np.asarray(idx)
+    T, N = L.shape
+    k = idx.shape[1]
+    m = L.max(axis=1)
+    lse = m + np.log(np.exp(L - m[:, None]).sum(axis=1))
+    probs = np.exp(L - lse[:, None])
+    f = np.bincount(idx.reshape(-1), minlength=N).astype(np.float64) / (T * k)
+    P = probs.mean(axis=0)
+    return RoutingStats(f=f, P=P, aux=float(N * np.dot(f, P)), z=float(np.mean(lse * lse)))
+
+
+# --------------------------------------------------------------------------
 # Capacity C.  [Wiki] "Communication cost in distributed settings":
 # C = gamma * k * T / N.  Reading R2 for rounding and "no limit".
 # --------------------------------------------------------------------------
@@ -176,7 +219,9 @@ class Dispatch:
 # E3 drops x4 at 0.286).  Readings R3 (rank by the float64 log-probability
 # key, ties to the lower token) and R7 (slot order).
 # --------------------------------------------------------------------------
-def capacity_dispatch(idx, key, w, N: int, C: int) -> Dispatch:
+def capacity_dispatch(idx, key, w, N: int, C: int, first_come: bool = False) -> Dispatch:
+    """``first_come`` (reading R9a): keep each expert's first C requests in token
+    order instead of the C highest keys."""
     idx = np.asarray(idx)
     key = np.asarray(key, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
@@ -193,8 +238,9 @@ def capacity_dispatch(idx, key, w, N: int, C: int) -> Dispatch:
             perm_parts.append(np.zeros(0, dtype=np.int64))
             continue
         kap = key[t_e, j_e]
-        # primary: key descending; secondary: token ascending
-        rank = np.lexsort((t_e, -kap))
+        # primary: key descending; secondary: token ascending (first-come:
+        # token ascending only)
+        rank = np.arange(len(t_e)) if first_come else np.lexsort((t_e, -kap))
         keep = np.sort(rank[:C])  # back to token-ascending order (R7)
         cnt[e] = len(keep)
         perm_parts.append(t_e[keep].astype(np.int64) * k + j_e[keep])
@@ -205,6 +251,25 @@ def capacity_dispatch(idx, key, w, N: int, C: int) -> Dispatch:
     slot_gate = w.reshape(-1)[perm] if len(perm) else np.zeros(0)
     return Dispatch(C=C, req_counts=req, counts=cnt, offsets=offsets, perm=perm, inv=inv,
                     slot_gate=slot_gate, n_dropped=int(P - len(perm)))
+
+
+def renormalise_survivors(disp: Dispatch, w, k: int) -> Dispatch:
+    """Reading R9b: a token that lost at least one pick but kept some gets its
+    kept weights divided by their sum ([Wiki] worked example: x4 keeps only
+    E2, with weight 1.0). Tokens that kept every pick are left unchanged."""
+    w = np.asarray(w, dtype=np.float64).reshape(-1, k)
+    gate = disp.slot_gate.copy()
+    inv = disp.inv.reshape(-1, k)
+    for t in range(inv.shape[0]):
+        kept = inv[t] >= 0
+        if kept.all() or not kept.any():
+            continue
+        tot = w[t, kept].sum()
+        for j in np.nonzero(kept)[0]:
+            gate[inv[t, j]] = w[t, j] / tot
+    return Dispatch(C=disp.C, req_counts=disp.req_counts, counts=disp.counts,
+                    offsets=disp.offsets, perm=disp.perm, inv=disp.inv, slot_gate=gate,
+                    n_dropped=disp.n_dropped)
 
 
 # --------------------------------------------------------------------------
@@ -276,14 +341,18 @@ def expert_slots_out(x, disp: Dispatch, k: int, W1, b1, W2, b2,
 # Readings R4 (dropped pair contributes zero) and R5 (all dropped -> 0).
 # --------------------------------------------------------------------------
 def combine(slot_out, disp: Dispatch, T: int, k: int, d: int,
-            tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+            tokens: Optional[Sequence[int]] = None, x_fallback=None) -> np.ndarray:
     """y[t] = sum over kept j of w[t,j] * out[slot(t,j)]; rows for ``tokens`` only if given.
 
-    ``slot_out`` is either an [S, d] array or a dict slot -> row.
+    ``slot_out`` is either an [S, d] array or a dict slot -> row. ``x_fallback``
+    (reading R9c): a token whose every pick was dropped gets x[t] instead of 0.
     """
     toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     y = np.zeros((len(toks), d))
     for i, t in enumerate(toks):
+        if x_fallback is not None and np.all(disp.inv[t * k:(t + 1) * k] < 0):
+            y[i] = to_f64(x_fallback[int(t)])
+            continue
         for j in range(k):
             s = disp.inv[t * k + j]
             if s < 0:
@@ -294,7 +363,8 @@ def combine(slot_out, disp: Dispatch, T: int, k: int, d: int,
 
 def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: float,
                 logits: Optional[np.ndarray] = None, C: Optional[int] = None,
-                tokens: Optional[Sequence[int]] = None):
+                tokens: Optional[Sequence[int]] = None, first_come: bool = False,
+                renorm_survivors: bool = False, identity_fallback: bool = False):
     """Whole layer forward ([Wiki] MoE_Layer, steps 1-7).
 
     ``logits``: when given (e.g. another implementation's fp32 router logits,
@@ -302,6 +372,8 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
     ``C``: explicit capacity (the worked example gives C directly).
     ``tokens``: evaluate the output rows for these tokens only; routing and
     capacity still use every token, since capacity ranks across tokens.
+    ``first_come``, ``renorm_survivors``, ``identity_fallback``: the drop-policy
+    variants of reading R9.
 
     Returns dict with y ([T,d] or [len(tokens), d]), logits, routing, dispatch.
     """
@@ -313,15 +385,18 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
     r = route_topk(L, k)
     if C is None:
         C = capacity(T, N, k, capacity_factor)
-    disp = capacity_dispatch(r.idx, r.key, r.w, N, C)
+    disp = capacity_dispatch(r.idx, r.key, r.w, N, C, first_come=first_come)
+    if renorm_survivors:
+        disp = renormalise_survivors(disp, r.w, k)
+    xf = X if identity_fallback else None
     if tokens is None:
         O = expert_slots_out(X, disp, k, W1, b1, W2, b2)
-        y = combine(O, disp, T, k, d)
+        y = combine(O, disp, T, k, d, x_fallback=xf)
     else:
         toks = np.asarray(tokens, dtype=np.int64)
         pairs = (toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)
         slots = disp.inv[pairs]
         slots = slots[slots >= 0]
         O = expert_slots_out(X, disp, k, W1, b1, W2, b2, slots=slots)
-        y = combine(O, disp, T, k, d, tokens=toks)
+        y = combine(O, disp, T, k, d, tokens=toks, x_fallback=xf)
     return {"y": y, "logits": L, "routing": r, "dispatch": disp}

@@ -20,7 +20,16 @@ Pins used (none of them re-types the oracle's own formula):
     capacity by the softmax probability with pure-Python sorting;
   * the linear-expert closed form of the practice exercise on the "How Sparse
     Routing Scales Transformers" page;
-  * dispatch invariants (counts <= C, slot bookkeeping, score order at cuts).
+  * dispatch invariants (counts <= C, slot bookkeeping, score order at cuts);
+  * routing statistics: the wiki page's closed form (aux = 1 when f = P = 1/N,
+    here from circulant logits), a collapsed router (aux -> N), the code form
+    of the "Scaling" and "Rise" pages (k-hot mask averaged over tokens, i.e.
+    k * f) evaluated with torch ops, torch.logsumexp for the z term, and
+    pure-Python sums (oracle/brute.py);
+  * drop policies: the worked example's survivor renormalisation (weight 1.0
+    on E2 for x4, on E4 for x2), first-come capacity as the pseudocode's
+    arrival-order loop (worked example and brute force), identity fallback
+    for a token that loses every pick.
 """
 from __future__ import annotations
 
@@ -33,7 +42,7 @@ import pytest
 import torch
 
 import oracle.moe_ref as M
-from oracle.brute import brute_moe, make_experts
+from oracle.brute import brute_moe, brute_routing_stats, make_experts
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -245,10 +254,147 @@ def pin_capacity_ties_lower_token():
     assert disp.inv.tolist() == [0, 1, -1, -1]
 
 
+def pin_routing_stats_uniform():
+    # circulant logits: token t prefers expert t mod N, then (t+1) mod N; with
+    # k = 2 every expert gets the same share of picks and, by symmetry, the same
+    # mean probability: f = P = 1/N and aux = N * N * (1/N)^2 = 1 (wiki page)
+    N, reps, k = 8, 3, 2
+    T = N * reps
+    L = np.zeros((T, N))
+    for t in range(T):
+        L[t, t % N] = 3.0
+        L[t, (t + 1) % N] = 2.0
+    r = M.route_topk(L, k)
+    st = M.routing_stats(L, r.idx)
+    np.testing.assert_allclose(st.f, 1.0 / N, rtol=1e-15)
+    np.testing.assert_allclose(st.P, 1.0 / N, rtol=1e-12)
+    assert abs(st.aux - 1.0) < 1e-12
+    lse = math.log(math.exp(3.0) + math.exp(2.0) + (N - 2))
+    assert abs(st.z - lse * lse) < 1e-12
+    # all-zero logits: lse = log N for every token
+    st0 = M.routing_stats(np.zeros((5, N)), np.zeros((5, 1), dtype=np.int32))
+    assert abs(st0.z - math.log(N) ** 2) < 1e-12
+
+
+def pin_routing_stats_collapse():
+    # every token strongly prefers expert 0: f = (1, 0, ...), aux = N * P_0 -> N
+    N, T = 6, 40
+    L = np.zeros((T, N))
+    L[:, 0] = 40.0
+    r = M.route_topk(L, 1)
+    st = M.routing_stats(L, r.idx)
+    assert st.f.tolist() == [1.0] + [0.0] * (N - 1)
+    p0 = 1.0 / (1.0 + (N - 1) * math.exp(-40.0))
+    assert abs(st.aux - N * p0) < 1e-12
+
+
+def pin_routing_stats_code_form():
+    # the load-balance snippets of the "Scaling" and "Rise" pages: a k-hot mask
+    # averaged over tokens (sums to k) times the mean softmax, times N; the
+    # z term with torch.logsumexp
+    rng = np.random.default_rng(7)
+    for (T, N, k) in ((50, 8, 2), (33, 16, 4), (20, 5, 1)):
+        L = rng.standard_normal((T, N)) * 1.5 + np.linspace(1.0, 0.0, N)[None, :]
+        r = M.route_topk(L, k)
+        st = M.routing_stats(L, r.idx)
+        Lt = torch.from_numpy(L)
+        probs = torch.softmax(Lt, dim=-1)
+        mask = torch.zeros_like(probs)
+        mask.scatter_(-1, torch.from_numpy(r.idx.astype(np.int64)), 1.0)
+        code = N * (mask.mean(dim=0) * probs.mean(dim=0)).sum().item()
+        assert abs(code - k * st.aux) < 1e-12 * max(1.0, code)
+        np.testing.assert_allclose(st.P, probs.mean(dim=0).numpy(), rtol=1e-12)
+        zt = (torch.logsumexp(Lt, dim=-1) ** 2).mean().item()
+        assert abs(zt - st.z) < 1e-12 * max(1.0, zt)
+        fb, Pb, auxb, zb = brute_routing_stats(L, k)
+        np.testing.assert_allclose(st.f, fb, rtol=1e-15)
+        np.testing.assert_allclose(st.P, Pb, rtol=1e-12)
+        assert abs(st.aux - auxb) < 1e-12 and abs(st.z - zb) < 1e-12 * max(1.0, zb)
+
+
+def _worked_example_routing():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    N, k, T, C = g["N"], g["k"], g["T"], g["C"]
+    L = np.full((T, N), -30.0)
+    for t, picks in g["picks"].items():
+        for e, p in picks.items():
+            L[int(t), int(e)] = math.log(p)
+    return g, N, k, T, C, M.route_topk(L, k)
+
+
+def pin_first_come_worked_example():
+    # the wiki pseudocode's dispatch loop (tokens in order, an expert's buffer
+    # accepts while it holds fewer than C) on the worked example's requests:
+    # E2 gets x1, x2, x4 and keeps x1, x2; E3 gets x1, x4, x5 and keeps x1, x4
+    g, N, k, T, C, r = _worked_example_routing()
+    disp = M.capacity_dispatch(r.idx, r.key, r.w, N, C, first_come=True)
+    toks = disp.slot_token(k)
+    segs = {e: toks[disp.offsets[e]:disp.offsets[e + 1]].tolist() for e in range(N)}
+    assert segs == {0: [2, 4], 1: [0, 1], 2: [0, 3], 3: [1, 2]}, segs
+    dropped = sorted((int(p // k), int(r.idx[p // k, p % k])) for p in np.nonzero(disp.inv < 0)[0])
+    assert dropped == [(3, 1), (4, 2)]
+
+
+def pin_renorm_worked_example():
+    # "renormalize over the surviving expert alone (weight 1.0 on E2's output)"
+    # for x4; x2 likewise keeps only E4, with weight 1.0
+    g, N, k, T, C, r = _worked_example_routing()
+    disp = M.renormalise_survivors(M.capacity_dispatch(r.idx, r.key, r.w, N, C), r.w, k)
+    toks = disp.slot_token(k)
+    X = np.arange(1, T * 3 + 1, dtype=np.float64).reshape(T, 3)
+    out = {s: X[toks[s]] * (1 + int(e)) for e in range(N)
+           for s in range(disp.offsets[e], disp.offsets[e + 1])}
+    y = M.combine(out, disp, T, k, 3)
+    for t, e in g["tokens_served_by_one_expert"].items():
+        t = int(t)
+        np.testing.assert_allclose(y[t], 1.0 * (1 + e) * X[t], rtol=1e-12)
+    for t in range(T):
+        if str(t) not in g["tokens_served_by_one_expert"]:
+            ref = sum(p * (1 + int(e)) for e, p in g["picks"][str(t)].items()) * X[t]
+            np.testing.assert_allclose(y[t], ref, rtol=1e-9)
+
+
+def pin_identity_fallback():
+    # four identical tokens, one expert each, capacity 1: tokens 1..3 lose their
+    # only pick and keep their input (the pseudocode's fallback); token 0 is served
+    rng = np.random.default_rng(8)
+    T, d, d_ff, N = 4, 5, 7, 3
+    x, W_g, W1, b1, W2, b2 = _rand_layer(rng, T, d, d_ff, N)
+    x = x[:1].repeat(T, 1)
+    res = M.moe_forward(x, W_g, None, W1, b1, W2, b2, k=1, capacity_factor=0.0, C=1,
+                        identity_fallback=True)
+    e0 = int(res["routing"].idx[0, 0])
+    ref0 = make_experts(W1, b1, W2, b2)[e0](x[:1]).detach().numpy()[0]
+    np.testing.assert_allclose(res["y"][0], ref0, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(res["y"][1:], x[1:].numpy())
+    plain = M.moe_forward(x, W_g, None, W1, b1, W2, b2, k=1, capacity_factor=0.0, C=1)
+    assert np.all(plain["y"][1:] == 0.0)
+
+
+def pin_brute_force_policies():
+    for i, (T, d, d_ff, N, k, cf, bias) in enumerate(BRUTE_CASES[:4]):
+        rng = np.random.default_rng(200 + i)
+        x, W_g, W1, b1, W2, b2 = _rand_layer(rng, T, d, d_ff, N, bias)
+        lb = np.zeros(N); lb[0] = 2.5
+        C = M.capacity(T, N, k, cf) if cf > 0 else None
+        for fc, rn, idn in ((True, False, False), (False, True, False), (False, False, True),
+                            (True, True, True)):
+            res = M.moe_forward(x, W_g, lb, W1, b1, W2, b2, k=k, capacity_factor=cf,
+                                first_come=fc, renorm_survivors=rn, identity_fallback=idn)
+            yb, kept, _ = brute_moe(x, res["logits"], k, C, make_experts(W1, b1, W2, b2),
+                                    first_come=fc, renorm=rn, identity=idn)
+            disp = res["dispatch"]
+            kept_oracle = {(int(p // k), int(res["routing"].idx[p // k, p % k])) for p in disp.perm}
+            assert kept_oracle == kept, (i, fc, rn, idn)
+            np.testing.assert_allclose(res["y"], yb, rtol=1e-11, atol=1e-12)
+
+
 PINS = [pin_worked_example, pin_capacity_formula, pin_gelu_textbook, pin_topk_then_softmax_router,
         pin_topk_ties_lower_expert, pin_k1_gates_exactly_one, pin_dense_mixture_k_equals_n,
         pin_single_expert_is_mlp, pin_brute_force, pin_linear_experts_closed_form,
-        pin_dispatch_invariants, pin_capacity_ties_lower_token]
+        pin_dispatch_invariants, pin_capacity_ties_lower_token, pin_routing_stats_uniform,
+        pin_routing_stats_collapse, pin_routing_stats_code_form, pin_first_come_worked_example,
+        pin_renorm_worked_example, pin_identity_fallback, pin_brute_force_policies]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -258,7 +404,8 @@ def test_pin(pin):
 
 # ------------------------------------------------------------- mutants ----
 _orig = {n: getattr(M, n) for n in ("gelu", "route_topk", "capacity", "capacity_dispatch",
-                                    "expert_ffn_rows", "combine")}
+                                    "expert_ffn_rows", "combine", "routing_stats",
+                                    "renormalise_survivors")}
 
 
 def _mut_gelu_tanh(z):
@@ -300,12 +447,12 @@ def _mut_capacity_no_k(T, N, k, cf):
     return _orig["capacity"](T, N, 1, cf)
 
 
-def _mut_drop_highest(idx, key, w, N, C):
-    return _orig["capacity_dispatch"](idx, -np.asarray(key), w, N, C)
+def _mut_drop_highest(idx, key, w, N, C, first_come=False):
+    return _orig["capacity_dispatch"](idx, -np.asarray(key), w, N, C, first_come=first_come)
 
 
-def _mut_slot_order_by_key(idx, key, w, N, C):
-    disp = _orig["capacity_dispatch"](idx, key, w, N, C)
+def _mut_slot_order_by_key(idx, key, w, N, C, first_come=False):
+    disp = _orig["capacity_dispatch"](idx, key, w, N, C, first_come=first_come)
     key = np.asarray(key).reshape(-1)
     for e in range(N):
         seg = slice(disp.offsets[e], disp.offsets[e + 1])
@@ -325,19 +472,61 @@ def _mut_drop_b2(X_rows, W1_e, b1_e, W2_e, b2_e, return_hidden=False):
     return _orig["expert_ffn_rows"](X_rows, W1_e, b1_e, W2_e, None, return_hidden)
 
 
-def _mut_combine_no_gate(slot_out, disp, T, k, d, tokens=None):
+def _mut_combine_no_gate(slot_out, disp, T, k, d, tokens=None, x_fallback=None):
     import copy
     d2 = copy.copy(disp)
     d2.slot_gate = np.ones_like(disp.slot_gate)
-    return _orig["combine"](slot_out, d2, T, k, d, tokens)
+    return _orig["combine"](slot_out, d2, T, k, d, tokens, x_fallback)
 
 
-def _mut_combine_first_only(slot_out, disp, T, k, d, tokens=None):
+def _mut_combine_first_only(slot_out, disp, T, k, d, tokens=None, x_fallback=None):
     import copy
     d2 = copy.copy(disp)
     d2.inv = disp.inv.copy()
     d2.inv.reshape(-1, k)[:, 1:] = -1
-    return _orig["combine"](slot_out, d2, T, k, d, tokens)
+    return _orig["combine"](slot_out, d2, T, k, d, tokens, x_fallback)
+
+
+def _mut_stats_f_over_tokens(L, idx):
+    st = _orig["routing_stats"](L, idx)
+    k = np.asarray(idx).shape[1]
+    st.f = st.f * k
+    st.aux = st.aux * k
+    return st
+
+
+def _mut_stats_P_from_topk(L, idx):
+    st = _orig["routing_stats"](L, idx)
+    L = np.asarray(L, dtype=np.float64)
+    idx = np.asarray(idx)
+    T, N = L.shape
+    Pk = np.zeros(N)
+    for t in range(T):
+        v = np.exp(L[t, idx[t]] - L[t, idx[t]].max())
+        Pk[idx[t]] += v / v.sum()
+    st.P = Pk / T
+    st.aux = float(N * np.dot(st.f, st.P))
+    return st
+
+
+def _mut_stats_z_unsquared(L, idx):
+    st = _orig["routing_stats"](L, idx)
+    L = np.asarray(L, dtype=np.float64)
+    m = L.max(axis=1)
+    st.z = float(np.mean(m + np.log(np.exp(L - m[:, None]).sum(axis=1))))
+    return st
+
+
+def _mut_first_come_ignored(idx, key, w, N, C, first_come=False):
+    return _orig["capacity_dispatch"](idx, key, w, N, C)
+
+
+def _mut_renorm_over_all_picks(disp, w, k):
+    return disp
+
+
+def _mut_fallback_ignored(slot_out, disp, T, k, d, tokens=None, x_fallback=None):
+    return _orig["combine"](slot_out, disp, T, k, d, tokens)
 
 
 MUTANTS = {
@@ -353,6 +542,12 @@ MUTANTS = {
     "second_bias_dropped": ("expert_ffn_rows", _mut_drop_b2),
     "combine_without_gate": ("combine", _mut_combine_no_gate),
     "combine_first_pick_only": ("combine", _mut_combine_first_only),
+    "stats_f_over_tokens": ("routing_stats", _mut_stats_f_over_tokens),
+    "stats_P_from_topk_weights": ("routing_stats", _mut_stats_P_from_topk),
+    "stats_z_unsquared": ("routing_stats", _mut_stats_z_unsquared),
+    "first_come_ignored": ("capacity_dispatch", _mut_first_come_ignored),
+    "renorm_not_applied": ("renormalise_survivors", _mut_renorm_over_all_picks),
+    "identity_fallback_ignored": ("combine", _mut_fallback_ignored),
 }
 
 
@@ -364,6 +559,8 @@ def test_every_mutant_is_caught(name, monkeypatch):
     for pin in PINS:
         try:
             pin()
-        except Exception as exc:  # noqa: BLE001 - any failure counts as a catch
+        except TypeError:
+            raise  # a mutant with the wrong signature proves nothing
+        except Exception as exc:  # noqa: BLE001 - a wrong value or shape counts as a catch
             caught.append((pin.__name__, type(exc).__name__))
     assert caught, f"mutant {name} passed every pin"
