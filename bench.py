@@ -133,6 +133,48 @@ def cpu_baseline(w, inp, sample):
     }
 
 
+def measure_extras(moe, torch, w, dv, ws, y, flags):
+    """After the timed region: moe_routing_stats on this input's logits and
+    top-k ids (20 calls), and the layer with every drop-policy flag (20 steps)."""
+    _, rx = moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"],
+                            dv["b2"], w.k, w.capacity_factor, workspace=ws, want_routing=True,
+                            flags=flags)
+    nx = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stats = moe.moe_routing_stats(rx["logits"], rx["topk_idx"], workspace=ws)
+    e0.record()
+    for _ in range(nx):
+        moe.moe_routing_stats(rx["logits"], rx["topk_idx"], workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    stats_us = e0.elapsed_time(e1) * 1e3 / nx
+    st_h = stats.cpu()
+    pol = (flags | moe.MOE_FLAG_FIRST_COME | moe.MOE_FLAG_RENORM_SURVIVORS
+           | moe.MOE_FLAG_IDENTITY_FALLBACK)
+
+    def pstep():
+        moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"],
+                        dv["b2"], w.k, w.capacity_factor, workspace=ws, y=y, flags=pol)
+
+    for _ in range(3):
+        pstep()
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    for _ in range(nx):
+        pstep()
+    torch.cuda.synchronize()
+    pol_ms = (time.perf_counter() - tp0) * 1e3 / nx
+    extras = {"routing_stats_us": stats_us, "aux_balance": float(st_h[2 * w.N]),
+              "z_mean_lse_sq": float(st_h[2 * w.N + 1]),
+              "all_drop_policies_ms_per_step": pol_ms,
+              "note": "after the timed steps; moe_routing_stats averaged over 20 calls, the layer "
+                      "with first-come capacity + survivor renormalisation + identity fallback "
+                      "over 20 steps"}
+    log(f"extras: routing stats {stats_us:.1f}us, aux {extras['aux_balance']:.4f}, "
+        f"all drop policies {pol_ms:.3f} ms/step")
+    return extras
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +183,8 @@ def main():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--flags", default=None, help="'split' for the bf16 hi+lo hidden layer, 'plain' for bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the routing-statistics and drop-policy measurements after timing")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the "
                          "reference dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -220,6 +264,12 @@ def main():
         f"timed steps); stage breakdown (untimed pass with stage events): "
         + ", ".join(f"{n} {v * 1e3:.1f}us" for n, v in per.items()))
 
+    # extras, after the timed region: the routing statistics pass (from this
+    # input's logits and top-k ids) and the layer with every drop-policy flag
+    extras = None
+    if not args.no_extras:
+        extras = measure_extras(moe, torch, w, dv, ws, y, flags)
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 18  # fp32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -292,6 +342,7 @@ def main():
                   "touched_experts": touched},
         "kernels_us": {n: v * 1e3 for n, v in per.items()},
         "kernels_us_note": "stage times from an untimed pass with an event between stages",
+        "extras": extras,
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -77,12 +77,25 @@ extern "C" {
 #define MOE_F32 0
 #define MOE_BF16 1
 
-/* flags of moe_expert_ffn / moe_forward (bitwise or; 0 = defaults) */
+/* flags (bitwise or; 0 = defaults). Each entry point lists the ones it honours
+ * and rejects unknown bits with MOE_ERR_INVALID_ARG. */
 #define MOE_FLAG_HIDDEN_SPLIT 1 /* bf16 only: carry each hidden activation h into the
                                    second GEMM as bf16(h) plus the bf16 residual
                                    h - bf16(h) (about 16 significant bits instead of
                                    8) at twice the second GEMM's matrix-core work */
-#define MOE_FLAG_Y_F32 2        /* moe_forward writes y as fp32 whatever `dtype` is */
+#define MOE_FLAG_Y_F32 2        /* y is written as fp32 whatever `dtype` is */
+/* Drop-policy variants (wiki page "Mixture-of-Experts": the MoE_Layer
+ * pseudocode and the worked example's final combine). Defaults: capacity by
+ * score, pre-drop weights (partial combine), y[t] = 0 for a fully dropped
+ * token. */
+#define MOE_FLAG_FIRST_COME 4        /* capacity keeps each expert's first C requests in
+                                        token order (the pseudocode's arrival order)
+                                        instead of the C highest-scoring ones */
+#define MOE_FLAG_RENORM_SURVIVORS 8  /* a token that lost a pick but kept others gets its
+                                        kept weights divided by their sum (the worked
+                                        example: weight 1.0 on E2 for x4) */
+#define MOE_FLAG_IDENTITY_FALLBACK 16 /* a token that lost every pick gets y[t] = x[t]
+                                         (the pseudocode's fallback) */
 
 /* Library ABI version (major*100 + minor). */
 int moe_version(void);
@@ -119,6 +132,24 @@ int moe_route(const void* x, const void* W_g, const float* logit_bias,
               float* logits, int32_t* topk_idx, float* topk_w, double* topk_key,
               void* workspace, size_t ws_bytes, void* stream);
 
+/* Forward routing statistics (wiki page, step 8 and "The load-balancing
+ * auxiliary loss"; page "Mixture of Experts (MoE): Architecture, Routing, and
+ * Scaling", "Auxiliary Load Balancing Loss" and "Importance Loss and Z-Loss").
+ *   in : logits [T,N] fp32 and topk_idx [T,k] as produced by moe_route
+ *   out: stats [2N + 2] fp32:
+ *          stats[e]       f_e, share of the T*k top-k picks (before capacity)
+ *                         that chose expert e (sums to 1; the k-hot mask averaged
+ *                         over tokens, as in some pages' code, is k * f_e)
+ *          stats[N + e]   P_e, mean over tokens of the softmax probability of e
+ *          stats[2N]      N * sum_e f_e * P_e (the load-balancing loss without its
+ *                         coefficient; 1 when routing is uniform)
+ *          stats[2N + 1]  mean over tokens of logsumexp_t(L)^2 (the router
+ *                         z-loss without its coefficient)
+ * Evaluated in fp64 with fixed-order sums (bit-reproducible). Needs workspace
+ * (moe_workspace_bytes is enough). */
+int moe_routing_stats(const float* logits, const int32_t* topk_idx, int T, int N, int k,
+                      float* stats, void* workspace, size_t ws_bytes, void* stream);
+
 /* Steps 4-5 (wiki page, steps 4-5 and the capacity-constrained dispatch of
  * its pseudocode; worked example with N=4, k=2, T=5, C=2).
  * Pair index p = t*k + j names token t's j-th pick.
@@ -133,9 +164,13 @@ int moe_route(const void* x, const void* W_g, const float* logit_bias,
  *        slot_gate  [T*k] combine weight topk_w of each slot; first S valid
  *        n_dropped  [1]   T*k - S
  * At an expert with more than C requests the C pairs with the largest key
- * are kept (equal keys: lower token first). Needs workspace. */
+ * are kept (equal keys: lower token first).
+ * flags: MOE_FLAG_FIRST_COME (keep the first C requests in token order; the
+ * keys are then not read) and MOE_FLAG_RENORM_SURVIVORS (slot_gate of a token
+ * that lost a pick = its topk_w / sum of its kept topk_w, in fp32, kept picks
+ * summed in pick order) are honoured. Needs workspace. */
 int moe_dispatch(const int32_t* topk_idx, const float* topk_w, const double* topk_key,
-                 int T, int N, int k, double capacity_factor,
+                 int T, int N, int k, double capacity_factor, int flags,
                  int32_t* req_counts, int32_t* counts, int32_t* offsets,
                  int32_t* perm, int32_t* inv, float* slot_gate, int32_t* n_dropped,
                  void* workspace, size_t ws_bytes, void* stream);
@@ -159,19 +194,22 @@ int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
                    int flags, void* slot_out, void* workspace, size_t ws_bytes, void* stream);
 
 /* Step 7 (wiki page, step 7; weighted combine of the pseudocode).
- *   in : slot_out [T*k, d] fp32 (already gate-scaled), inv [T*k]
- *   out: y [T,d] in `dtype`, y[t] = sum over j = 0..k-1 with inv[t*k+j] >= 0
- *        of slot_out[inv[t*k+j]], summed in fp32 in increasing j; 0 if none.
- * Needs no workspace. */
-int moe_combine(const void* slot_out, const int32_t* inv, int T, int d, int k, int dtype,
-                void* y, void* stream);
+ *   in : slot_out [T*k, d] fp32 (already gate-scaled), inv [T*k]; x [T,d] in
+ *        `dtype` (read only with MOE_FLAG_IDENTITY_FALLBACK, else may be NULL)
+ *   out: y [T,d] in `dtype` (fp32 with MOE_FLAG_Y_F32), y[t] = sum over
+ *        j = 0..k-1 with inv[t*k+j] >= 0 of slot_out[inv[t*k+j]], summed in
+ *        fp32 in increasing j; for a token with no kept pick 0, or x[t] with
+ *        MOE_FLAG_IDENTITY_FALLBACK.
+ * flags: MOE_FLAG_Y_F32, MOE_FLAG_IDENTITY_FALLBACK. Needs no workspace. */
+int moe_combine(const void* slot_out, const int32_t* inv, const void* x, int T, int d, int k,
+                int dtype, int flags, void* y, void* stream);
 
 /* Whole layer, steps 1-7, as one enqueue of the calls above on `stream`.
  *   out: y [T,d] (required) in `dtype`, or fp32 with MOE_FLAG_Y_F32; optional
  *        copies of intermediate results, each NULL to skip: logits_opt [T,N]
  *        fp32, topk_idx_opt [T,k], inv_opt [T*k], req_counts_opt [N],
  *        counts_opt [N], n_dropped_opt [1].
- * flags: MOE_FLAG_* (unknown bits: MOE_ERR_INVALID_ARG).
+ * flags: every MOE_FLAG_* above (unknown bits: MOE_ERR_INVALID_ARG).
  * Needs workspace of moe_workspace_bytes(...) bytes. */
 int moe_forward(const void* x, const void* W_g, const float* logit_bias,
                 const void* W1, const void* b1, const void* W2, const void* b2,

@@ -9,7 +9,10 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     MOE_BF16,
     MOE_F32,
+    MOE_FLAG_FIRST_COME,
     MOE_FLAG_HIDDEN_SPLIT,
+    MOE_FLAG_IDENTITY_FALLBACK,
+    MOE_FLAG_RENORM_SURVIVORS,
     MOE_FLAG_Y_F32,
     MoeError,
     alloc_workspace,
@@ -19,6 +22,7 @@ from ._lib import (  # noqa: F401
     moe_expert_ffn,
     moe_forward,
     moe_route,
+    moe_routing_stats,
     moe_set_profile_events,
     moe_version,
     moe_workspace_bytes,

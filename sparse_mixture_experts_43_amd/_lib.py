@@ -21,6 +21,9 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_FLAG_HIDDEN_SPLIT = 1
 MOE_FLAG_Y_F32 = 2
+MOE_FLAG_FIRST_COME = 4
+MOE_FLAG_RENORM_SURVIVORS = 8
+MOE_FLAG_IDENTITY_FALLBACK = 16
 
 _c_int, _c_size, _c_double, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_double, ctypes.c_void_p
 
@@ -48,11 +51,12 @@ def _load() -> ctypes.CDLL:
         "moe_capacity": (_c_int, [_c_int, _c_int, _c_int, _c_double]),
         "moe_workspace_bytes": (_c_size, [_c_int] * 5 + [_c_double, _c_int]),
         "moe_route": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_vp, _c_size, _vp]),
-        "moe_dispatch": (_c_int, [_vp] * 3 + [_c_int] * 3 + [_c_double] + [_vp] * 7
+        "moe_routing_stats": (_c_int, [_vp, _vp] + [_c_int] * 3 + [_vp] + [_vp, _c_size, _vp]),
+        "moe_dispatch": (_c_int, [_vp] * 3 + [_c_int] * 3 + [_c_double, _c_int] + [_vp] * 7
                          + [_vp, _c_size, _vp]),
         "moe_expert_ffn": (_c_int, [_vp] * 8 + [_c_int] * 5 + [_c_double, _c_int, _c_int]
                            + [_vp, _vp, _c_size, _vp]),
-        "moe_combine": (_c_int, [_vp, _vp] + [_c_int] * 4 + [_vp, _vp]),
+        "moe_combine": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]),
         "moe_forward": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_c_double, _c_int, _c_int]
                         + [_vp] * 7 + [_vp, _c_size, _vp]),
         "moe_set_profile_events": (_c_int, [ctypes.POINTER(_vp), _c_int]),
@@ -67,8 +71,8 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 
 EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_capacity",
-            "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
-            "moe_combine", "moe_forward", "moe_set_profile_events")
+            "moe_workspace_bytes", "moe_route", "moe_routing_stats", "moe_dispatch",
+            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_set_profile_events")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -154,14 +158,36 @@ def moe_route(x: torch.Tensor, W_g: torch.Tensor, logit_bias: Optional[torch.Ten
     return logits, idx, w, key
 
 
-def moe_dispatch(topk_idx: torch.Tensor, topk_w: torch.Tensor, topk_key: torch.Tensor, N: int,
-                 capacity_factor: float, workspace: Optional[torch.Tensor] = None) -> dict:
-    """Steps 4-5. Returns dict of device tensors req_counts, counts, offsets, perm, inv, slot_gate, n_dropped."""
+def moe_routing_stats(logits: torch.Tensor, topk_idx: torch.Tensor,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Routing statistics from moe_route's outputs: fp32 [2N + 2] device tensor
+    holding f (share of the top-k picks per expert), P (mean router probability
+    per expert), N * sum f P, and the mean squared log-sum-exp."""
+    dev = logits.device
+    T, N = logits.shape
+    k = topk_idx.shape[1]
+    _check(logits, "logits", dev, torch.float32)
+    _check(topk_idx, "topk_idx", dev, torch.int32, (T, k))
+    stats = torch.empty(2 * N + 2, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(moe_workspace_bytes(T, 8, 8, N, k, 0.0, torch.float32), dev)
+    st = _lib.moe_routing_stats(_ptr(logits), _ptr(topk_idx), T, N, k, _ptr(stats),
+                                _ptr(workspace), workspace.numel(), _stream(dev))
+    _raise(st, "moe_routing_stats")
+    return stats
+
+
+def moe_dispatch(topk_idx: torch.Tensor, topk_w: torch.Tensor, topk_key: Optional[torch.Tensor],
+                 N: int, capacity_factor: float, workspace: Optional[torch.Tensor] = None,
+                 flags: int = 0) -> dict:
+    """Steps 4-5. Returns dict of device tensors req_counts, counts, offsets, perm, inv, slot_gate, n_dropped.
+    flags: MOE_FLAG_FIRST_COME (topk_key may then be None), MOE_FLAG_RENORM_SURVIVORS."""
     dev = topk_idx.device
     T, k = topk_idx.shape
     _check(topk_idx, "topk_idx", dev, torch.int32)
     _check(topk_w, "topk_w", dev, torch.float32, (T, k))
-    _check(topk_key, "topk_key", dev, torch.float64, (T, k))
+    if topk_key is not None:
+        _check(topk_key, "topk_key", dev, torch.float64, (T, k))
     out = {
         "req_counts": torch.empty(N, dtype=torch.int32, device=dev),
         "counts": torch.empty(N, dtype=torch.int32, device=dev),
@@ -175,7 +201,8 @@ def moe_dispatch(topk_idx: torch.Tensor, topk_w: torch.Tensor, topk_key: torch.T
         workspace = alloc_workspace(moe_workspace_bytes(T, 8, 8, N, k, capacity_factor,
                                                         torch.float32), dev)
     st = _lib.moe_dispatch(_ptr(topk_idx), _ptr(topk_w), _ptr(topk_key), T, N, k,
-                           float(capacity_factor), _ptr(out["req_counts"]), _ptr(out["counts"]),
+                           float(capacity_factor), int(flags), _ptr(out["req_counts"]),
+                           _ptr(out["counts"]),
                            _ptr(out["offsets"]), _ptr(out["perm"]), _ptr(out["inv"]),
                            _ptr(out["slot_gate"]), _ptr(out["n_dropped"]), _ptr(workspace),
                            workspace.numel(), _stream(dev))
@@ -209,15 +236,19 @@ def moe_expert_ffn(x, perm, offsets, slot_gate, W1, b1, W2, b2, k: int, capacity
 
 
 def moe_combine(slot_out: torch.Tensor, inv: torch.Tensor, T: int, k: int,
-                dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
-    """Step 7. slot_out is fp32 [T*k, d]; returns y [T, d] in ``dtype``."""
+                dtype: torch.dtype = torch.bfloat16, x: Optional[torch.Tensor] = None,
+                flags: int = 0) -> torch.Tensor:
+    """Step 7. slot_out is fp32 [T*k, d]; returns y [T, d] in ``dtype`` (the
+    activation dtype; float32 with MOE_FLAG_Y_F32). With
+    MOE_FLAG_IDENTITY_FALLBACK, x [T, d] in ``dtype`` fills fully dropped tokens."""
     dev = slot_out.device
     d = slot_out.shape[1]
     _check(slot_out, "slot_out", dev, torch.float32)
     _check(inv, "inv", dev, torch.int32)
-    y = torch.empty((T, d), dtype=dtype, device=dev)
-    st = _lib.moe_combine(_ptr(slot_out), _ptr(inv), T, d, k, _dtype_code(dtype), _ptr(y),
-                          _stream(dev))
+    _check(x, "x", dev, dtype, (T, d))
+    y = torch.empty((T, d), dtype=torch.float32 if (flags & MOE_FLAG_Y_F32) else dtype, device=dev)
+    st = _lib.moe_combine(_ptr(slot_out), _ptr(inv), _ptr(x), T, d, k, _dtype_code(dtype),
+                          int(flags), _ptr(y), _stream(dev))
     _raise(st, "moe_combine")
     return y
 
@@ -227,7 +258,7 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
                 want_routing: bool = False, flags: int = 0):
     """Steps 1-7 in one enqueue. Returns y, or (y, extras) when want_routing is set;
     extras holds logits, topk_idx, inv, req_counts, counts, n_dropped (device tensors).
-    flags: MOE_FLAG_HIDDEN_SPLIT and/or MOE_FLAG_Y_F32 (y is then float32)."""
+    flags: any MOE_FLAG_* (MOE_FLAG_Y_F32 makes y float32)."""
     dev = x.device
     T, d = x.shape
     N, d_ff, _ = W1.shape

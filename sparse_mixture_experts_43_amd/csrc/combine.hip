@@ -4,19 +4,29 @@
 // Page "Mixture-of-Experts" (wiki), step 7 and the combine of its pseudocode
 // (Y[t] += w * o over the token's experts); a dropped pick adds nothing and a
 // token with every pick dropped gets zeros (its residual path lives outside
-// the layer). The gate-scaled expert outputs arrive in fp32. Each thread owns
-// 16 bytes of one output row: coalesced fp32 loads per kept pick, one 16-byte
-// store.
+// the layer), or its input row when the caller asks for the pseudocode's
+// identity fallback (x not null). The gate-scaled expert outputs arrive in
+// fp32. Each thread owns 16 bytes of one output row: coalesced fp32 loads per
+// kept pick, one 16-byte store.
 #include "moe_common.h"
 
 namespace moe {
 
 namespace {
 
-template <typename T>
+// y[t][c .. c+V) = x[t][c .. c+V) widened to fp32 (identity fallback)
+template <int V, typename XT>
+__device__ __forceinline__ void load_x_row(const XT* __restrict__ x, int t, int d, int c,
+                                           float (&acc)[V]) {
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = to_f32(x[(size_t)t * d + c + i]);
+}
+
+template <typename T, typename XT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ slot_out,
                                                       const int32_t* __restrict__ inv, int T_,
-                                                      int d, int k, T* __restrict__ y) {
+                                                      int d, int k, const XT* __restrict__ x,
+                                                      T* __restrict__ y) {
   constexpr int V = 16 / sizeof(T);  // output elements per 16-byte store
   const int vpr = d / V;             // vectors per row (d % 8 == 0)
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -27,13 +37,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
   const int32_t* it = inv + (size_t)t * k;
+  bool any = false;
   // picks in groups of 4: all slot indices first, then every kept pick's row
   // load issued before the first add (more loads in flight), then the sums in
   // fixed pick order
   for (int j0 = 0; j0 < k; j0 += 4) {
     int s[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s[q] = j0 + q < k ? it[j0 + q] : -1;
+    for (int q = 0; q < 4; ++q) {
+      s[q] = j0 + q < k ? it[j0 + q] : -1;
+      any |= s[q] >= 0;
+    }
     f32x4 v[4][V / 4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -50,6 +64,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         for (int i = 0; i < 4; ++i) acc[4 * h + i] += v[q][h][i];
     }
   }
+  if (!any && x != nullptr) load_x_row<V>(x, t, d, c, acc);
   i32x4 outv;
   T* o = (T*)&outv;
 #pragma unroll
@@ -61,11 +76,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // kept pick's slot value is finished here as gate * (((0 + p_0) + p_1) + ... +
 // b2), the operations and order of the split-K reduction, then summed over the
 // picks in fixed order, so y is bit-identical to the two-kernel path.
-template <typename T, typename B>
+template <typename T, typename B, typename XT>
 __global__ __launch_bounds__(256) void combine_splitk_kernel(
     const float* __restrict__ part, int nsplit, int S_cap, const B* __restrict__ bias,
     const float* __restrict__ gate, const int32_t* __restrict__ off, int N,
-    const int32_t* __restrict__ inv, int T_, int d, int k, T* __restrict__ y) {
+    const int32_t* __restrict__ inv, int T_, int d, int k, const XT* __restrict__ x,
+    T* __restrict__ y) {
 #pragma clang fp contract(off)
   constexpr int V = 16 / sizeof(T);
   const int vpr = d / V;
@@ -76,9 +92,11 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  bool any = false;
   for (int j = 0; j < k; ++j) {
     const int s = inv[(size_t)t * k + j];
     if (s < 0) continue;
+    any = true;
     float v[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) v[i] = 0.f;
@@ -108,6 +126,7 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(
       acc[i] += v[i] * g;  // rounded product, as the stored slot value (no fma)
     }
   }
+  if (!any && x != nullptr) load_x_row<V>(x, t, d, c, acc);
   i32x4 outv;
   T* o = (T*)&outv;
 #pragma unroll
@@ -118,36 +137,50 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(
 }  // namespace
 
 hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, int d, int k,
-                                 int dtype, void* y, hipStream_t st) {
+                                 int y_dtype, const void* x, int x_dtype, void* y,
+                                 hipStream_t st) {
   if (T == 0) return hipSuccess;
-  // the split-K path exists for bf16 weights only; y may be fp32 or bf16
+  // the split-K path exists for bf16 weights (and activations) only; y may be
+  // fp32 or bf16
+  if (x_dtype != kBF16) x = nullptr;
   const bf16* b = (const bf16*)sk.bias;
-  const int V = dtype == kF32 ? 4 : 8;
+  const bf16* xb = (const bf16*)x;
+  const int V = y_dtype == kF32 ? 4 : 8;
   const long long n = (long long)T * (d / V);
   const int blocks = (int)((n + 255) / 256);
-  if (dtype == kF32)
-    hipLaunchKernelGGL((combine_splitk_kernel<float, bf16>), dim3(blocks), dim3(256), 0, st,
-                       sk.part, sk.nsplit, sk.S_cap, b, sk.gate, sk.off, sk.N, inv, T, d, k,
+  if (y_dtype == kF32)
+    hipLaunchKernelGGL((combine_splitk_kernel<float, bf16, bf16>), dim3(blocks), dim3(256), 0, st,
+                       sk.part, sk.nsplit, sk.S_cap, b, sk.gate, sk.off, sk.N, inv, T, d, k, xb,
                        (float*)y);
   else
-    hipLaunchKernelGGL((combine_splitk_kernel<bf16, bf16>), dim3(blocks), dim3(256), 0, st,
-                       sk.part, sk.nsplit, sk.S_cap, b, sk.gate, sk.off, sk.N, inv, T, d, k,
+    hipLaunchKernelGGL((combine_splitk_kernel<bf16, bf16, bf16>), dim3(blocks), dim3(256), 0, st,
+                       sk.part, sk.nsplit, sk.S_cap, b, sk.gate, sk.off, sk.N, inv, T, d, k, xb,
                        (bf16*)y);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d, int k,
-                          int dtype, void* y, hipStream_t st) {
+                          int y_dtype, const void* x, int x_dtype, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const int V = dtype == kF32 ? 4 : 8;
+  const int V = y_dtype == kF32 ? 4 : 8;
   const long long n = (long long)T * (d / V);
   const int blocks = (int)((n + 255) / 256);
-  if (dtype == kF32)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, st,
-                       (const float*)slot_out, inv, T, d, k, (float*)y);
-  else
-    hipLaunchKernelGGL(combine_kernel<bf16>, dim3(blocks), dim3(256), 0, st,
-                       (const float*)slot_out, inv, T, d, k, (bf16*)y);
+  const float* so = (const float*)slot_out;
+  if (y_dtype == kF32) {
+    if (x_dtype == kBF16)
+      hipLaunchKernelGGL((combine_kernel<float, bf16>), dim3(blocks), dim3(256), 0, st, so, inv,
+                         T, d, k, (const bf16*)x, (float*)y);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, float>), dim3(blocks), dim3(256), 0, st, so, inv,
+                         T, d, k, (const float*)x, (float*)y);
+  } else {
+    if (x_dtype == kBF16)
+      hipLaunchKernelGGL((combine_kernel<bf16, bf16>), dim3(blocks), dim3(256), 0, st, so, inv,
+                         T, d, k, (const bf16*)x, (bf16*)y);
+    else
+      hipLaunchKernelGGL((combine_kernel<bf16, float>), dim3(blocks), dim3(256), 0, st, so, inv,
+                         T, d, k, (const float*)x, (bf16*)y);
+  }
   return hipGetLastError();
 }
 

@@ -131,6 +131,15 @@ __device__ __forceinline__ void write_slot(int32_t* perm, int32_t* inv, float* g
   inv[p] = s;
 }
 
+// Capacity rank of pair p as an order-preserving 64-bit code (larger = kept
+// first): the fp64 log-probability key, or with first-come capacity (fc_k =
+// k) the negated token index, so an expert keeps its earliest requests (a
+// token asks an expert at most once, so these never tie).
+__device__ __forceinline__ unsigned long long rank_code(const double* __restrict__ key, int p,
+                                                        int fc_k) {
+  return fc_k > 0 ? key_code(-(double)(p / fc_k)) : key_code(key[p]);
+}
+
 // ------------------------------------------------------------ fused (small P)
 // One block of 16 waves. The expert ids are first copied into LDS as int16
 // (-1 for ids outside [0, N)); wave v then walks a contiguous range of pairs
@@ -142,7 +151,8 @@ __device__ __forceinline__ void write_slot(int32_t* perm, int32_t* inv, float* g
 // bucket and its keys.
 __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ w, const double* __restrict__ key,
-    int P, int N, int C, int direct, int32_t* __restrict__ req, int32_t* __restrict__ cnt,
+    int P, int N, int C, int direct, int fc_k, int32_t* __restrict__ req,
+    int32_t* __restrict__ cnt,
     int32_t* __restrict__ off, int32_t* __restrict__ reqoff, int32_t* __restrict__ n_dropped,
     int32_t* __restrict__ bucket, unsigned long long* __restrict__ codes,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, float* __restrict__ gate) {
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
       write_slot(perm, inv, gate, w, p, s);
     } else {
       bucket[s] = p;
-      codes[s] = key_code(key[p]);
+      codes[s] = rank_code(key, p, fc_k);
     }
   }
 }
@@ -291,7 +301,8 @@ __global__ __launch_bounds__(kScanThreads) void offsets_kernel(
 }
 
 __global__ __launch_bounds__(256) void bucket_kernel(
-    const int32_t* __restrict__ idx, const double* __restrict__ key, int P, int N, int ntiles,
+    const int32_t* __restrict__ idx, const double* __restrict__ key, int fc_k, int P, int N,
+    int ntiles,
     const int32_t* __restrict__ tbase, const int32_t* __restrict__ reqoff,
     int32_t* __restrict__ bucket, unsigned long long* __restrict__ codes,
     int32_t* __restrict__ inv) {
@@ -307,7 +318,7 @@ __global__ __launch_bounds__(256) void bucket_kernel(
   const int p0 = tile * kDispatchTile, p1 = min(P, p0 + kDispatchTile);
   walk_pairs(idx, p0, p1, N, c, [&](int p, int, int pos) {
     bucket[pos] = p;
-    codes[pos] = key_code(key[p]);
+    codes[pos] = rank_code(key, p, fc_k);
   });
   for (int p = p0 + l; p < p1; p += kWave)
     if ((unsigned)idx[p] >= (unsigned)N) inv[p] = -1;
@@ -595,6 +606,30 @@ __global__ __launch_bounds__(kScanThreads) void select_kernel(
     select_body<false>(bucket, codes, w, n, base, o, C, perm, inv, gate, nullptr, shm);
 }
 
+// ------------------------------------------------------------ survivor renormalisation
+// One thread per token: a token that lost some but not all of its picks gets
+// each kept pick's gate = w / (sum of its kept w), the kept weights summed in
+// fp32 in pick order (wiki page, worked example: x4 keeps only E2, weight 1.0).
+// Tokens that kept every pick keep their weights bit for bit.
+__global__ __launch_bounds__(256) void renorm_kernel(const float* __restrict__ w,
+                                                     const int32_t* __restrict__ inv, int T,
+                                                     int k, float* __restrict__ gate) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  const int32_t* it = inv + (size_t)t * k;
+  const float* wt = w + (size_t)t * k;
+  float sum = 0.f;
+  int kept = 0;
+  for (int j = 0; j < k; ++j)
+    if (it[j] >= 0) {
+      sum += wt[j];
+      ++kept;
+    }
+  if (kept == 0 || kept == k) return;
+  for (int j = 0; j < k; ++j)
+    if (it[j] >= 0) gate[it[j]] = wt[j] / sum;
+}
+
 }  // namespace
 
 void carve_dispatch(Carver& c, int P, int N, DispatchScratch* s) {
@@ -607,8 +642,8 @@ void carve_dispatch(Carver& c, int P, int N, DispatchScratch* s) {
 }
 
 hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key, int T, int N,
-                           int k, int C, int32_t* req, int32_t* cnt, int32_t* off, int32_t* perm,
-                           int32_t* inv, float* gate, int32_t* n_dropped,
+                           int k, int C, int flags, int32_t* req, int32_t* cnt, int32_t* off,
+                           int32_t* perm, int32_t* inv, float* gate, int32_t* n_dropped,
                            const DispatchScratch& s, hipStream_t st) {
   const int P = T * k;
   if (P == 0) return hipSuccess;
@@ -616,12 +651,13 @@ hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key
   // and bucket order is slot order
   const bool can_drop = C < T;
   const bool fused = P <= kFusedMaxPairs;
+  const int fc_k = (flags & kFlagFirstCome) ? k : 0;
   if (fused) {
     const size_t lds = ((size_t)(kScanThreads / kWave) * N + N) * sizeof(int) +
                        (size_t)P * sizeof(int16_t);
     MOE_SET_LDS_ONCE(fused_dispatch_kernel, 160 * 1024);
     hipLaunchKernelGGL(fused_dispatch_kernel, dim3(1), dim3(kScanThreads), lds, st, idx, w, key, P,
-                       N, C, can_drop ? 0 : 1, req, cnt, off, s.reqoff, n_dropped, s.bucket,
+                       N, C, can_drop ? 0 : 1, fc_k, req, cnt, off, s.reqoff, n_dropped, s.bucket,
                        s.codes, perm, inv, gate);
   } else {
     const int ntiles = cdiv(P, kDispatchTile);
@@ -632,8 +668,8 @@ hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key
                        req);
     hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, st, req, N, P, C, cnt,
                        s.reqoff, off, n_dropped);
-    hipLaunchKernelGGL(bucket_kernel, dim3(nblk), dim3(256), lds, st, idx, key, P, N, ntiles,
-                       s.tilebase, s.reqoff, s.bucket, s.codes, inv);
+    hipLaunchKernelGGL(bucket_kernel, dim3(nblk), dim3(256), lds, st, idx, key, fc_k, P, N,
+                       ntiles, s.tilebase, s.reqoff, s.bucket, s.codes, inv);
   }
   if (can_drop || !fused)
   {
@@ -644,6 +680,9 @@ hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key
     hipLaunchKernelGGL(select_kernel, dim3(N), dim3(kScanThreads), lds, st, s.bucket, s.codes, w,
                        req, s.reqoff, off, C, perm, inv, gate);
   }
+  // nothing can drop when C >= T: the weights stay as they are
+  if ((flags & kFlagRenorm) && can_drop)
+    hipLaunchKernelGGL(renorm_kernel, dim3(cdiv(T, 256)), dim3(256), 0, st, w, inv, T, k, gate);
   return hipGetLastError();
 }
 

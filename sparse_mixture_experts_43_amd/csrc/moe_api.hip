@@ -105,7 +105,7 @@ using namespace moe;
 
 extern "C" {
 
-int moe_version(void) { return 100; }
+int moe_version(void) { return 101; }
 
 const char* moe_strerror(int status) {
   switch (status) {
@@ -140,7 +140,9 @@ size_t moe_workspace_bytes(int T, int d, int d_ff, int N, int k, double capacity
   ForwardWs f, g;
   carve_forward(nullptr, T, d, d_ff, N, k, C, dtype, MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32, &f);
   carve_forward(nullptr, T, d, d_ff, N, k, C, dtype, MOE_FLAG_Y_F32, &g);
-  return f.bytes > g.bytes ? f.bytes : g.bytes;
+  size_t b = f.bytes > g.bytes ? f.bytes : g.bytes;
+  const size_t sb = align_up(stats_scratch_bytes(T, N), 256);  // moe_routing_stats
+  return b > sb ? b : sb;
 }
 
 int moe_route(const void* x, const void* W_g, const float* logit_bias, int T, int d, int N, int k,
@@ -160,16 +162,31 @@ int moe_route(const void* x, const void* W_g, const float* logit_bias, int T, in
                                  topk_key, workspace, (hipStream_t)stream));
 }
 
+int moe_routing_stats(const float* logits, const int32_t* topk_idx, int T, int N, int k,
+                      float* stats, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_shape(T, 8, 8, N, k, MOE_F32, false);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !stats) return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(stats, 4))
+    return MOE_ERR_UNSUPPORTED;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < stats_scratch_bytes(T, N))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(launch_routing_stats(logits, topk_idx, T, N, k, stats, workspace,
+                                         (hipStream_t)stream));
+}
+
 int moe_dispatch(const int32_t* topk_idx, const float* topk_w, const double* topk_key, int T,
-                 int N, int k, double capacity_factor, int32_t* req_counts, int32_t* counts,
-                 int32_t* offsets, int32_t* perm, int32_t* inv, float* slot_gate,
+                 int N, int k, double capacity_factor, int flags, int32_t* req_counts,
+                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, float* slot_gate,
                  int32_t* n_dropped, void* workspace, size_t ws_bytes, void* stream) {
   int st = check_shape(T, 8, 8, N, k, MOE_F32, false);
   if (st != MOE_OK) return st;
   if (isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (flags & ~(MOE_FLAG_FIRST_COME | MOE_FLAG_RENORM_SURVIVORS)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
-  if (!topk_idx || !topk_w || !topk_key || !req_counts || !counts || !offsets || !perm || !inv ||
-      !slot_gate || !n_dropped)
+  if (!topk_idx || !topk_w || (!topk_key && !(flags & MOE_FLAG_FIRST_COME)) || !req_counts ||
+      !counts || !offsets || !perm || !inv || !slot_gate || !n_dropped)
     return MOE_ERR_INVALID_ARG;
   if (!workspace || !aligned(workspace, 256) || ws_bytes < dispatch_bytes(T, N, k))
     return MOE_ERR_WORKSPACE;
@@ -177,8 +194,8 @@ int moe_dispatch(const int32_t* topk_idx, const float* topk_w, const double* top
   Carver c(workspace);
   DispatchScratch ds;
   carve_dispatch(c, T * k, N, &ds);
-  return hip_status(launch_dispatch(topk_idx, topk_w, topk_key, T, N, k, C, req_counts, counts,
-                                    offsets, perm, inv, slot_gate, n_dropped, ds,
+  return hip_status(launch_dispatch(topk_idx, topk_w, topk_key, T, N, k, C, flags, req_counts,
+                                    counts, offsets, perm, inv, slot_gate, n_dropped, ds,
                                     (hipStream_t)stream));
 }
 
@@ -209,17 +226,22 @@ int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
                                       (hipStream_t)stream));
 }
 
-int moe_combine(const void* slot_out, const int32_t* inv, int T, int d, int k, int dtype, void* y,
-                void* stream) {
+int moe_combine(const void* slot_out, const int32_t* inv, const void* x, int T, int d, int k,
+                int dtype, int flags, void* y, void* stream) {
   if (T < 0 || k < 1 || k > kMaxK || d < 8 || d > 65536 || (d % 8) != 0) {
     return (T < 0 || k < 1 || k > kMaxK) ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED;
   }
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (flags & ~(MOE_FLAG_Y_F32 | MOE_FLAG_IDENTITY_FALLBACK)) return MOE_ERR_INVALID_ARG;
   if ((long long)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!slot_out || !inv || !y) return MOE_ERR_INVALID_ARG;
-  if (!aligned(slot_out, 16) || !aligned(y, 16)) return MOE_ERR_UNSUPPORTED;
-  return hip_status(launch_combine(slot_out, inv, T, d, k, dtype, y, (hipStream_t)stream));
+  const bool fallback = (flags & MOE_FLAG_IDENTITY_FALLBACK) != 0;
+  if (!slot_out || !inv || !y || (fallback && !x)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(slot_out, 16) || !aligned(y, 16) || (fallback && !aligned(x, 16)))
+    return MOE_ERR_UNSUPPORTED;
+  const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
+  return hip_status(launch_combine(slot_out, inv, T, d, k, y_dtype, fallback ? x : nullptr, dtype,
+                                   y, (hipStream_t)stream));
 }
 
 int moe_forward(const void* x, const void* W_g, const float* logit_bias, const void* W1,
@@ -231,7 +253,9 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
   int st = check_shape(T, d, d_ff, N, k, dtype, true);
   if (st != MOE_OK) return st;
   if (isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
-  if (flags & ~(MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32)) return MOE_ERR_INVALID_ARG;
+  if (flags & ~(MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32 | MOE_FLAG_FIRST_COME |
+                MOE_FLAG_RENORM_SURVIVORS | MOE_FLAG_IDENTITY_FALLBACK))
+    return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !W_g || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(W_g, 16) || !aligned(W1, 16) || !aligned(W2, 16) ||
@@ -256,8 +280,8 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
       launch_route(x, W_g, logit_bias, T, d, N, k, dtype, f.logits, f.idx, f.w, f.key, f.wgt, s);
   if (e != hipSuccess) return hip_status(e);
   profile_mark(1, s);
-  e = launch_dispatch(f.idx, f.w, f.key, T, N, k, C, f.req, f.cnt, f.off, f.perm, f.inv, f.gate,
-                      f.ndrop, f.ds, s);
+  e = launch_dispatch(f.idx, f.w, f.key, T, N, k, C, flags, f.req, f.cnt, f.off, f.perm, f.inv,
+                      f.gate, f.ndrop, f.ds, s);
   if (e != hipSuccess) return hip_status(e);
   profile_mark(2, s);
   SplitK sk;  // a K-split second GEMM hands its partials straight to the combine
@@ -265,8 +289,9 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
                         dtype, flags, f.slot_out, f.fs, s, &sk);
   if (e != hipSuccess) return hip_status(e);
   const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
-  e = sk.nsplit > 1 ? launch_combine_splitk(sk, f.inv, T, d, k, y_dtype, y, s)
-                    : launch_combine(f.slot_out, f.inv, T, d, k, y_dtype, y, s);
+  const void* xf = (flags & MOE_FLAG_IDENTITY_FALLBACK) ? x : nullptr;
+  e = sk.nsplit > 1 ? launch_combine_splitk(sk, f.inv, T, d, k, y_dtype, xf, dtype, y, s)
+                    : launch_combine(f.slot_out, f.inv, T, d, k, y_dtype, xf, dtype, y, s);
   profile_mark(6, s);
   return hip_status(e);
 }

@@ -126,6 +126,9 @@ struct FfnScratch {
 };
 constexpr int kFlagHiddenSplit = 1;  // MOE_FLAG_HIDDEN_SPLIT
 constexpr int kFlagYF32 = 2;         // MOE_FLAG_Y_F32
+constexpr int kFlagFirstCome = 4;    // MOE_FLAG_FIRST_COME
+constexpr int kFlagRenorm = 8;       // MOE_FLAG_RENORM_SURVIVORS
+constexpr int kFlagIdentity = 16;    // MOE_FLAG_IDENTITY_FALLBACK
 void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype,
                int flags, FfnScratch* s);
 
@@ -140,10 +143,15 @@ size_t route_scratch_bytes(int d, int N, int dtype);  // transposed router weigh
 hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T, int d, int N,
                         int k, int dtype, float* logits, int32_t* idx, float* w, double* key,
                         void* scratch, hipStream_t st);
+// flags: kFlagFirstCome, kFlagRenorm.
 hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key, int T, int N,
-                           int k, int C, int32_t* req, int32_t* cnt, int32_t* off, int32_t* perm,
-                           int32_t* inv, float* gate, int32_t* n_dropped,
+                           int k, int C, int flags, int32_t* req, int32_t* cnt, int32_t* off,
+                           int32_t* perm, int32_t* inv, float* gate, int32_t* n_dropped,
                            const DispatchScratch& s, hipStream_t st);
+// Routing statistics: scratch bytes and launch (stats: [2N + 2] fp32).
+size_t stats_scratch_bytes(int T, int N);
+hipError_t launch_routing_stats(const float* logits, const int32_t* idx, int T, int N, int k,
+                                float* stats, void* scratch, hipStream_t st);
 // Second expert GEMM left as K-split fp32 partials (decode path): the combine
 // finishes the slot outputs, gate * (sum_q part[q] + b2), in the same order of
 // operations as the split-K reduction would.
@@ -163,9 +171,12 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
                              const void* b2, int T, int d, int d_ff, int N, int k, int C,
                              int S_max, int dtype, int flags, void* slot_out,
                              const FfnScratch& s, hipStream_t st, SplitK* defer = nullptr);
+// y_dtype: dtype of y; x (x_dtype, [T, d]) is read for tokens with no kept
+// pick when not null (identity fallback), else such tokens get zeros.
 hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d, int k,
-                          int dtype, void* y, hipStream_t st);
+                          int y_dtype, const void* x, int x_dtype, void* y, hipStream_t st);
 hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, int d, int k,
-                                 int dtype, void* y, hipStream_t st);
+                                 int y_dtype, const void* x, int x_dtype, void* y,
+                                 hipStream_t st);
 
 }  // namespace moe

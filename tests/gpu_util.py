@@ -126,12 +126,17 @@ def run_and_compare(w: Workload, lib, sample_tokens=None, check_compose=True, se
 
     sample_tokens: None = full output check; int = check that many evenly spaced
     tokens (large workloads), logits checked on the same rows.
-    flags: MOE_FLAG_HIDDEN_SPLIT or 0 (the fp32-output variant is always run).
+    flags: MOE_FLAG_HIDDEN_SPLIT and the drop-policy flags (FIRST_COME,
+    RENORM_SURVIVORS, IDENTITY_FALLBACK); the fp32-output variant is always run.
     strict: also hold y to max|dy| <= 2e-2 (bf16) / 1e-4 (fp32) x RMS(y_ref).
     Returns a dict of measured errors.
     """
     t0 = time.time()
     split = bool(flags & lib.MOE_FLAG_HIDDEN_SPLIT)
+    first_come = bool(flags & lib.MOE_FLAG_FIRST_COME)
+    renorm = bool(flags & lib.MOE_FLAG_RENORM_SURVIVORS)
+    identity = bool(flags & lib.MOE_FLAG_IDENTITY_FALLBACK)
+    dflags = flags & (lib.MOE_FLAG_FIRST_COME | lib.MOE_FLAG_RENORM_SURVIVORS)
     say(f"[case] {w.name} T={w.T} d={w.d} d_ff={w.d_ff} N={w.N} k={w.k} cf={w.capacity_factor} "
         f"dtype={w.dtype} skew={w.skew} seed={w.seed if seed is None else seed} flags={flags}")
     inp = make_inputs(w, seed=seed) if inputs is None else inputs
@@ -146,7 +151,7 @@ def run_and_compare(w: Workload, lib, sample_tokens=None, check_compose=True, se
     torch.cuda.synchronize()
     say(f"[step] moe_route/moe_dispatch {w.name}")
     logits, idx, gw, gkey = lib.moe_route(dv["x"], dv["W_g"], dv["logit_bias"], k)
-    disp = lib.moe_dispatch(idx, gw, gkey, N, w.capacity_factor)
+    disp = lib.moe_dispatch(idx, gw, gkey, N, w.capacity_factor, flags=dflags)
     torch.cuda.synchronize()
     L_gpu = logits.cpu().double().numpy()
     res = {}
@@ -173,7 +178,7 @@ def run_and_compare(w: Workload, lib, sample_tokens=None, check_compose=True, se
 
     C = M.capacity(T, N, k, w.capacity_factor)
     assert C == lib.moe_capacity(T, N, k, w.capacity_factor)
-    od = M.capacity_dispatch(r.idx, r.key, r.w, N, C)
+    od = M.capacity_dispatch(r.idx, r.key, r.w, N, C, first_come=first_come)
     S = od.S
     g_off = disp["offsets"].cpu().numpy()
     g_perm = disp["perm"].cpu().numpy()[:S]
@@ -184,7 +189,7 @@ def run_and_compare(w: Workload, lib, sample_tokens=None, check_compose=True, se
     assert int(disp["n_dropped"].item()) == od.n_dropped
     res["S"], res["n_dropped"], res["C"] = S, od.n_dropped, C
     exact = np.array_equal(g_perm, od.perm) and np.array_equal(g_inv, od.inv)
-    if not exact:
+    if not exact and not first_come:
         gap = capacity_cut_gap(r.idx, r.key, N, C)
         assert gap < 1e-12, f"perm/inv differ and no near-tie at a capacity cut (gap {gap})"
         check_dispatch_valid(r.idx, r.key, N, C, g_perm, g_inv, g_off, k)
@@ -193,6 +198,13 @@ def run_and_compare(w: Workload, lib, sample_tokens=None, check_compose=True, se
                         perm=g_perm.astype(np.int32), inv=g_inv.astype(np.int32),
                         slot_gate=r.w.reshape(-1)[g_perm], n_dropped=od.n_dropped)
     else:
+        assert exact, "first-come perm/inv differ (no ties are possible)"
+    if renorm:
+        od = M.renormalise_survivors(od, r.w, k)
+        # fp32 w / fp32 sum of the kept w against the fp64 quotient
+        np.testing.assert_allclose(disp["slot_gate"].cpu().double().numpy()[:S], od.slot_gate,
+                                   rtol=4 * (k + 2) * EPS32, atol=0)
+    elif exact:
         np.testing.assert_array_equal(disp["slot_gate"].cpu().numpy()[:S],
                                       gw.cpu().numpy().reshape(-1)[od.perm])
     assert np.array_equal(ex["inv"].cpu().numpy()[:T * k], g_inv)
@@ -204,7 +216,7 @@ def run_and_compare(w: Workload, lib, sample_tokens=None, check_compose=True, se
     say(f"[step] oracle output {w.name}")
     if sample_tokens is None:
         O = M.expert_slots_out(inp["x"], od, k, inp["W1"], inp["b1"], inp["W2"], inp["b2"])
-        y_ref = M.combine(O, od, T, k, w.d)
+        y_ref = M.combine(O, od, T, k, w.d, x_fallback=inp["x"] if identity else None)
         toks = np.arange(T)
     else:
         toks = rows
@@ -212,7 +224,8 @@ def run_and_compare(w: Workload, lib, sample_tokens=None, check_compose=True, se
         sl = od.inv[pairs]
         sl = sl[sl >= 0]
         O = M.expert_slots_out(inp["x"], od, k, inp["W1"], inp["b1"], inp["W2"], inp["b2"], slots=sl)
-        y_ref = M.combine(O, od, T, k, w.d, tokens=toks)
+        y_ref = M.combine(O, od, T, k, w.d, tokens=toks,
+                          x_fallback=inp["x"] if identity else None)
     y_gpu = y32.cpu().double().numpy()[toks]
     diff = np.abs(y_gpu - y_ref)
     rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
@@ -228,17 +241,26 @@ def run_and_compare(w: Workload, lib, sample_tokens=None, check_compose=True, se
     if strict:
         tol = 1e-4 if w.dtype == "f32" else 2e-2
         assert err <= tol * rms, res
-    # fully dropped tokens are exactly zero
+    # fully dropped tokens are exactly zero, or exactly their input row with
+    # the identity fallback
     dropped_all = np.all(od.inv.reshape(T, k) < 0, axis=1)
+    res["fully_dropped"] = int(dropped_all.sum())
     if dropped_all.any():
         sel = torch.as_tensor(np.nonzero(dropped_all)[0], device=y32.device)
-        assert torch.count_nonzero(y32[sel]) == 0 and torch.count_nonzero(y_act[sel]) == 0
+        if identity:
+            assert torch.equal(y32[sel], dv["x"][sel].float())
+            assert torch.equal(y_act[sel].view(torch.uint8), dv["x"][sel].view(torch.uint8))
+        else:
+            assert torch.count_nonzero(y32[sel]) == 0 and torch.count_nonzero(y_act[sel]) == 0
 
     if check_compose:
         say(f"[step] sub-call composition + determinism {w.name}")
         so = lib.moe_expert_ffn(dv["x"], disp["perm"], disp["offsets"], disp["slot_gate"], dv["W1"],
-                                dv["b1"], dv["W2"], dv["b2"], k, w.capacity_factor, flags=flags)
-        y2 = lib.moe_combine(so, disp["inv"], T, k, dtype=y_act.dtype)
+                                dv["b1"], dv["W2"], dv["b2"], k, w.capacity_factor,
+                                flags=flags & lib.MOE_FLAG_HIDDEN_SPLIT)
+        y2 = lib.moe_combine(so, disp["inv"], T, k, dtype=y_act.dtype,
+                             x=dv["x"] if identity else None,
+                             flags=lib.MOE_FLAG_IDENTITY_FALLBACK if identity else 0)
         y3 = lib.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"],
                              dv["b2"], k, w.capacity_factor, flags=flags)
         torch.cuda.synchronize()

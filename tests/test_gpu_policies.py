@@ -1,0 +1,133 @@
+"""GPU parity of the routing statistics and the drop-policy variants (through
+the C ABI) against the CPU oracle.
+
+Routing statistics (moe_routing_stats) from the GPU's own logits and top-k ids:
+  * f bit-exact (a pick count over T*k, rounded once to fp32);
+  * P, N sum f P and the mean squared log-sum-exp within 1e-6 relative (fp64
+    sums in another order, rounded once to fp32);
+  * repeated calls bit-identical.
+Drop policies (first-come capacity, survivor renormalisation, identity
+fallback, and all three together) on workloads with drops: indices, counts,
+permutation and inverse map bit-exact, gates within fp32 rounding of the
+oracle's quotient, outputs within the arithmetic error bound
+(tests/gpu_util.py), fully dropped tokens equal to their input row under the
+identity fallback, sub-calls composing to the forward's bits.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_ref as M
+from moe_inputs import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+STATS_CASES = [
+    # name, T, d, N, k, dtype, skew
+    ("stats_small", 300, 64, 6, 3, "f32", "none"),
+    ("stats_N13", 256, 64, 13, 3, "bf16", "normal0.5"),
+    ("stats_N64_zipf", 2048, 128, 64, 8, "bf16", "zipf1.1"),
+    ("stats_N1000", 512, 64, 1000, 16, "bf16", "none"),
+    ("stats_k_eq_N", 128, 64, 4, 4, "bf16", "none"),
+]
+
+POLICY_CASES = [
+    # name, T, d, d_ff, N, k, cf, dtype, bias, skew
+    ("f32_drops", 300, 64, 96, 6, 3, 0.5, "f32", True, "none"),
+    ("switch_small", 1024, 128, 256, 16, 1, 1.0, "bf16", False, "normal0.5"),
+    ("fine_small_zipf", 2048, 128, 64, 64, 8, 1.25, "bf16", False, "zipf1.1"),
+    ("capacity_one", 64, 64, 64, 8, 2, 0.01, "bf16", False, "zipf1.1"),
+    ("decode_path_drops", 96, 256, 384, 8, 2, 0.5, "bf16", True, "normal0.5"),
+]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_mixture_experts_43_amd as m
+    return m
+
+
+def _stats_check(lib, w: Workload):
+    from gpu_util import say, to_dev
+    say(f"[case] routing stats {w.name} T={w.T} d={w.d} N={w.N} k={w.k} dtype={w.dtype}")
+    dv = to_dev(make_inputs(w))
+    logits, idx, _, _ = lib.moe_route(dv["x"], dv["W_g"], dv["logit_bias"], w.k)
+    s1 = lib.moe_routing_stats(logits, idx)
+    s2 = lib.moe_routing_stats(logits, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32)), "stats not reproducible"
+    L = logits.cpu().double().numpy()
+    ids = idx.cpu().numpy()
+    ref = M.routing_stats(L, ids)
+    g = s1.cpu().double().numpy()
+    N = w.N
+    np.testing.assert_array_equal(g[:N], ref.f.astype(np.float32).astype(np.float64))
+    np.testing.assert_allclose(g[N:2 * N], ref.P, rtol=1e-6, atol=1e-12)
+    np.testing.assert_allclose(g[2 * N], ref.aux, rtol=1e-6)
+    np.testing.assert_allclose(g[2 * N + 1], ref.z, rtol=1e-6)
+    say(f"[ok] {w.name} aux={g[2 * N]:.6f} z={g[2 * N + 1]:.6f}")
+
+
+@pytest.mark.parametrize("case", STATS_CASES, ids=[c[0] for c in STATS_CASES])
+def test_routing_stats_small(lib, case):
+    name, T, d, N, k, dt, skew = case
+    _stats_check(lib, Workload(name, T=T, d=d, d_ff=8, N=N, k=k, capacity_factor=0.0, dtype=dt,
+                               ffn_bias=False, skew=skew, seed=0))
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_routing_stats_workloads(lib, name):
+    _stats_check(lib, WORKLOADS[name])
+
+
+FLAG_SETS = {
+    "first_come": "MOE_FLAG_FIRST_COME",
+    "renorm": "MOE_FLAG_RENORM_SURVIVORS",
+    "identity": "MOE_FLAG_IDENTITY_FALLBACK",
+    "all": ("MOE_FLAG_FIRST_COME", "MOE_FLAG_RENORM_SURVIVORS", "MOE_FLAG_IDENTITY_FALLBACK"),
+}
+
+
+def _flags(lib, key):
+    names = FLAG_SETS[key]
+    names = (names,) if isinstance(names, str) else names
+    f = 0
+    for n in names:
+        f |= getattr(lib, n)
+    return f
+
+
+@pytest.mark.parametrize("policy", sorted(FLAG_SETS))
+@pytest.mark.parametrize("case", POLICY_CASES, ids=[c[0] for c in POLICY_CASES])
+def test_drop_policy(lib, case, policy):
+    from gpu_util import run_and_compare
+    name, T, d, d_ff, N, k, cf, dt, bias, skew = case
+    w = Workload(f"{name}_{policy}", T=T, d=d, d_ff=d_ff, N=N, k=k, capacity_factor=cf, dtype=dt,
+                 ffn_bias=bias, skew=skew, seed=0)
+    res = run_and_compare(w, lib, flags=_flags(lib, policy))
+    assert res["n_dropped"] > 0
+
+
+def test_identity_fallback_fully_dropped(lib):
+    """Identical tokens, one pick each, capacity 1 at their shared expert: all
+    but the first token lose their only pick and must come out as their input."""
+    from gpu_util import run_and_compare
+    w = Workload("fully_dropped", T=64, d=64, d_ff=64, N=8, k=1, capacity_factor=0.01,
+                 dtype="bf16", ffn_bias=False, skew="none")
+    inp = make_inputs(w)
+    inp["x"] = inp["x"][:1].repeat(w.T, 1).contiguous()
+    res = run_and_compare(w, lib, inputs=inp, flags=lib.MOE_FLAG_IDENTITY_FALLBACK)
+    assert res["fully_dropped"] == w.T - 1
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["switch_top1", "fine_grained"])
+def test_drop_policies_full_size(lib, name):
+    from gpu_util import run_and_compare
+    flags = lib.MOE_FLAG_HIDDEN_SPLIT | _flags(lib, "all")
+    run_and_compare(WORKLOADS[name], lib, sample_tokens=24, flags=flags, strict=True,
+                    check_compose=False)
