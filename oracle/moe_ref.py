@@ -40,13 +40,13 @@ reason in the design notes of the repository):
   R6 GELU is the exact erf form (nn.GELU default in [Arch] and [Rise]).
   R7 slots are ordered by expert ascending, tokens ascending inside an expert
      (the append order of the [Wiki] pseudocode).
-  R8 routing statistics: f_e = share of the T*k top-k picks (before capacity)
+  R15 routing statistics: f_e = share of the T*k top-k picks (before capacity)
      that chose expert e, so sum_e f_e = 1 ([Wiki] normalisation; the code of
      [Scaling] and [Rise] averages the k-hot mask over tokens, which is k*f_e);
      P_e = mean over tokens of the full softmax probability; aux = N * sum_e
      f_e P_e without the training coefficient (1 at uniform routing); z = mean
      over tokens of lse_t^2 without its coefficient.
-  R9 drop-policy variants, each off by default: (a) first-come capacity keeps
+  R16 drop-policy variants, each off by default: (a) first-come capacity keeps
      each expert's first C requests in token order (the arrival order of the
      [Wiki] pseudocode's dispatch loop); (b) survivor renormalisation divides a
      token's kept weights by their sum when it lost a pick ([Wiki] worked
@@ -152,7 +152,7 @@ def route_topk(L, k: int) -> Routing:
 # loss" (f_e, P_e, N * sum f_e P_e, minimum 1 when f = P = 1/N); [Arch]
 # "Auxiliary Load Balancing Loss" and "Importance Loss and Z-Loss" (z-loss over
 # the tokens' log-sum-exp); [Scaling] "Training Dynamics and Stability" (z-loss
-# as the batch mean of the squared log-sum-exp).  Reading R8.
+# as the batch mean of the squared log-sum-exp).  Reading R15.
 # --------------------------------------------------------------------------
 @dataclass
 class RoutingStats:
@@ -220,7 +220,7 @@ class Dispatch:
 # key, ties to the lower token) and R7 (slot order).
 # --------------------------------------------------------------------------
 def capacity_dispatch(idx, key, w, N: int, C: int, first_come: bool = False) -> Dispatch:
-    """``first_come`` (reading R9a): keep each expert's first C requests in token
+    """``first_come`` (reading R16a): keep each expert's first C requests in token
     order instead of the C highest keys."""
     idx = np.asarray(idx)
     key = np.asarray(key, dtype=np.float64)
@@ -254,7 +254,7 @@ def capacity_dispatch(idx, key, w, N: int, C: int, first_come: bool = False) -> 
 
 
 def renormalise_survivors(disp: Dispatch, w, k: int) -> Dispatch:
-    """Reading R9b: a token that lost at least one pick but kept some gets its
+    """Reading R16b: a token that lost at least one pick but kept some gets its
     kept weights divided by their sum ([Wiki] worked example: x4 keeps only
     E2, with weight 1.0). Tokens that kept every pick are left unchanged."""
     w = np.asarray(w, dtype=np.float64).reshape(-1, k)
@@ -345,7 +345,7 @@ def combine(slot_out, disp: Dispatch, T: int, k: int, d: int,
     """y[t] = sum over kept j of w[t,j] * out[slot(t,j)]; rows for ``tokens`` only if given.
 
     ``slot_out`` is either an [S, d] array or a dict slot -> row. ``x_fallback``
-    (reading R9c): a token whose every pick was dropped gets x[t] instead of 0.
+    (reading R16c): a token whose every pick was dropped gets x[t] instead of 0.
     """
     toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     y = np.zeros((len(toks), d))
@@ -373,7 +373,7 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
     ``tokens``: evaluate the output rows for these tokens only; routing and
     capacity still use every token, since capacity ranks across tokens.
     ``first_come``, ``renorm_survivors``, ``identity_fallback``: the drop-policy
-    variants of reading R9.
+    variants of reading R16.
 
     Returns dict with y ([T,d] or [len(tokens), d]), logits, routing, dispatch.
     """
