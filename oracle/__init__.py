@@ -11,10 +11,12 @@ from .moe_ref import (  # noqa: F401
     capacity,
     capacity_dispatch,
     combine,
+    expert_choice_dispatch,
     expert_ffn_rows,
     expert_slots_out,
     gelu,
     moe_forward,
+    moe_forward_expert_choice,
     renormalise_survivors,
     route_topk,
     routing_stats,

@@ -137,3 +137,28 @@ def brute_routing_stats(logits, k: int):
     f = [c / (T * k) for c in counts]
     P = [s / T for s in psum]
     return f, P, N * sum(a * b for a, b in zip(f, P)), zsum / T
+
+
+def brute_expert_choice(x, logits, C: int, experts: List[Callable], identity: bool = False):
+    """Expert-choice layer with pure-Python selection: each expert sorts all
+    tokens by its softmax probability (ties: lower token) and takes the first
+    C; y[t] = sum over the experts that took t of p[t,e] * E_e(x_t)."""
+    X = _f64(x)
+    L = _f64(logits)
+    T, N = L.shape
+    probs = torch.softmax(L, dim=-1)
+    taken = {}
+    for e in range(N):
+        col = sorted(range(T), key=lambda t: (-float(probs[t, e]), t))
+        for t in col[:C]:
+            taken.setdefault(t, []).append(e)
+    dense = [experts[e](X).detach() for e in range(N)]
+    y = torch.zeros_like(X)
+    for t in range(T):
+        if t not in taken:
+            if identity:
+                y[t] = X[t]
+            continue
+        for e in taken[t]:
+            y[t] += float(probs[t, e]) * dense[e][t]
+    return y.numpy(), {(t, e) for t, es in taken.items() for e in es}

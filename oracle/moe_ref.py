@@ -52,6 +52,12 @@ reason in the design notes of the repository):
      token's kept weights by their sum when it lost a pick ([Wiki] worked
      example: weight 1.0 on E2's output for x4); (c) identity fallback gives a
      token that lost every pick y[t] = x[t] (the [Wiki] pseudocode's fallback).
+  R17 expert-choice routing: every expert takes the C tokens with the highest
+     softmax probability p[t,e] (equal probabilities: lower token), C from the
+     capacity formula with k read as the average number of experts per token
+     (cf <= 0: every token, C = T); the combine weight is p[t,e] itself; a token
+     no expert took gets 0 (or x[t] with the identity fallback). [Scaling]
+     "Expert Choice Routing", [Arch] "Expert Choice Routing (ECR)".
 
 Every function here is pinned by tests under tests/ against facts the pages
 or the mathematics fix (see tests/test_oracle_pins.py). The bf16 rounding of
@@ -83,6 +89,8 @@ __all__ = [
     "RoutingStats",
     "routing_stats",
     "renormalise_survivors",
+    "expert_choice_dispatch",
+    "moe_forward_expert_choice",
 ]
 
 
@@ -270,6 +278,66 @@ def renormalise_survivors(disp: Dispatch, w, k: int) -> Dispatch:
     return Dispatch(C=disp.C, req_counts=disp.req_counts, counts=disp.counts,
                     offsets=disp.offsets, perm=disp.perm, inv=disp.inv, slot_gate=gate,
                     n_dropped=disp.n_dropped)
+
+
+# --------------------------------------------------------------------------
+# Expert-choice routing ([Scaling] "Expert Choice Routing": each expert picks
+# its top tokens from the batch, every expert the same number; [Arch] "Expert
+# Choice Routing (ECR)": tokens no expert picks get zero).  Reading R17.
+# Pairs are indexed p = t*N + e (every token is a candidate of every expert),
+# so the Dispatch below uses k = N in its pair bookkeeping.
+# --------------------------------------------------------------------------
+def expert_choice_dispatch(L, C: int) -> Dispatch:
+    L = np.asarray(L, dtype=np.float64)
+    T, N = L.shape
+    m = L.max(axis=1)
+    lse = m + np.log(np.exp(L - m[:, None]).sum(axis=1))
+    key = L - lse[:, None]  # log p[t, e]
+    p = np.exp(key)
+    inv = np.full(T * N, -1, dtype=np.int32)
+    cnt = np.zeros(N, dtype=np.int32)
+    parts = []
+    toks = np.arange(T)
+    for e in range(N):
+        rank = np.lexsort((toks, -key[:, e]))  # probability descending, then token
+        keep = np.sort(rank[:C])  # token-ascending slot order
+        cnt[e] = len(keep)
+        parts.append(keep.astype(np.int64) * N + e)
+    perm = np.concatenate(parts).astype(np.int32)
+    offsets = np.zeros(N + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(cnt)
+    inv[perm] = np.arange(len(perm), dtype=np.int32)
+    return Dispatch(C=C, req_counts=np.full(N, T, dtype=np.int32), counts=cnt, offsets=offsets,
+                    perm=perm, inv=inv, slot_gate=p.reshape(-1)[perm],
+                    n_dropped=int(T * N - len(perm)))
+
+
+def moe_forward_expert_choice(x, W_g, logit_bias, W1, b1, W2, b2, k: int,
+                              capacity_factor: float, logits: Optional[np.ndarray] = None,
+                              tokens: Optional[Sequence[int]] = None,
+                              identity_fallback: bool = False):
+    """Layer forward with expert-choice routing (reading R17). ``k`` is the
+    average number of experts per token behind C; ``logits`` / ``tokens`` as in
+    moe_forward. Returns dict with y, logits, dispatch (pairs t*N + e)."""
+    X = x
+    T = X.shape[0]
+    N = W_g.shape[1]
+    d = W_g.shape[0]
+    L = router_logits(X, W_g, logit_bias) if logits is None else np.asarray(logits, np.float64)
+    C = capacity(T, N, k, capacity_factor)
+    disp = expert_choice_dispatch(L, C)
+    xf = X if identity_fallback else None
+    if tokens is None:
+        O = expert_slots_out(X, disp, N, W1, b1, W2, b2)
+        y = combine(O, disp, T, N, d, x_fallback=xf)
+    else:
+        toks = np.asarray(tokens, dtype=np.int64)
+        pairs = (toks[:, None] * N + np.arange(N)[None, :]).reshape(-1)
+        slots = disp.inv[pairs]
+        slots = slots[slots >= 0]
+        O = expert_slots_out(X, disp, N, W1, b1, W2, b2, slots=slots)
+        y = combine(O, disp, T, N, d, tokens=toks, x_fallback=xf)
+    return {"y": y, "logits": L, "dispatch": disp}
 
 
 # --------------------------------------------------------------------------

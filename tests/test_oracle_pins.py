@@ -29,7 +29,11 @@ Pins used (none of them re-types the oracle's own formula):
   * drop policies: the worked example's survivor renormalisation (weight 1.0
     on E2 for x4, on E4 for x2), first-come capacity as the pseudocode's
     arrival-order loop (worked example and brute force), identity fallback
-    for a token that loses every pick.
+    for a token that loses every pick;
+  * expert-choice routing: with no capacity limit every expert takes every
+    token, which is the dense softmax mixture of all experts; every expert
+    takes exactly min(C, T) tokens; pure-Python selection per expert
+    (oracle/brute.py), with and without the identity fallback.
 """
 from __future__ import annotations
 
@@ -42,7 +46,7 @@ import pytest
 import torch
 
 import oracle.moe_ref as M
-from oracle.brute import brute_moe, brute_routing_stats, make_experts
+from oracle.brute import brute_expert_choice, brute_moe, brute_routing_stats, make_experts
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -389,12 +393,45 @@ def pin_brute_force_policies():
             np.testing.assert_allclose(res["y"], yb, rtol=1e-11, atol=1e-12)
 
 
+def pin_expert_choice_dense():
+    # no capacity limit: every expert takes every token with weight p[t, e],
+    # the dense softmax mixture of all experts
+    rng = np.random.default_rng(9)
+    T, d, d_ff, N = 14, 6, 9, 5
+    x, W_g, W1, b1, W2, b2 = _rand_layer(rng, T, d, d_ff, N)
+    res = M.moe_forward_expert_choice(x, W_g, None, W1, b1, W2, b2, k=2, capacity_factor=0.0)
+    experts = make_experts(W1, b1, W2, b2)
+    G = torch.softmax(x @ W_g, dim=-1)
+    ref = sum(G[:, e:e + 1] * experts[e](x) for e in range(N)).detach().numpy()
+    np.testing.assert_allclose(res["y"], ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_expert_choice_balance_and_brute():
+    for i, (T, d, d_ff, N, k, cf, bias) in enumerate(BRUTE_CASES[:5]):
+        rng = np.random.default_rng(300 + i)
+        x, W_g, W1, b1, W2, b2 = _rand_layer(rng, T, d, d_ff, N, bias)
+        lb = np.zeros(N); lb[0] = 2.0
+        for identity in (False, True):
+            res = M.moe_forward_expert_choice(x, W_g, lb, W1, b1, W2, b2, k=k, capacity_factor=cf,
+                                              identity_fallback=identity)
+            C = M.capacity(T, N, k, cf)
+            disp = res["dispatch"]
+            # perfect balance by construction: every expert takes min(C, T) tokens
+            assert np.all(disp.counts == min(C, T))
+            yb, taken = brute_expert_choice(x, res["logits"], C, make_experts(W1, b1, W2, b2),
+                                            identity=identity)
+            kept = {(int(p // N), int(p % N)) for p in disp.perm}
+            assert kept == taken, (i, identity)
+            np.testing.assert_allclose(res["y"], yb, rtol=1e-11, atol=1e-12)
+
+
 PINS = [pin_worked_example, pin_capacity_formula, pin_gelu_textbook, pin_topk_then_softmax_router,
         pin_topk_ties_lower_expert, pin_k1_gates_exactly_one, pin_dense_mixture_k_equals_n,
         pin_single_expert_is_mlp, pin_brute_force, pin_linear_experts_closed_form,
         pin_dispatch_invariants, pin_capacity_ties_lower_token, pin_routing_stats_uniform,
         pin_routing_stats_collapse, pin_routing_stats_code_form, pin_first_come_worked_example,
-        pin_renorm_worked_example, pin_identity_fallback, pin_brute_force_policies]
+        pin_renorm_worked_example, pin_identity_fallback, pin_brute_force_policies,
+        pin_expert_choice_dense, pin_expert_choice_balance_and_brute]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -405,7 +442,7 @@ def test_pin(pin):
 # ------------------------------------------------------------- mutants ----
 _orig = {n: getattr(M, n) for n in ("gelu", "route_topk", "capacity", "capacity_dispatch",
                                     "expert_ffn_rows", "combine", "routing_stats",
-                                    "renormalise_survivors")}
+                                    "renormalise_survivors", "expert_choice_dispatch")}
 
 
 def _mut_gelu_tanh(z):
@@ -529,6 +566,33 @@ def _mut_fallback_ignored(slot_out, disp, T, k, d, tokens=None, x_fallback=None)
     return _orig["combine"](slot_out, disp, T, k, d, tokens)
 
 
+def _mut_ec_first_tokens(L, C):
+    # every expert takes the first C tokens (arrival order) instead of its top C
+    disp = _orig["expert_choice_dispatch"](L, C)
+    L = np.asarray(L, dtype=np.float64)
+    T, N = L.shape
+    Cc = min(C, T)
+    perm = np.concatenate([np.arange(Cc) * N + e for e in range(N)]).astype(np.int32)
+    inv = np.full(T * N, -1, dtype=np.int32)
+    inv[perm] = np.arange(len(perm), dtype=np.int32)
+    p = np.exp(L - (L.max(1) + np.log(np.exp(L - L.max(1)[:, None]).sum(1)))[:, None])
+    disp.perm, disp.inv = perm, inv
+    disp.slot_gate = p.reshape(-1)[perm]
+    return disp
+
+
+def _mut_ec_gate_renormalised(L, C):
+    disp = _orig["expert_choice_dispatch"](L, C)
+    N = np.asarray(L).shape[1]
+    g = disp.slot_gate.copy()
+    tok = disp.perm // N
+    for t in np.unique(tok):
+        sel = tok == t
+        g[sel] = g[sel] / g[sel].sum()
+    disp.slot_gate = g
+    return disp
+
+
 MUTANTS = {
     "gelu_tanh_approx": ("gelu", _mut_gelu_tanh),
     "no_renormalisation": ("route_topk", _mut_no_renorm),
@@ -548,6 +612,8 @@ MUTANTS = {
     "first_come_ignored": ("capacity_dispatch", _mut_first_come_ignored),
     "renorm_not_applied": ("renormalise_survivors", _mut_renorm_over_all_picks),
     "identity_fallback_ignored": ("combine", _mut_fallback_ignored),
+    "expert_choice_by_token_order": ("expert_choice_dispatch", _mut_ec_first_tokens),
+    "expert_choice_gate_renormalised": ("expert_choice_dispatch", _mut_ec_gate_renormalised),
 }
 
 
