@@ -164,14 +164,33 @@ def measure_extras(moe, torch, w, dv, ws, y, flags):
         pstep()
     torch.cuda.synchronize()
     pol_ms = (time.perf_counter() - tp0) * 1e3 / nx
+    ecf = flags | moe.MOE_FLAG_EXPERT_CHOICE
+
+    def estep():
+        moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"],
+                        dv["b2"], w.k, w.capacity_factor, workspace=ws, y=y, flags=ecf)
+
+    for _ in range(3):
+        estep()
+    torch.cuda.synchronize()
+    te0 = time.perf_counter()
+    for _ in range(nx):
+        estep()
+    torch.cuda.synchronize()
+    ec_ms = (time.perf_counter() - te0) * 1e3 / nx
+    C = moe.moe_capacity(w.T, w.N, w.k, w.capacity_factor)
     extras = {"routing_stats_us": stats_us, "aux_balance": float(st_h[2 * w.N]),
               "z_mean_lse_sq": float(st_h[2 * w.N + 1]),
               "all_drop_policies_ms_per_step": pol_ms,
+              "expert_choice_ms_per_step": ec_ms,
+              "expert_choice_slots": w.N * min(C, w.T),
               "note": "after the timed steps; moe_routing_stats averaged over 20 calls, the layer "
                       "with first-come capacity + survivor renormalisation + identity fallback "
-                      "over 20 steps"}
+                      "over 20 steps, and with expert-choice routing (every expert takes "
+                      "min(C, T) tokens) over 20 steps"}
     log(f"extras: routing stats {stats_us:.1f}us, aux {extras['aux_balance']:.4f}, "
-        f"all drop policies {pol_ms:.3f} ms/step")
+        f"all drop policies {pol_ms:.3f} ms/step, expert choice {ec_ms:.3f} ms/step "
+        f"({extras['expert_choice_slots']} slots)")
     return extras
 
 

@@ -96,6 +96,18 @@ extern "C" {
                                         example: weight 1.0 on E2 for x4) */
 #define MOE_FLAG_IDENTITY_FALLBACK 16 /* a token that lost every pick gets y[t] = x[t]
                                          (the pseudocode's fallback) */
+/* Expert-choice routing (page "Mixture of Experts: Scaling Language Models with
+ * Sparse Activation", "Expert Choice Routing"; page "Mixture of Experts (MoE):
+ * Architecture, Routing, and Scaling", "Expert Choice Routing (ECR)"),
+ * moe_forward only: every expert takes the C tokens with the highest softmax
+ * probability p[t,e] (equal probabilities: lower token), C from the capacity
+ * formula with k read as the average number of experts per token (cf <= 0:
+ * C = T, every expert takes every token); the combine weight is p[t,e]; a token
+ * no expert took gets 0, or x[t] with MOE_FLAG_IDENTITY_FALLBACK. Pairs are
+ * indexed t*N + e: inv_opt is then [T*N], req_counts are T, n_dropped counts the
+ * pairs not taken. Not combinable with FIRST_COME / RENORM_SURVIVORS or a
+ * topk_idx_opt output. */
+#define MOE_FLAG_EXPERT_CHOICE 32
 
 /* Library ABI version (major*100 + minor). */
 int moe_version(void);

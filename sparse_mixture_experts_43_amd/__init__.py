@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     MOE_BF16,
     MOE_F32,
+    MOE_FLAG_EXPERT_CHOICE,
     MOE_FLAG_FIRST_COME,
     MOE_FLAG_HIDDEN_SPLIT,
     MOE_FLAG_IDENTITY_FALLBACK,

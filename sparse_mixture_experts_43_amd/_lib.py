@@ -24,6 +24,7 @@ MOE_FLAG_Y_F32 = 2
 MOE_FLAG_FIRST_COME = 4
 MOE_FLAG_RENORM_SURVIVORS = 8
 MOE_FLAG_IDENTITY_FALLBACK = 16
+MOE_FLAG_EXPERT_CHOICE = 32
 
 _c_int, _c_size, _c_double, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_double, ctypes.c_void_p
 
@@ -276,11 +277,13 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
     if workspace is None:
         workspace = alloc_workspace(moe_workspace_bytes(T, d, d_ff, N, k, capacity_factor, x.dtype), dev)
     ex = {}
+    ec = bool(flags & MOE_FLAG_EXPERT_CHOICE)
+    kp = N if ec else k  # pairs per token (expert choice: every expert)
     if want_routing:
         ex = {
             "logits": torch.empty((T, N), dtype=torch.float32, device=dev),
-            "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
-            "inv": torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+            "topk_idx": None if ec else torch.empty((T, k), dtype=torch.int32, device=dev),
+            "inv": torch.empty(max(T * kp, 1), dtype=torch.int32, device=dev),
             "req_counts": torch.empty(N, dtype=torch.int32, device=dev),
             "counts": torch.empty(N, dtype=torch.int32, device=dev),
             "n_dropped": torch.empty(1, dtype=torch.int32, device=dev),

@@ -141,6 +141,10 @@ size_t moe_workspace_bytes(int T, int d, int d_ff, int N, int k, double capacity
   carve_forward(nullptr, T, d, d_ff, N, k, C, dtype, MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32, &f);
   carve_forward(nullptr, T, d, d_ff, N, k, C, dtype, MOE_FLAG_Y_F32, &g);
   size_t b = f.bytes > g.bytes ? f.bytes : g.bytes;
+  // expert choice: every (token, expert) pair is a candidate
+  ForwardWs ec;
+  carve_forward(nullptr, T, d, d_ff, N, N, C, dtype, MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32, &ec);
+  b = b > ec.bytes ? b : ec.bytes;
   const size_t sb = align_up(stats_scratch_bytes(T, N), 256);  // moe_routing_stats
   return b > sb ? b : sb;
 }
@@ -254,7 +258,10 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
   if (st != MOE_OK) return st;
   if (isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
   if (flags & ~(MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32 | MOE_FLAG_FIRST_COME |
-                MOE_FLAG_RENORM_SURVIVORS | MOE_FLAG_IDENTITY_FALLBACK))
+                MOE_FLAG_RENORM_SURVIVORS | MOE_FLAG_IDENTITY_FALLBACK | MOE_FLAG_EXPERT_CHOICE))
+    return MOE_ERR_INVALID_ARG;
+  const bool ec = (flags & MOE_FLAG_EXPERT_CHOICE) != 0;
+  if (ec && ((flags & (MOE_FLAG_FIRST_COME | MOE_FLAG_RENORM_SURVIVORS)) || topk_idx_opt))
     return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !W_g || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
@@ -263,35 +270,41 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
       (logit_bias && !aligned(logit_bias, 4)) || (logits_opt && !aligned(logits_opt, 4)))
     return MOE_ERR_UNSUPPORTED;
   const int C = capacity_host(T, N, k, capacity_factor);
+  // pairs per token: k picks, or with expert choice every expert (pair t*N + e)
+  const int kp = ec ? N : k;
   ForwardWs f;
-  carve_forward(nullptr, T, d, d_ff, N, k, C, dtype, flags, &f);
+  carve_forward(nullptr, T, d, d_ff, N, kp, C, dtype, flags, &f);
   if (!workspace || !aligned(workspace, 256) || ws_bytes < f.bytes) return MOE_ERR_WORKSPACE;
-  carve_forward(workspace, T, d, d_ff, N, k, C, dtype, flags, &f);
+  carve_forward(workspace, T, d, d_ff, N, kp, C, dtype, flags, &f);
   if (logits_opt) f.logits = logits_opt;
   if (topk_idx_opt) f.idx = topk_idx_opt;
   if (inv_opt) f.inv = inv_opt;
   if (req_counts_opt) f.req = req_counts_opt;
   if (counts_opt) f.cnt = counts_opt;
   if (n_dropped_opt) f.ndrop = n_dropped_opt;
-  const int S_max = (int)((long long)T * k < (long long)N * C ? (long long)T * k : (long long)N * C);
+  const int S_max =
+      (int)((long long)T * kp < (long long)N * C ? (long long)T * kp : (long long)N * C);
   hipStream_t s = (hipStream_t)stream;
   profile_mark(0, s);
-  hipError_t e =
-      launch_route(x, W_g, logit_bias, T, d, N, k, dtype, f.logits, f.idx, f.w, f.key, f.wgt, s);
+  // expert choice: the router's logits (its top-1 outputs are scratch), then
+  // every pair as a candidate
+  hipError_t e = launch_route(x, W_g, logit_bias, T, d, N, ec ? 1 : k, dtype, f.logits, f.idx,
+                              f.w, f.key, f.wgt, s);
+  if (e == hipSuccess && ec) e = launch_route_expert_choice(f.logits, T, N, f.idx, f.w, f.key, s);
   if (e != hipSuccess) return hip_status(e);
   profile_mark(1, s);
-  e = launch_dispatch(f.idx, f.w, f.key, T, N, k, C, flags, f.req, f.cnt, f.off, f.perm, f.inv,
+  e = launch_dispatch(f.idx, f.w, f.key, T, N, kp, C, flags, f.req, f.cnt, f.off, f.perm, f.inv,
                       f.gate, f.ndrop, f.ds, s);
   if (e != hipSuccess) return hip_status(e);
   profile_mark(2, s);
   SplitK sk;  // a K-split second GEMM hands its partials straight to the combine
-  e = launch_expert_ffn(x, f.perm, f.off, f.gate, W1, b1, W2, b2, T, d, d_ff, N, k, C, S_max,
+  e = launch_expert_ffn(x, f.perm, f.off, f.gate, W1, b1, W2, b2, T, d, d_ff, N, kp, C, S_max,
                         dtype, flags, f.slot_out, f.fs, s, &sk);
   if (e != hipSuccess) return hip_status(e);
   const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
   const void* xf = (flags & MOE_FLAG_IDENTITY_FALLBACK) ? x : nullptr;
-  e = sk.nsplit > 1 ? launch_combine_splitk(sk, f.inv, T, d, k, y_dtype, xf, dtype, y, s)
-                    : launch_combine(f.slot_out, f.inv, T, d, k, y_dtype, xf, dtype, y, s);
+  e = sk.nsplit > 1 ? launch_combine_splitk(sk, f.inv, T, d, kp, y_dtype, xf, dtype, y, s)
+                    : launch_combine(f.slot_out, f.inv, T, d, kp, y_dtype, xf, dtype, y, s);
   profile_mark(6, s);
   return hip_status(e);
 }

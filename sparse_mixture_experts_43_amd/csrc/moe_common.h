@@ -129,6 +129,7 @@ constexpr int kFlagYF32 = 2;         // MOE_FLAG_Y_F32
 constexpr int kFlagFirstCome = 4;    // MOE_FLAG_FIRST_COME
 constexpr int kFlagRenorm = 8;       // MOE_FLAG_RENORM_SURVIVORS
 constexpr int kFlagIdentity = 16;    // MOE_FLAG_IDENTITY_FALLBACK
+constexpr int kFlagExpertChoice = 32;  // MOE_FLAG_EXPERT_CHOICE
 void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype,
                int flags, FfnScratch* s);
 
@@ -144,6 +145,10 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
                         int k, int dtype, float* logits, int32_t* idx, float* w, double* key,
                         void* scratch, hipStream_t st);
 // flags: kFlagFirstCome, kFlagRenorm.
+// Expert choice: from fp32 logits [T, N], every pair t*N + e as a candidate:
+// idx = e, w = p[t,e], key = log p[t,e] (fp64).
+hipError_t launch_route_expert_choice(const float* logits, int T, int N, int32_t* idx, float* w,
+                                     double* key, hipStream_t st);
 hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key, int T, int N,
                            int k, int C, int flags, int32_t* req, int32_t* cnt, int32_t* off,
                            int32_t* perm, int32_t* inv, float* gate, int32_t* n_dropped,

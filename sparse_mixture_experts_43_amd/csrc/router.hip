@@ -155,6 +155,51 @@ __device__ __forceinline__ void topk_row16(const float* __restrict__ Lrow, bool 
   }
 }
 
+// ---------------------------------------------------------------- expert choice
+// Every (token, expert) pair is a candidate (page "Mixture of Experts: Scaling
+// Language Models with Sparse Activation", "Expert Choice Routing"): pair
+// t*N + e gets expert e, weight p[t,e] (the softmax probability itself) and the
+// fp64 rank key L[t,e] - lse_t, computed as in topk_row (wave max, per-lane
+// sums of exp over the lane's experts, xor butterfly). One wave per token.
+__global__ __launch_bounds__(256) void ec_route_kernel(const float* __restrict__ logits, int T,
+                                                       int N, int32_t* __restrict__ idx,
+                                                       float* __restrict__ w,
+                                                       double* __restrict__ key) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  const int l = lane_id();
+  const float* row = logits + (size_t)t * N;
+  float v[kMaxN / kWave];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMaxN / kWave; ++i) {
+    const int n = l + kWave * i;
+    v[i] = (n < N) ? row[n] : -INFINITY;
+    if (n < N) m = fmaxf(m, v[i]);
+  }
+  m = wave_max_f32(m);
+  const double md = (double)m;
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < kMaxN / kWave; ++i) {
+    const int n = l + kWave * i;
+    if (n < N) s += exp((double)v[i] - md);
+  }
+  s = wave_sum_f64(s);
+  const double lse = md + log(s);
+#pragma unroll
+  for (int i = 0; i < kMaxN / kWave; ++i) {
+    const int n = l + kWave * i;
+    if (n < N) {
+      const size_t p = (size_t)t * N + n;
+      const double kk = (double)v[i] - lse;
+      idx[p] = n;
+      key[p] = kk;
+      w[p] = (float)exp(kk);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- W_g transpose
 // W_g [d, N] (N-contiguous) -> WgT [NP, d] (K-contiguous, rows n >= N zero), the
 // layout the MFMA B operand wants: 8 consecutive k of one expert per lane.
@@ -578,6 +623,14 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
   if (N <= 512 && T >= 32 * 256) return launch_bf16<32, 64>(x, W_g, bias, T, d, N, k, logits, idx, w, key, st);
   if (N <= 512) return launch_bf16<16, 64>(x, W_g, bias, T, d, N, k, logits, idx, w, key, st);
   return launch_bf16<16, 32>(x, W_g, bias, T, d, N, k, logits, idx, w, key, st);
+}
+
+hipError_t launch_route_expert_choice(const float* logits, int T, int N, int32_t* idx, float* w,
+                                     double* key, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(ec_route_kernel, dim3(cdiv(T, 4)), dim3(256), 0, st, logits, T, N, idx, w,
+                     key);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -106,7 +106,11 @@ def test_argument_checks_return_before_launch():
     assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, float("nan"), 1, 0, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -1
     assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 0, p, nul, nul, nul, nul, nul, nul, p, 16, nul) == -3
     # unknown flag bits
-    assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 32, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -1
+    assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 64, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -1
+    # expert choice with a flag or output it does not combine with
+    assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 32 | 4, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -1
+    assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 32 | 8, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -1
+    assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 32, p, nul, p, nul, nul, nul, nul, p, 1 << 30, nul) == -1
     # combine: d % 8, k range, flags, identity fallback without x
     assert raw.moe_combine(p, p, nul, 4, 60, 2, 1, 0, p, nul) == -2
     assert raw.moe_combine(p, p, nul, 4, 64, 0, 1, 0, p, nul) == -1
