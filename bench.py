@@ -135,7 +135,8 @@ def cpu_baseline(w, inp, sample):
 
 def measure_extras(moe, torch, w, dv, ws, y, flags):
     """After the timed region: moe_routing_stats on this input's logits and
-    top-k ids (20 calls), and the layer with every drop-policy flag (20 steps)."""
+    top-k ids (20 calls), the layer with every drop-policy flag, with
+    expert-choice routing, and with a shared expert (20 steps each)."""
     _, rx = moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"],
                             dv["b2"], w.k, w.capacity_factor, workspace=ws, want_routing=True,
                             flags=flags)
@@ -178,19 +179,59 @@ def measure_extras(moe, torch, w, dv, ws, y, flags):
         estep()
     torch.cuda.synchronize()
     ec_ms = (time.perf_counter() - te0) * 1e3 / nx
+    # a shared expert of the routed experts' width on every token
+    from moe_inputs import make_shared_expert
+    sh = {k_: (None if v is None else v.to(dv["x"].device)) for k_, v in
+          make_shared_expert(w).items()}
+    sflags = flags & moe.MOE_FLAG_HIDDEN_SPLIT
+    sws = moe.alloc_workspace(moe.moe_shared_workspace_bytes(w.T, w.d, w.d_ff, dv["x"].dtype),
+                              dv["x"].device)
+    sout = torch.empty((w.T, w.d), dtype=torch.float32, device=dv["x"].device)
+
+    def shstep():
+        moe.moe_shared_expert(dv["x"], sh["W1s"], sh["b1s"], sh["W2s"], sh["b2s"], workspace=sws,
+                              flags=sflags, out=sout)
+
+    def sstep():
+        shstep()
+        moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"],
+                        dv["b2"], w.k, w.capacity_factor, workspace=ws, y=y, flags=flags,
+                        shared_out=sout)
+
+    for _ in range(3):
+        sstep()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(nx):
+        shstep()
+    e1.record()
+    torch.cuda.synchronize()
+    sh_ms = e0.elapsed_time(e1) / nx
+    ts0 = time.perf_counter()
+    for _ in range(nx):
+        sstep()
+    torch.cuda.synchronize()
+    ss_ms = (time.perf_counter() - ts0) * 1e3 / nx
+    sh_tflops = 4.0 * w.T * w.d * w.d_ff / (sh_ms * 1e-3) / 1e12  # algorithmic flops
     C = moe.moe_capacity(w.T, w.N, w.k, w.capacity_factor)
     extras = {"routing_stats_us": stats_us, "aux_balance": float(st_h[2 * w.N]),
               "z_mean_lse_sq": float(st_h[2 * w.N + 1]),
               "all_drop_policies_ms_per_step": pol_ms,
               "expert_choice_ms_per_step": ec_ms,
               "expert_choice_slots": w.N * min(C, w.T),
+              "shared_expert_ms": sh_ms,
+              "shared_expert_tflops": sh_tflops,
+              "with_shared_expert_ms_per_step": ss_ms,
               "note": "after the timed steps; moe_routing_stats averaged over 20 calls, the layer "
                       "with first-come capacity + survivor renormalisation + identity fallback "
-                      "over 20 steps, and with expert-choice routing (every expert takes "
-                      "min(C, T) tokens) over 20 steps"}
+                      "over 20 steps, with expert-choice routing (every expert takes "
+                      "min(C, T) tokens) over 20 steps, a shared expert of width d_ff on every "
+                      "token alone (HIP events, 20 calls; TFLOP/s = 4 T d d_ff / time) and "
+                      "added to the layer (20 steps)"}
     log(f"extras: routing stats {stats_us:.1f}us, aux {extras['aux_balance']:.4f}, "
         f"all drop policies {pol_ms:.3f} ms/step, expert choice {ec_ms:.3f} ms/step "
-        f"({extras['expert_choice_slots']} slots)")
+        f"({extras['expert_choice_slots']} slots), shared expert {sh_ms:.3f} ms "
+        f"({sh_tflops:.0f} TFLOP/s), layer + shared expert {ss_ms:.3f} ms/step")
     return extras
 
 

@@ -41,6 +41,8 @@
  *      b2     [N, d]            activation dtype, may be NULL
  *      logit_bias [N]           fp32, may be NULL
  *      y      [T, d]            activation dtype
+ *      W1s    [d_fs, d], b1s [d_fs], W2s [d, d_fs], b2s [d]: a shared expert
+ *                               (activation dtype; biases may be NULL)
  *    Router logits and combine weights are fp32; rank keys are fp64.
  *  - dtype: MOE_F32 (all activation tensors fp32) or MOE_BF16 (bf16 storage,
  *    fp32 accumulation).
@@ -128,6 +130,27 @@ int moe_capacity(int T, int N, int k, double capacity_factor);
  * Returns 0 on invalid arguments. */
 size_t moe_workspace_bytes(int T, int d, int d_ff, int N, int k, double capacity_factor, int dtype);
 
+/* Device workspace, in bytes, that is enough for moe_shared_expert with these
+ * sizes and any flags. Returns 0 on invalid arguments. */
+size_t moe_shared_workspace_bytes(int T, int d, int d_fs, int dtype);
+
+/* Shared expert (page "Mixture of Experts: Scaling Language Models with Sparse
+ * Activation", "Comparing MoE Architectures": shared experts that see every
+ * token next to the sparsely activated routed ones; page "Mixture of Experts
+ * (MoE): Architecture, Routing, and Scaling", "Expert Choice Routing (ECR)":
+ * tokens no expert took are still processed by a shared expert). The same FFN as step 6 with its own weights,
+ * applied to every token with weight 1:
+ *   in : x [T,d]; W1s [d_fs,d], b1s [d_fs] or NULL, W2s [d,d_fs], b2s [d] or NULL
+ *   out: out [T,d] fp32, out[t] = W2s GELU(W1s x[t] + b1s) + b2s (hidden
+ *        activations rounded to the activation dtype, as in moe_expert_ffn)
+ * Pass `out` as shared_out to moe_combine / moe_forward to add it to the
+ * routed output before y is rounded. d_fs follows d_ff's limits. flags:
+ * MOE_FLAG_HIDDEN_SPLIT (bf16). Needs workspace of
+ * moe_shared_workspace_bytes(...) bytes; records no profiling events. */
+int moe_shared_expert(const void* x, const void* W1s, const void* b1s, const void* W2s,
+                      const void* b2s, int T, int d, int d_fs, int dtype, int flags, float* out,
+                      void* workspace, size_t ws_bytes, void* stream);
+
 /* Steps 1-3 (wiki page, steps 1-3; "Inside the Router" on the corecocept page
  * for keeping logits at higher precision).
  *   in : x [T,d], W_g [d,N], logit_bias [N] fp32 or NULL
@@ -207,26 +230,31 @@ int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
 
 /* Step 7 (wiki page, step 7; weighted combine of the pseudocode).
  *   in : slot_out [T*k, d] fp32 (already gate-scaled), inv [T*k]; x [T,d] in
- *        `dtype` (read only with MOE_FLAG_IDENTITY_FALLBACK, else may be NULL)
+ *        `dtype` (read only with MOE_FLAG_IDENTITY_FALLBACK, else may be NULL);
+ *        shared_out [T,d] fp32 from moe_shared_expert, or NULL
  *   out: y [T,d] in `dtype` (fp32 with MOE_FLAG_Y_F32), y[t] = sum over
  *        j = 0..k-1 with inv[t*k+j] >= 0 of slot_out[inv[t*k+j]], summed in
  *        fp32 in increasing j; for a token with no kept pick 0, or x[t] with
- *        MOE_FLAG_IDENTITY_FALLBACK.
+ *        MOE_FLAG_IDENTITY_FALLBACK; then + shared_out[t] when given (fp32),
+ *        and one rounding to y's dtype.
  * flags: MOE_FLAG_Y_F32, MOE_FLAG_IDENTITY_FALLBACK. Needs no workspace. */
-int moe_combine(const void* slot_out, const int32_t* inv, const void* x, int T, int d, int k,
-                int dtype, int flags, void* y, void* stream);
+int moe_combine(const void* slot_out, const int32_t* inv, const void* x, const float* shared_out,
+                int T, int d, int k, int dtype, int flags, void* y, void* stream);
 
 /* Whole layer, steps 1-7, as one enqueue of the calls above on `stream`.
  *   out: y [T,d] (required) in `dtype`, or fp32 with MOE_FLAG_Y_F32; optional
  *        copies of intermediate results, each NULL to skip: logits_opt [T,N]
  *        fp32, topk_idx_opt [T,k], inv_opt [T*k], req_counts_opt [N],
  *        counts_opt [N], n_dropped_opt [1].
+ *   in : shared_out [T,d] fp32 (moe_shared_expert's output) or NULL: added
+ *        to every token in the combine, as in moe_combine.
  * flags: every MOE_FLAG_* above (unknown bits: MOE_ERR_INVALID_ARG).
  * Needs workspace of moe_workspace_bytes(...) bytes. */
 int moe_forward(const void* x, const void* W_g, const float* logit_bias,
                 const void* W1, const void* b1, const void* W2, const void* b2,
                 int T, int d, int d_ff, int N, int k, double capacity_factor, int dtype,
-                int flags, void* y, float* logits_opt, int32_t* topk_idx_opt, int32_t* inv_opt,
+                int flags, const float* shared_out, void* y,
+                float* logits_opt, int32_t* topk_idx_opt, int32_t* inv_opt,
                 int32_t* req_counts_opt, int32_t* counts_opt, int32_t* n_dropped_opt,
                 void* workspace, size_t ws_bytes, void* stream);
 

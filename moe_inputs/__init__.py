@@ -20,6 +20,14 @@ fp32 standard normals in this fixed order):
     W2     [N, d, d_ff]  ~ N(0, 1/d_ff)        nn.Linear(d_ff, d) layout [out, in]
     b2     [N, d]        ~ N(0, 0.01^2)        only where the workload has biases
 
+A shared expert (``make_shared_expert``) has a generator of its own, seeded
+with the workload seed + 7919, drawing in this order:
+
+    W1s    [d_fs, d]     ~ N(0, 1/d)
+    b1s    [d_fs]        ~ N(0, 0.01^2)        only where the workload has biases
+    W2s    [d, d_fs]     ~ N(0, 1/d_fs)
+    b2s    [d]           ~ N(0, 0.01^2)        only where the workload has biases
+
 Each tensor is drawn in fp32, scaled, then rounded once (round-to-nearest-
 even) to the workload's activation dtype. Both sides consume exactly these
 rounded values; the logit bias stays fp32.
@@ -32,7 +40,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "get_workload", "make_inputs", "scaled"]
+__all__ = ["Workload", "WORKLOADS", "get_workload", "make_inputs", "make_shared_expert",
+           "scaled"]
 
 
 @dataclass(frozen=True)
@@ -137,3 +146,18 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     W2 = scaled(g, (w.N, w.d, w.d_ff), 1.0 / math.sqrt(w.d_ff), dt)
     b2 = scaled(g, (w.N, w.d), 0.01, dt) if w.ffn_bias else None
     return {"x": x, "W_g": W_g, "logit_bias": bias, "W1": W1, "b1": b1, "W2": W2, "b2": b2}
+
+
+def make_shared_expert(w: Workload, d_fs: Optional[int] = None,
+                       seed: Optional[int] = None) -> dict:
+    """Draw a shared expert's weights for workload ``w`` (hidden width ``d_fs``,
+    default the workload's d_ff). Keys: W1s, b1s (or None), W2s, b2s (or None)."""
+    d_fs = w.d_ff if d_fs is None else d_fs
+    g = torch.Generator(device="cpu")
+    g.manual_seed((w.seed if seed is None else seed) + 7919)
+    dt = _torch_dtype(w.dtype)
+    W1s = scaled(g, (d_fs, w.d), 1.0 / math.sqrt(w.d), dt)
+    b1s = scaled(g, (d_fs,), 0.01, dt) if w.ffn_bias else None
+    W2s = scaled(g, (w.d, d_fs), 1.0 / math.sqrt(d_fs), dt)
+    b2s = scaled(g, (w.d,), 0.01, dt) if w.ffn_bias else None
+    return {"W1s": W1s, "b1s": b1s, "W2s": W2s, "b2s": b2s}

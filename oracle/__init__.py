@@ -20,6 +20,7 @@ from .moe_ref import (  # noqa: F401
     renormalise_survivors,
     route_topk,
     routing_stats,
+    shared_expert_out,
     router_logits,
     to_f64,
 )

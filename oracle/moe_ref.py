@@ -58,6 +58,13 @@ reason in the design notes of the repository):
      (cf <= 0: every token, C = T); the combine weight is p[t,e] itself; a token
      no expert took gets 0 (or x[t] with the identity fallback). [Scaling]
      "Expert Choice Routing", [Arch] "Expert Choice Routing (ECR)".
+  R18 shared expert: an always-on FFN of its own weights, applied to every
+     token with weight 1 and added to the routed output (after the identity
+     fallback, which replaces only the routed part). [Scaling] "Comparing MoE
+     Architectures" (shared experts that see every token next to sparsely
+     activated routed ones), [Arch]
+     "Expert Choice Routing (ECR)" (unselected tokens processed by a shared
+     expert).
 
 Every function here is pinned by tests under tests/ against facts the pages
 or the mathematics fix (see tests/test_oracle_pins.py). The bf16 rounding of
@@ -91,6 +98,7 @@ __all__ = [
     "renormalise_survivors",
     "expert_choice_dispatch",
     "moe_forward_expert_choice",
+    "shared_expert_out",
 ]
 
 
@@ -315,10 +323,12 @@ def expert_choice_dispatch(L, C: int) -> Dispatch:
 def moe_forward_expert_choice(x, W_g, logit_bias, W1, b1, W2, b2, k: int,
                               capacity_factor: float, logits: Optional[np.ndarray] = None,
                               tokens: Optional[Sequence[int]] = None,
-                              identity_fallback: bool = False):
+                              identity_fallback: bool = False, shared=None):
     """Layer forward with expert-choice routing (reading R17). ``k`` is the
-    average number of experts per token behind C; ``logits`` / ``tokens`` as in
-    moe_forward. Returns dict with y, logits, dispatch (pairs t*N + e)."""
+    average number of experts per token behind C; ``logits`` / ``tokens`` /
+    ``shared`` as in moe_forward (the shared expert also serves the tokens no
+    expert took, reading R18). Returns dict with y, logits, dispatch (pairs
+    t*N + e)."""
     X = x
     T = X.shape[0]
     N = W_g.shape[1]
@@ -337,6 +347,8 @@ def moe_forward_expert_choice(x, W_g, logit_bias, W1, b1, W2, b2, k: int,
         slots = slots[slots >= 0]
         O = expert_slots_out(X, disp, N, W1, b1, W2, b2, slots=slots)
         y = combine(O, disp, T, N, d, tokens=toks, x_fallback=xf)
+    if shared is not None:
+        y = y + shared_expert_out(X, shared, tokens)
     return {"y": y, "logits": L, "dispatch": disp}
 
 
@@ -429,10 +441,21 @@ def combine(slot_out, disp: Dispatch, T: int, k: int, d: int,
     return y
 
 
+def shared_expert_out(x, shared, tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Reading R18: FFN_s(x_t) for every token (or the given ones); ``shared``
+    is (W1s [d_fs, d], b1s or None, W2s [d, d_fs], b2s or None)."""
+    W1s, b1s, W2s, b2s = shared
+    X = to_f64(x)
+    if tokens is not None:
+        X = X[np.asarray(tokens, dtype=np.int64)]
+    return expert_ffn_rows(X, W1s, b1s, W2s, b2s)
+
+
 def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: float,
                 logits: Optional[np.ndarray] = None, C: Optional[int] = None,
                 tokens: Optional[Sequence[int]] = None, first_come: bool = False,
-                renorm_survivors: bool = False, identity_fallback: bool = False):
+                renorm_survivors: bool = False, identity_fallback: bool = False,
+                shared=None):
     """Whole layer forward ([Wiki] MoE_Layer, steps 1-7).
 
     ``logits``: when given (e.g. another implementation's fp32 router logits,
@@ -441,7 +464,8 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
     ``tokens``: evaluate the output rows for these tokens only; routing and
     capacity still use every token, since capacity ranks across tokens.
     ``first_come``, ``renorm_survivors``, ``identity_fallback``: the drop-policy
-    variants of reading R16.
+    variants of reading R16. ``shared``: a shared expert's (W1s, b1s, W2s, b2s),
+    added to every token's output (reading R18).
 
     Returns dict with y ([T,d] or [len(tokens), d]), logits, routing, dispatch.
     """
@@ -467,4 +491,6 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
         slots = slots[slots >= 0]
         O = expert_slots_out(X, disp, k, W1, b1, W2, b2, slots=slots)
         y = combine(O, disp, T, k, d, tokens=toks, x_fallback=xf)
+    if shared is not None:
+        y = y + shared_expert_out(X, shared, tokens)
     return {"y": y, "logits": L, "routing": r, "dispatch": disp}

@@ -25,6 +25,8 @@ from ._lib import (  # noqa: F401
     moe_route,
     moe_routing_stats,
     moe_set_profile_events,
+    moe_shared_expert,
+    moe_shared_workspace_bytes,
     moe_version,
     moe_workspace_bytes,
 )

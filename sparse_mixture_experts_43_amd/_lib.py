@@ -57,9 +57,11 @@ def _load() -> ctypes.CDLL:
                          + [_vp, _c_size, _vp]),
         "moe_expert_ffn": (_c_int, [_vp] * 8 + [_c_int] * 5 + [_c_double, _c_int, _c_int]
                            + [_vp, _vp, _c_size, _vp]),
-        "moe_combine": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]),
+        "moe_combine": (_c_int, [_vp] * 4 + [_c_int] * 5 + [_vp, _vp]),
         "moe_forward": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_c_double, _c_int, _c_int]
-                        + [_vp] * 7 + [_vp, _c_size, _vp]),
+                        + [_vp] * 8 + [_vp, _c_size, _vp]),
+        "moe_shared_workspace_bytes": (_c_size, [_c_int] * 4),
+        "moe_shared_expert": (_c_int, [_vp] * 5 + [_c_int] * 5 + [_vp] + [_vp, _c_size, _vp]),
         "moe_set_profile_events": (_c_int, [ctypes.POINTER(_vp), _c_int]),
     }
     for name, (res, args) in sig.items():
@@ -73,7 +75,8 @@ _lib = _load()
 
 EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_capacity",
             "moe_workspace_bytes", "moe_route", "moe_routing_stats", "moe_dispatch",
-            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_set_profile_events")
+            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_set_profile_events",
+            "moe_shared_workspace_bytes", "moe_shared_expert")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -127,6 +130,13 @@ def moe_workspace_bytes(T: int, d: int, d_ff: int, N: int, k: int, capacity_fact
     n = _lib.moe_workspace_bytes(T, d, d_ff, N, k, float(capacity_factor), _dtype_code(dtype))
     if n == 0:
         raise ValueError("moe_workspace_bytes: invalid arguments")
+    return n
+
+
+def moe_shared_workspace_bytes(T: int, d: int, d_fs: int, dtype: torch.dtype) -> int:
+    n = _lib.moe_shared_workspace_bytes(T, d, d_fs, _dtype_code(dtype))
+    if n == 0:
+        raise ValueError("moe_shared_workspace_bytes: invalid arguments")
     return n
 
 
@@ -236,30 +246,59 @@ def moe_expert_ffn(x, perm, offsets, slot_gate, W1, b1, W2, b2, k: int, capacity
     return slot_out
 
 
+def moe_shared_expert(x, W1s, b1s, W2s, b2s, workspace: Optional[torch.Tensor] = None,
+                      flags: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Shared expert on every token: fp32 [T, d] = W2s GELU(W1s x + b1s) + b2s,
+    for the shared_out argument of moe_combine / moe_forward.
+    flags: MOE_FLAG_HIDDEN_SPLIT."""
+    dev = x.device
+    T, d = x.shape
+    d_fs = W1s.shape[0]
+    _check(x, "x", dev)
+    _check(W1s, "W1s", dev, x.dtype, (d_fs, d))
+    _check(W2s, "W2s", dev, x.dtype, (d, d_fs))
+    _check(b1s, "b1s", dev, x.dtype, (d_fs,))
+    _check(b2s, "b2s", dev, x.dtype, (d,))
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    _check(out, "out", dev, torch.float32, (T, d))
+    if workspace is None:
+        workspace = alloc_workspace(moe_shared_workspace_bytes(T, d, d_fs, x.dtype), dev)
+    st = _lib.moe_shared_expert(_ptr(x), _ptr(W1s), _ptr(b1s), _ptr(W2s), _ptr(b2s), T, d, d_fs,
+                                _dtype_code(x.dtype), int(flags), _ptr(out), _ptr(workspace),
+                                workspace.numel(), _stream(dev))
+    _raise(st, "moe_shared_expert")
+    return out
+
+
 def moe_combine(slot_out: torch.Tensor, inv: torch.Tensor, T: int, k: int,
                 dtype: torch.dtype = torch.bfloat16, x: Optional[torch.Tensor] = None,
-                flags: int = 0) -> torch.Tensor:
+                flags: int = 0, shared_out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Step 7. slot_out is fp32 [T*k, d]; returns y [T, d] in ``dtype`` (the
     activation dtype; float32 with MOE_FLAG_Y_F32). With
-    MOE_FLAG_IDENTITY_FALLBACK, x [T, d] in ``dtype`` fills fully dropped tokens."""
+    MOE_FLAG_IDENTITY_FALLBACK, x [T, d] in ``dtype`` fills fully dropped tokens;
+    shared_out (fp32 [T, d], moe_shared_expert's output) is added to every token."""
     dev = slot_out.device
     d = slot_out.shape[1]
     _check(slot_out, "slot_out", dev, torch.float32)
     _check(inv, "inv", dev, torch.int32)
     _check(x, "x", dev, dtype, (T, d))
+    _check(shared_out, "shared_out", dev, torch.float32, (T, d))
     y = torch.empty((T, d), dtype=torch.float32 if (flags & MOE_FLAG_Y_F32) else dtype, device=dev)
-    st = _lib.moe_combine(_ptr(slot_out), _ptr(inv), _ptr(x), T, d, k, _dtype_code(dtype),
-                          int(flags), _ptr(y), _stream(dev))
+    st = _lib.moe_combine(_ptr(slot_out), _ptr(inv), _ptr(x), _ptr(shared_out), T, d, k,
+                          _dtype_code(dtype), int(flags), _ptr(y), _stream(dev))
     _raise(st, "moe_combine")
     return y
 
 
 def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: float,
                 workspace: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
-                want_routing: bool = False, flags: int = 0):
+                want_routing: bool = False, flags: int = 0,
+                shared_out: Optional[torch.Tensor] = None):
     """Steps 1-7 in one enqueue. Returns y, or (y, extras) when want_routing is set;
     extras holds logits, topk_idx, inv, req_counts, counts, n_dropped (device tensors).
-    flags: any MOE_FLAG_* (MOE_FLAG_Y_F32 makes y float32)."""
+    flags: any MOE_FLAG_* (MOE_FLAG_Y_F32 makes y float32). shared_out: fp32
+    [T, d] from moe_shared_expert, added to every token before y's rounding."""
     dev = x.device
     T, d = x.shape
     N, d_ff, _ = W1.shape
@@ -270,6 +309,7 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
     _check(W2, "W2", dev, x.dtype, (N, d, d_ff))
     _check(b1, "b1", dev, x.dtype, (N, d_ff))
     _check(b2, "b2", dev, x.dtype, (N, d))
+    _check(shared_out, "shared_out", dev, torch.float32, (T, d))
     y_dtype = torch.float32 if (flags & MOE_FLAG_Y_F32) else x.dtype
     if y is None:
         y = torch.empty((T, d), dtype=y_dtype, device=dev)
@@ -290,7 +330,8 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
         }
     st = _lib.moe_forward(_ptr(x), _ptr(W_g), _ptr(logit_bias), _ptr(W1), _ptr(b1), _ptr(W2),
                           _ptr(b2), T, d, d_ff, N, k, float(capacity_factor), _dtype_code(x.dtype),
-                          int(flags), _ptr(y), _ptr(ex.get("logits")), _ptr(ex.get("topk_idx")), _ptr(ex.get("inv")),
+                          int(flags), _ptr(shared_out), _ptr(y), _ptr(ex.get("logits")),
+                          _ptr(ex.get("topk_idx")), _ptr(ex.get("inv")),
                           _ptr(ex.get("req_counts")), _ptr(ex.get("counts")), _ptr(ex.get("n_dropped")),
                           _ptr(workspace), workspace.numel(), _stream(dev))
     _raise(st, "moe_forward")

@@ -5,9 +5,11 @@
 // (Y[t] += w * o over the token's experts); a dropped pick adds nothing and a
 // token with every pick dropped gets zeros (its residual path lives outside
 // the layer), or its input row when the caller asks for the pseudocode's
-// identity fallback (x not null). The gate-scaled expert outputs arrive in
-// fp32. Each thread owns 16 bytes of one output row: coalesced fp32 loads per
-// kept pick, one 16-byte store.
+// identity fallback (x not null). A shared expert's fp32 output, when given,
+// is added to every token last (after the fallback, which replaces only the
+// routed part), so y is still rounded once. The gate-scaled expert outputs
+// arrive in fp32. Each thread owns 16 bytes of one output row: coalesced fp32
+// loads per kept pick, one 16-byte store.
 #include "moe_common.h"
 
 namespace moe {
@@ -22,10 +24,24 @@ __device__ __forceinline__ void load_x_row(const XT* __restrict__ x, int t, int 
   for (int i = 0; i < V; ++i) acc[i] = to_f32(x[(size_t)t * d + c + i]);
 }
 
+// acc += sh[t][c .. c+V) (shared expert output, fp32)
+template <int V>
+__device__ __forceinline__ void add_shared(const float* __restrict__ sh, int t, int d, int c,
+                                           float (&acc)[V]) {
+  const f32x4* src = (const f32x4*)(sh + (size_t)t * d + c);
+#pragma unroll
+  for (int h = 0; h < V / 4; ++h) {
+    const f32x4 v = src[h];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[4 * h + i] += v[i];
+  }
+}
+
 template <typename T, typename XT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ slot_out,
                                                       const int32_t* __restrict__ inv, int T_,
                                                       int d, int k, const XT* __restrict__ x,
+                                                      const float* __restrict__ sh,
                                                       T* __restrict__ y) {
   constexpr int V = 16 / sizeof(T);  // output elements per 16-byte store
   const int vpr = d / V;             // vectors per row (d % 8 == 0)
@@ -65,6 +81,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
   }
   if (!any && x != nullptr) load_x_row<V>(x, t, d, c, acc);
+  if (sh != nullptr) add_shared<V>(sh, t, d, c, acc);
   i32x4 outv;
   T* o = (T*)&outv;
 #pragma unroll
@@ -81,7 +98,7 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(
     const float* __restrict__ part, int nsplit, int S_cap, const B* __restrict__ bias,
     const float* __restrict__ gate, const int32_t* __restrict__ off, int N,
     const int32_t* __restrict__ inv, int T_, int d, int k, const XT* __restrict__ x,
-    T* __restrict__ y) {
+    const float* __restrict__ sh, T* __restrict__ y) {
 #pragma clang fp contract(off)
   constexpr int V = 16 / sizeof(T);
   const int vpr = d / V;
@@ -127,6 +144,7 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(
     }
   }
   if (!any && x != nullptr) load_x_row<V>(x, t, d, c, acc);
+  if (sh != nullptr) add_shared<V>(sh, t, d, c, acc);
   i32x4 outv;
   T* o = (T*)&outv;
 #pragma unroll
@@ -137,8 +155,8 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(
 }  // namespace
 
 hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, int d, int k,
-                                 int y_dtype, const void* x, int x_dtype, void* y,
-                                 hipStream_t st) {
+                                 int y_dtype, const void* x, int x_dtype, const float* sh,
+                                 void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
   // the split-K path exists for bf16 weights (and activations) only; y may be
   // fp32 or bf16
@@ -151,16 +169,17 @@ hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, in
   if (y_dtype == kF32)
     hipLaunchKernelGGL((combine_splitk_kernel<float, bf16, bf16>), dim3(blocks), dim3(256), 0, st,
                        sk.part, sk.nsplit, sk.S_cap, b, sk.gate, sk.off, sk.N, inv, T, d, k, xb,
-                       (float*)y);
+                       sh, (float*)y);
   else
     hipLaunchKernelGGL((combine_splitk_kernel<bf16, bf16, bf16>), dim3(blocks), dim3(256), 0, st,
                        sk.part, sk.nsplit, sk.S_cap, b, sk.gate, sk.off, sk.N, inv, T, d, k, xb,
-                       (bf16*)y);
+                       sh, (bf16*)y);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d, int k,
-                          int y_dtype, const void* x, int x_dtype, void* y, hipStream_t st) {
+                          int y_dtype, const void* x, int x_dtype, const float* sh, void* y,
+                          hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int V = y_dtype == kF32 ? 4 : 8;
   const long long n = (long long)T * (d / V);
@@ -169,17 +188,17 @@ hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d
   if (y_dtype == kF32) {
     if (x_dtype == kBF16)
       hipLaunchKernelGGL((combine_kernel<float, bf16>), dim3(blocks), dim3(256), 0, st, so, inv,
-                         T, d, k, (const bf16*)x, (float*)y);
+                         T, d, k, (const bf16*)x, sh, (float*)y);
     else
       hipLaunchKernelGGL((combine_kernel<float, float>), dim3(blocks), dim3(256), 0, st, so, inv,
-                         T, d, k, (const float*)x, (float*)y);
+                         T, d, k, (const float*)x, sh, (float*)y);
   } else {
     if (x_dtype == kBF16)
       hipLaunchKernelGGL((combine_kernel<bf16, bf16>), dim3(blocks), dim3(256), 0, st, so, inv,
-                         T, d, k, (const bf16*)x, (bf16*)y);
+                         T, d, k, (const bf16*)x, sh, (bf16*)y);
     else
       hipLaunchKernelGGL((combine_kernel<bf16, float>), dim3(blocks), dim3(256), 0, st, so, inv,
-                         T, d, k, (const float*)x, (bf16*)y);
+                         T, d, k, (const float*)x, sh, (bf16*)y);
   }
   return hipGetLastError();
 }

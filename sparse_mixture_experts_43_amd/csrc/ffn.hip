@@ -753,4 +753,40 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
                                                 s.part, st);
 }
 
+namespace {
+// Identity dispatch of a shared expert: one expert holding every token in
+// order (slot t = token t), combine weight 1.
+__global__ __launch_bounds__(256) void identity_dispatch_kernel(int T, int32_t* __restrict__ perm,
+                                                                int32_t* __restrict__ off,
+                                                                float* __restrict__ gate) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < T) {
+    perm[t] = t;
+    gate[t] = 1.0f;
+  }
+  if (t == 0) {
+    off[0] = 0;
+    off[1] = T;
+  }
+}
+}  // namespace
+
+void carve_shared(Carver& c, int T, int d, int d_fs, int dtype, int flags, SharedScratch* s) {
+  const size_t n = (size_t)(T > 0 ? T : 1);
+  s->perm = c.take<int32_t>(n);
+  s->off = c.take<int32_t>(2);
+  s->gate = c.take<float>(n);
+  carve_ffn(c, T, d, d_fs, 1, 1, T, T, dtype, flags, &s->fs);
+}
+
+hipError_t launch_shared_expert(const void* x, const void* W1s, const void* b1s, const void* W2s,
+                                const void* b2s, int T, int d, int d_fs, int dtype, int flags,
+                                float* out, const SharedScratch& s, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(identity_dispatch_kernel, dim3(cdiv(T, 256)), dim3(256), 0, st, T, s.perm,
+                     s.off, s.gate);
+  return launch_expert_ffn(x, s.perm, s.off, s.gate, W1s, b1s, W2s, b2s, T, d, d_fs, 1, 1, T, T,
+                           dtype, flags, out, s.fs, st, nullptr);
+}
+
 }  // namespace moe

@@ -91,6 +91,13 @@ static size_t dispatch_bytes(int T, int N, int k) {
   return align_up(c.off, 256);
 }
 
+static size_t shared_bytes(int T, int d, int d_fs, int dtype, int flags) {
+  Carver c(nullptr);
+  SharedScratch ss;
+  carve_shared(c, T, d, d_fs, dtype, flags, &ss);
+  return align_up(c.off, 256);
+}
+
 static size_t ffn_bytes(int T, int d, int d_ff, int N, int k, int C, int dtype, int flags) {
   Carver c(nullptr);
   FfnScratch fs;
@@ -105,7 +112,7 @@ using namespace moe;
 
 extern "C" {
 
-int moe_version(void) { return 101; }
+int moe_version(void) { return 102; }
 
 const char* moe_strerror(int status) {
   switch (status) {
@@ -147,6 +154,41 @@ size_t moe_workspace_bytes(int T, int d, int d_ff, int N, int k, double capacity
   b = b > ec.bytes ? b : ec.bytes;
   const size_t sb = align_up(stats_scratch_bytes(T, N), 256);  // moe_routing_stats
   return b > sb ? b : sb;
+}
+
+size_t moe_shared_workspace_bytes(int T, int d, int d_fs, int dtype) {
+  if (check_shape(T, d, d_fs, 1, 1, dtype, true) != MOE_OK) return 0;
+  const size_t a = shared_bytes(T, d, d_fs, dtype, MOE_FLAG_HIDDEN_SPLIT);
+  const size_t b = shared_bytes(T, d, d_fs, dtype, 0);
+  return a > b ? a : b;
+}
+
+int moe_shared_expert(const void* x, const void* W1s, const void* b1s, const void* W2s,
+                      const void* b2s, int T, int d, int d_fs, int dtype, int flags, float* out,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_shape(T, d, d_fs, 1, 1, dtype, true);
+  if (st != MOE_OK) return st;
+  if (flags & ~MOE_FLAG_HIDDEN_SPLIT) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !W1s || !W2s || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(W1s, 16) || !aligned(W2s, 16) || !aligned(out, 16) ||
+      (b1s && !aligned(b1s, 16)) || (b2s && !aligned(b2s, 16)))
+    return MOE_ERR_UNSUPPORTED;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < shared_bytes(T, d, d_fs, dtype, flags))
+    return MOE_ERR_WORKSPACE;
+  Carver c(workspace);
+  SharedScratch ss;
+  carve_shared(c, T, d, d_fs, dtype, flags, &ss);
+  // the expert FFN's profiling marks belong to moe_forward's sequence
+  void* saved[kProfileSlots];
+  for (int i = 0; i < kProfileSlots; ++i) {
+    saved[i] = g_prof[i];
+    g_prof[i] = nullptr;
+  }
+  const hipError_t e = launch_shared_expert(x, W1s, b1s, W2s, b2s, T, d, d_fs, dtype, flags, out,
+                                            ss, (hipStream_t)stream);
+  for (int i = 0; i < kProfileSlots; ++i) g_prof[i] = saved[i];
+  return hip_status(e);
 }
 
 int moe_route(const void* x, const void* W_g, const float* logit_bias, int T, int d, int N, int k,
@@ -230,8 +272,8 @@ int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
                                       (hipStream_t)stream));
 }
 
-int moe_combine(const void* slot_out, const int32_t* inv, const void* x, int T, int d, int k,
-                int dtype, int flags, void* y, void* stream) {
+int moe_combine(const void* slot_out, const int32_t* inv, const void* x, const float* shared_out,
+                int T, int d, int k, int dtype, int flags, void* y, void* stream) {
   if (T < 0 || k < 1 || k > kMaxK || d < 8 || d > 65536 || (d % 8) != 0) {
     return (T < 0 || k < 1 || k > kMaxK) ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED;
   }
@@ -241,16 +283,18 @@ int moe_combine(const void* slot_out, const int32_t* inv, const void* x, int T, 
   if (T == 0) return MOE_OK;
   const bool fallback = (flags & MOE_FLAG_IDENTITY_FALLBACK) != 0;
   if (!slot_out || !inv || !y || (fallback && !x)) return MOE_ERR_INVALID_ARG;
-  if (!aligned(slot_out, 16) || !aligned(y, 16) || (fallback && !aligned(x, 16)))
+  if (!aligned(slot_out, 16) || !aligned(y, 16) || (fallback && !aligned(x, 16)) ||
+      (shared_out && !aligned(shared_out, 16)))
     return MOE_ERR_UNSUPPORTED;
   const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
   return hip_status(launch_combine(slot_out, inv, T, d, k, y_dtype, fallback ? x : nullptr, dtype,
-                                   y, (hipStream_t)stream));
+                                   shared_out, y, (hipStream_t)stream));
 }
 
 int moe_forward(const void* x, const void* W_g, const float* logit_bias, const void* W1,
                 const void* b1, const void* W2, const void* b2, int T, int d, int d_ff, int N,
-                int k, double capacity_factor, int dtype, int flags, void* y, float* logits_opt,
+                int k, double capacity_factor, int dtype, int flags, const float* shared_out,
+                void* y, float* logits_opt,
                 int32_t* topk_idx_opt, int32_t* inv_opt, int32_t* req_counts_opt,
                 int32_t* counts_opt, int32_t* n_dropped_opt, void* workspace, size_t ws_bytes,
                 void* stream) {
@@ -267,7 +311,8 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
   if (!x || !W_g || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(W_g, 16) || !aligned(W1, 16) || !aligned(W2, 16) ||
       !aligned(y, 16) || (b1 && !aligned(b1, 16)) || (b2 && !aligned(b2, 16)) ||
-      (logit_bias && !aligned(logit_bias, 4)) || (logits_opt && !aligned(logits_opt, 4)))
+      (logit_bias && !aligned(logit_bias, 4)) || (logits_opt && !aligned(logits_opt, 4)) ||
+      (shared_out && !aligned(shared_out, 16)))
     return MOE_ERR_UNSUPPORTED;
   const int C = capacity_host(T, N, k, capacity_factor);
   // pairs per token: k picks, or with expert choice every expert (pair t*N + e)
@@ -303,8 +348,9 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
   if (e != hipSuccess) return hip_status(e);
   const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
   const void* xf = (flags & MOE_FLAG_IDENTITY_FALLBACK) ? x : nullptr;
-  e = sk.nsplit > 1 ? launch_combine_splitk(sk, f.inv, T, d, kp, y_dtype, xf, dtype, y, s)
-                    : launch_combine(f.slot_out, f.inv, T, d, kp, y_dtype, xf, dtype, y, s);
+  e = sk.nsplit > 1
+          ? launch_combine_splitk(sk, f.inv, T, d, kp, y_dtype, xf, dtype, shared_out, y, s)
+          : launch_combine(f.slot_out, f.inv, T, d, kp, y_dtype, xf, dtype, shared_out, y, s);
   profile_mark(6, s);
   return hip_status(e);
 }

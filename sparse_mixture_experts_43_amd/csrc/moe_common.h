@@ -177,11 +177,26 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
                              int S_max, int dtype, int flags, void* slot_out,
                              const FfnScratch& s, hipStream_t st, SplitK* defer = nullptr);
 // y_dtype: dtype of y; x (x_dtype, [T, d]) is read for tokens with no kept
-// pick when not null (identity fallback), else such tokens get zeros.
+// pick when not null (identity fallback), else such tokens get zeros; sh (fp32
+// [T, d], a shared expert's output) is added to every token when not null.
 hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d, int k,
-                          int y_dtype, const void* x, int x_dtype, void* y, hipStream_t st);
+                          int y_dtype, const void* x, int x_dtype, const float* sh, void* y,
+                          hipStream_t st);
 hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, int d, int k,
-                                 int y_dtype, const void* x, int x_dtype, void* y,
-                                 hipStream_t st);
+                                 int y_dtype, const void* x, int x_dtype, const float* sh,
+                                 void* y, hipStream_t st);
+// Shared expert: the grouped expert FFN run as one expert that holds every
+// token (slot t = token t, weight 1); out fp32 [T, d]. Scratch from
+// carve_shared (the identity dispatch plus the FFN scratch).
+struct SharedScratch {
+  int32_t* perm;  // [T]
+  int32_t* off;   // [2]
+  float* gate;    // [T]
+  FfnScratch fs;
+};
+void carve_shared(Carver& c, int T, int d, int d_fs, int dtype, int flags, SharedScratch* s);
+hipError_t launch_shared_expert(const void* x, const void* W1s, const void* b1s, const void* W2s,
+                                const void* b2s, int T, int d, int d_fs, int dtype, int flags,
+                                float* out, const SharedScratch& s, hipStream_t st);
 
 }  // namespace moe

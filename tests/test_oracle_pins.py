@@ -33,7 +33,10 @@ Pins used (none of them re-types the oracle's own formula):
   * expert-choice routing: with no capacity limit every expert takes every
     token, which is the dense softmax mixture of all experts; every expert
     takes exactly min(C, T) tokens; pure-Python selection per expert
-    (oracle/brute.py), with and without the identity fallback.
+    (oracle/brute.py), with and without the identity fallback;
+  * shared expert: with one routed expert and top-1 the layer is the sum of
+    two plain nn.Sequential MLPs; with every routed pick dropped it is the
+    shared MLP alone (plus the input row under the identity fallback).
 """
 from __future__ import annotations
 
@@ -425,13 +428,50 @@ def pin_expert_choice_balance_and_brute():
             np.testing.assert_allclose(res["y"], yb, rtol=1e-11, atol=1e-12)
 
 
+def _mlp(W1, b1, W2, b2):
+    d_ff, d = W1.shape
+    m = torch.nn.Sequential(torch.nn.Linear(d, d_ff, dtype=torch.float64), torch.nn.GELU(),
+                            torch.nn.Linear(d_ff, d, dtype=torch.float64))
+    with torch.no_grad():
+        m[0].weight.copy_(W1); m[0].bias.copy_(b1)
+        m[2].weight.copy_(W2); m[2].bias.copy_(b2)
+    return m
+
+
+def pin_shared_expert():
+    rng = np.random.default_rng(10)
+    T, d, d_ff, d_fs = 9, 6, 8, 5
+    x, W_g, W1, b1, W2, b2 = _rand_layer(rng, T, d, d_ff, 1)
+    W1s = torch.from_numpy(rng.standard_normal((d_fs, d)) / math.sqrt(d))
+    W2s = torch.from_numpy(rng.standard_normal((d, d_fs)) / math.sqrt(d_fs))
+    b1s = torch.from_numpy(rng.standard_normal(d_fs) * 0.1)
+    b2s = torch.from_numpy(rng.standard_normal(d) * 0.1)
+    shared = (W1s, b1s, W2s, b2s)
+    ref_s = _mlp(W1s, b1s, W2s, b2s)(x).detach().numpy()
+    # one routed expert, top-1: routed MLP + shared MLP
+    res = M.moe_forward(x, W_g, None, W1, b1, W2, b2, k=1, capacity_factor=0.0, shared=shared)
+    ref = _mlp(W1[0], b1[0], W2[0], b2[0])(x).detach().numpy() + ref_s
+    np.testing.assert_allclose(res["y"], ref, rtol=1e-12, atol=1e-13)
+    # every routed pick but the first dropped (capacity 1): the shared MLP alone,
+    # or the input row plus it under the identity fallback
+    for identity in (False, True):
+        res = M.moe_forward(x, W_g, None, W1, b1, W2, b2, k=1, capacity_factor=0.0, C=1,
+                            shared=shared, identity_fallback=identity)
+        tail = ref_s[1:] + (x[1:].numpy() if identity else 0.0)
+        np.testing.assert_allclose(res["y"][1:], tail, rtol=1e-12, atol=1e-13)
+    # the sampled-token form agrees with the full form
+    res_t = M.moe_forward(x, W_g, None, W1, b1, W2, b2, k=1, capacity_factor=0.0, shared=shared,
+                          tokens=[0, 4, 8])
+    np.testing.assert_allclose(res_t["y"], ref[[0, 4, 8]], rtol=1e-12, atol=1e-13)
+
+
 PINS = [pin_worked_example, pin_capacity_formula, pin_gelu_textbook, pin_topk_then_softmax_router,
         pin_topk_ties_lower_expert, pin_k1_gates_exactly_one, pin_dense_mixture_k_equals_n,
         pin_single_expert_is_mlp, pin_brute_force, pin_linear_experts_closed_form,
         pin_dispatch_invariants, pin_capacity_ties_lower_token, pin_routing_stats_uniform,
         pin_routing_stats_collapse, pin_routing_stats_code_form, pin_first_come_worked_example,
         pin_renorm_worked_example, pin_identity_fallback, pin_brute_force_policies,
-        pin_expert_choice_dense, pin_expert_choice_balance_and_brute]
+        pin_expert_choice_dense, pin_expert_choice_balance_and_brute, pin_shared_expert]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -442,7 +482,8 @@ def test_pin(pin):
 # ------------------------------------------------------------- mutants ----
 _orig = {n: getattr(M, n) for n in ("gelu", "route_topk", "capacity", "capacity_dispatch",
                                     "expert_ffn_rows", "combine", "routing_stats",
-                                    "renormalise_survivors", "expert_choice_dispatch")}
+                                    "renormalise_survivors", "expert_choice_dispatch",
+                                    "shared_expert_out")}
 
 
 def _mut_gelu_tanh(z):
@@ -593,6 +634,11 @@ def _mut_ec_gate_renormalised(L, C):
     return disp
 
 
+def _mut_shared_no_b2(x, shared, tokens=None):
+    W1s, b1s, W2s, b2s = shared
+    return _orig["shared_expert_out"](x, (W1s, b1s, W2s, None), tokens)
+
+
 MUTANTS = {
     "gelu_tanh_approx": ("gelu", _mut_gelu_tanh),
     "no_renormalisation": ("route_topk", _mut_no_renorm),
@@ -614,6 +660,7 @@ MUTANTS = {
     "identity_fallback_ignored": ("combine", _mut_fallback_ignored),
     "expert_choice_by_token_order": ("expert_choice_dispatch", _mut_ec_first_tokens),
     "expert_choice_gate_renormalised": ("expert_choice_dispatch", _mut_ec_gate_renormalised),
+    "shared_expert_second_bias_dropped": ("shared_expert_out", _mut_shared_no_b2),
 }
 
 
