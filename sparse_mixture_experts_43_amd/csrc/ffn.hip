@@ -532,12 +532,20 @@ Plan make_plan(int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype
 
 
 
+// Ring slots of a grouped GEMM: 4, or 3 where the split hidden layer's extra
+// token rows would otherwise leave one workgroup per CU (128x128 tiles: 96 KB
+// at 4 slots, 72 KB at 3); the 128x128 tiles issue each stage's copies at the
+// start of a step (EARLY), which a 3-slot ring needs.
+constexpr int ring_slots(bool alo) { return alo ? 3 : kRing; }
+
 // Largest persistent grid a ring GEMM of this shape is launched with (and the
 // split-tail partial buffer is sized for): the workgroups that fit in LDS on
-// 256 CUs, at most one per tile, a multiple of 8.
+// 256 CUs, at most one per tile, a multiple of 8. (With ring_slots, the split
+// second GEMM fits no more workgroups than the first, so the partial buffer
+// sized for alo = false covers both.)
 constexpr int kRingCUs = 256;
 int ring_grid_bound(int BM, int BN, bool alo, int max_tiles) {
-  const int lds = kRing * (BM + BN + (alo ? BM : 0)) * kRowB;
+  const int lds = ring_slots(alo) * (BM + BN + (alo ? BM : 0)) * kRowB;
   int occ = (160 * 1024) / lds;
   occ = occ < 1 ? 1 : occ;
   const int g = cdiv(max_tiles > 0 ? max_tiles : 1, 8) * 8;
@@ -559,13 +567,15 @@ void launch_gemm(const bf16* A, const bf16* A_lo, const int32_t* perm, int k, co
   constexpr bool ALO = SPLIT && !G1;
   if (K % kRK == 0) {
     constexpr int MODE = G1 ? kEpiGelu : kEpiGate;
-    const size_t lds = (size_t)kRing * (BM + BN + (ALO ? BM : 0)) * kRowB;
-    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, kRing>), lds);
-    int pgrid = ring_grid((const void*)gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, kRing>, NTH,
-                          lds, grid);
+    constexpr int R = ring_slots(ALO);
+    constexpr bool EARLY = BM < 256;
+    const size_t lds = (size_t)R * (BM + BN + (ALO ? BM : 0)) * kRowB;
+    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, R, EARLY>), lds);
+    int pgrid = ring_grid((const void*)gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, R, EARLY>,
+                          NTH, lds, grid);
     const int bound = ring_grid_bound(BM, BN, ALO, grid);
     pgrid = pgrid < bound ? pgrid : bound;
-    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, kRing>), dim3(pgrid),
+    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, R, EARLY>), dim3(pgrid),
                        dim3(NTH), lds, st, A, A_lo, perm, k, W, (const void*)bias, gate, tl, cnt, K,
                        Nout, out, out_lo, 0, 0, part);
     if (part != nullptr) {

@@ -243,7 +243,13 @@ __device__ __forceinline__ void ring_decode_tile(int tile, const int4* __restric
 
 // part: fp32 partial tiles of the split tail (2 per workgroup, BM*BN each) or
 // NULL (whole tiles only).
-template <int BM, int BN, int WM, int WN, int MODE, bool SPLIT, int RING>
+// EARLY: every ring step issues all copies of stage kt+RING-1 at its start and
+// waits for stage kt+1 with the two stages after it in flight; otherwise a
+// stage's copies go out over two steps (below). The two-step form measured
+// better on the 256x256 prefill tiles, the early form on the 128x128 tiles of
+// capacity-limited layers, where it also lets a 3-slot ring (the split hidden
+// layer's extra token rows) keep one stage in flight with two workgroups per CU.
+template <int BM, int BN, int WM, int WN, int MODE, bool SPLIT, int RING, bool EARLY = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ A_lo, const int32_t* __restrict__ perm,
     int kpairs, const bf16* __restrict__ W, const void* __restrict__ bias,
@@ -264,6 +270,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   constexpr int STAGE = L_OFF + (ALO ? BM * kRowB : 0);
   static_assert(AI >= 1 && BI >= 1, "tile too small for the wave count");
   static_assert(RING >= 3 && (RING - 2) * LPS < 64, "ring depth / vmcnt range");
+  static_assert(EARLY || RING >= 4, "the two-step copies need a stage of slack");
   static_assert(BM / WM == 2, "two wave rows (token blocks alternate between them)");
   static_assert(MT % 2 == 0, "token blocks are skipped in pairs");
 
@@ -365,7 +372,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
         dma16(pb[i] + kbyte, st + B_OFF + (i * NW + wv) * 1024);
     }
   };
-  // prologue of an item: stages 0 .. RING-3 whole, stage RING-2 part 0
+  // prologue of an item: stages 0 .. RING-3 whole, stage RING-2 part 0 (EARLY:
+  // stage RING-2 whole as well)
   auto issue_prologue = [&]() {
 #pragma unroll
     for (int q = 0; q < RING - 2; ++q) {
@@ -373,6 +381,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
       issue_part(q, 1);
     }
     issue_part(RING - 2, 0);
+    if constexpr (EARLY) issue_part(RING - 2, 1);
   };
 
   // Fragment reads (v_mfma_f32_16x16x32_bf16 operands): lane l reads row
@@ -433,26 +442,36 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
     using lo0 = std::integral_constant<int, 0>;
     using mid = std::integral_constant<int, H>;
     using hi1 = std::integral_constant<int, NA>;
+    // copies issued in the first half of a step: part 1 of stage kt+RING-2, or
+    // (EARLY) all of stage kt+RING-1
+    constexpr int C1 = EARLY ? LPS : BI;
     auto step = [&](int kt, auto set_c) {
       constexpr int SET = decltype(set_c)::value;
-      issue_part(kt + RING - 2, 1);
+      if constexpr (EARLY) {
+        // the slot of stage kt-1: every wave finished reading it before the
+        // barrier of step kt-1
+        issue_part(kt + RING - 1, 0);
+        issue_part(kt + RING - 1, 1);
+      } else {
+        issue_part(kt + RING - 2, 1);
+      }
       mma(SET, lo0{}, mid{});
       if constexpr (M1 > 0) {
-        // the weight-row copies of stage kt+RING-2 spread over the first half
+        // those copies spread over the first half
 #pragma unroll
-        for (int q = 0; q < BI; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, M1 / BI > 0 ? M1 / BI : 1, 0);
+        for (int q = 0; q < C1; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, M1 / C1 > 0 ? M1 / C1 : 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
       // stage kt+1 has landed (only the stages issued after it may still fly)
       // and no wave still reads the slot of stage kt-1
-      vm_wait_n<(RING - 3) * LPS>();
+      vm_wait_n<(EARLY ? RING - 2 : RING - 3) * LPS>();
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
       read_frags(kt + 1, SET ^ 1, na_c);  // past the last stage: reads a dead slot, never used
-      issue_part(kt + RING - 1, 0);
+      if constexpr (!EARLY) issue_part(kt + RING - 1, 0);
       mma(SET, mid{}, hi1{});
       if constexpr (M1 > 0) {
         // one MFMA, one fragment read of the next stage, ...; then the
@@ -463,7 +482,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
 #pragma unroll
-        for (int q = 0; q < LPS - BI; ++q) {
+        for (int q = 0; q < LPS - C1; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
@@ -488,10 +507,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   ring_decode_tile<MODE, BM, BN>(tile, tiles, M_total, Nout, e, m0, mcount, n0);
   set_ptrs(e, m0, mcount, n0);
   // Every ring step issues exactly LPS loads per wave (part 1 of stage
-  // kt+RING-2, then part 0 of stage kt+RING-1; past the last stage the copies
-  // land in slots nobody reads), so at the mid-step wait of step kt only the
-  // copies of stages kt+2 .. kt+RING-2 may still fly: vmcnt <= (RING-3)*LPS
-  // means stage kt+1 has landed.
+  // kt+RING-2, then part 0 of stage kt+RING-1; EARLY: stage kt+RING-1 whole;
+  // past the last stage the copies land in slots nobody reads), so at the
+  // mid-step wait of step kt only the copies of stages kt+2 .. kt+RING-2 (EARLY:
+  // kt+RING-1) may still fly: vmcnt <= (RING-3)*LPS (EARLY: (RING-2)*LPS) means
+  // stage kt+1 has landed.
   issue_prologue();
 
   for (int it = 0;;) {
