@@ -28,14 +28,19 @@ constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- phase 2
 // Row r of the block's logits tile (LDS, row stride ls_stride floats).
-// `logits` may be null (the row is already in global memory).
-__device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, int k, int t, float* __restrict__ logits,
-                         int32_t* __restrict__ idx, float* __restrict__ w, double* __restrict__ key) {
+// `logits` may be null (the row is already in global memory). S: 64-expert
+// slots per lane, S * 64 >= N (slots past N add nothing, so every S gives the
+// same bits; topk_row picks the smallest).
+template <int S>
+__device__ __forceinline__ void topk_row_s(const float* __restrict__ Lrow, int N, int k, int t,
+                                           float* __restrict__ logits, int32_t* __restrict__ idx,
+                                           float* __restrict__ w, double* __restrict__ key) {
+  static_assert(S >= 1 && S <= kMaxN / kWave, "slots");
   const int l = lane_id();
-  float v[kMaxN / kWave];
+  float v[S];
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kMaxN / kWave; ++i) {
+  for (int i = 0; i < S; ++i) {
     const int n = l + kWave * i;
     v[i] = (n < N) ? Lrow[n] : -INFINITY;
     if (n < N) {
@@ -49,7 +54,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, 
   double s = 0.0;
   const double md = (double)m;
 #pragma unroll
-  for (int i = 0; i < kMaxN / kWave; ++i) {
+  for (int i = 0; i < S; ++i) {
     const int n = l + kWave * i;
     if (n < N) s += exp((double)v[i] - md);
   }
@@ -67,7 +72,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, 
     float bv = -INFINITY;
     int bn = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < kMaxN / kWave; ++i) {
+    for (int i = 0; i < S; ++i) {
       const int n = l + kWave * i;
       if (n < N && !((taken >> i) & 1u) && (v[i] > bv || bn == 0x7fffffff)) {
         bv = v[i];
@@ -99,6 +104,15 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, 
   }
 }
 
+__device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, int k, int t,
+                                         float* __restrict__ logits, int32_t* __restrict__ idx,
+                                         float* __restrict__ w, double* __restrict__ key) {
+  if (N <= 64) topk_row_s<1>(Lrow, N, k, t, logits, idx, w, key);
+  else if (N <= 128) topk_row_s<2>(Lrow, N, k, t, logits, idx, w, key);
+  else if (N <= 256) topk_row_s<4>(Lrow, N, k, t, logits, idx, w, key);
+  else if (N <= 512) topk_row_s<8>(Lrow, N, k, t, logits, idx, w, key);
+  else topk_row_s<kMaxN / kWave>(Lrow, N, k, t, logits, idx, w, key);
+}
 
 // N <= 16: the same as topk_row with one 16-lane group per token row (lane c
 // of the group holds expert c), so a wave serves 4 rows. The reductions are
@@ -161,18 +175,15 @@ __device__ __forceinline__ void topk_row16(const float* __restrict__ Lrow, bool 
 // t*N + e gets expert e, weight p[t,e] (the softmax probability itself) and the
 // fp64 rank key L[t,e] - lse_t, computed as in topk_row (wave max, per-lane
 // sums of exp over the lane's experts, xor butterfly). One wave per token.
-__global__ __launch_bounds__(256) void ec_route_kernel(const float* __restrict__ logits, int T,
-                                                       int N, int32_t* __restrict__ idx,
-                                                       float* __restrict__ w,
-                                                       double* __restrict__ key) {
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (t >= T) return;
+template <int S>
+__device__ __forceinline__ void ec_route_row(const float* __restrict__ row, int t, int N,
+                                             int32_t* __restrict__ idx, float* __restrict__ w,
+                                             double* __restrict__ key) {
   const int l = lane_id();
-  const float* row = logits + (size_t)t * N;
-  float v[kMaxN / kWave];
+  float v[S];
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kMaxN / kWave; ++i) {
+  for (int i = 0; i < S; ++i) {
     const int n = l + kWave * i;
     v[i] = (n < N) ? row[n] : -INFINITY;
     if (n < N) m = fmaxf(m, v[i]);
@@ -181,14 +192,14 @@ __global__ __launch_bounds__(256) void ec_route_kernel(const float* __restrict__
   const double md = (double)m;
   double s = 0.0;
 #pragma unroll
-  for (int i = 0; i < kMaxN / kWave; ++i) {
+  for (int i = 0; i < S; ++i) {
     const int n = l + kWave * i;
     if (n < N) s += exp((double)v[i] - md);
   }
   s = wave_sum_f64(s);
   const double lse = md + log(s);
 #pragma unroll
-  for (int i = 0; i < kMaxN / kWave; ++i) {
+  for (int i = 0; i < S; ++i) {
     const int n = l + kWave * i;
     if (n < N) {
       const size_t p = (size_t)t * N + n;
@@ -198,6 +209,21 @@ __global__ __launch_bounds__(256) void ec_route_kernel(const float* __restrict__
       w[p] = (float)exp(kk);
     }
   }
+}
+
+__global__ __launch_bounds__(256) void ec_route_kernel(const float* __restrict__ logits, int T,
+                                                       int N, int32_t* __restrict__ idx,
+                                                       float* __restrict__ w,
+                                                       double* __restrict__ key) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * N;
+  // 64-expert slots per lane: the smallest count that covers N
+  if (N <= 64) ec_route_row<1>(row, t, N, idx, w, key);
+  else if (N <= 128) ec_route_row<2>(row, t, N, idx, w, key);
+  else if (N <= 256) ec_route_row<4>(row, t, N, idx, w, key);
+  else if (N <= 512) ec_route_row<8>(row, t, N, idx, w, key);
+  else ec_route_row<kMaxN / kWave>(row, t, N, idx, w, key);
 }
 
 // ---------------------------------------------------------------- W_g transpose
@@ -469,15 +495,23 @@ __global__ __launch_bounds__(kThreads) void router_bf16_kernel(
 }
 
 // ---------------------------------------------------------------- fp32
+// 16 tokens per block; K in chunks of 32; NQ*64 expert columns per pass (NQ =
+// ceil(N/64), at most 4), so few experts cost few columns. The next chunk's x
+// and W_g values are loaded into registers before the current one is
+// multiplied. Top-k per token: 16-lane groups (4 tokens per wave) for N <= 16,
+// a wave per token else.
+template <int NQ>
 __global__ __launch_bounds__(kThreads) void router_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ Wg, const float* __restrict__ bias, int T,
     int d, int N, int k, float* __restrict__ logits, int32_t* __restrict__ idx,
     float* __restrict__ w, double* __restrict__ key) {
-  constexpr int RT = 16, KC = 32, NC = 256;
+  constexpr int RT = 16, KC = 32, NC = 64 * NQ;
+  constexpr int XE = RT * KC / kThreads;  // x values per thread per chunk
+  constexpr int WE = KC * NC / kThreads;  // W_g values per thread per chunk
+  __shared__ float xs[RT * KC];
+  __shared__ float ws[KC * NC];
   extern __shared__ __align__(16) unsigned char smem[];
-  float* xs = (float*)smem;   // [RT][KC]
-  float* ws = xs + RT * KC;   // [KC][NC]
-  float* Ls = ws + KC * NC;   // [RT][NP + 4]
+  float* Ls = (float*)smem;  // [RT][NP + 4]
   const int NP = cdiv(N, 16) * 16;
   const int LS = NP + 4;
   const int tid = threadIdx.x;
@@ -485,34 +519,45 @@ __global__ __launch_bounds__(kThreads) void router_f32_kernel(
   const int rq = (tid / 64) * 4;  // rows rq..rq+3
   const int cq = tid % 64;        // columns cq + 64*q
   for (int c0 = 0; c0 < N; c0 += NC) {
-    float acc[4][4];
+    float acc[4][NQ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[i][q] = 0.f;
+      for (int q = 0; q < NQ; ++q) acc[i][q] = 0.f;
+    float xr[XE], wr[WE];
+    auto load = [&](int kc) {
+#pragma unroll
+      for (int q = 0; q < XE; ++q) {
+        const int e = tid + q * kThreads, r = e / KC, kk = e % KC;
+        xr[q] = (t0 + r < T && kc + kk < d) ? x[(size_t)(t0 + r) * d + kc + kk] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < WE; ++q) {
+        const int e = tid + q * kThreads, kk = e / NC, n = c0 + e % NC;
+        wr[q] = (kc + kk < d && n < N) ? Wg[(size_t)(kc + kk) * N + n] : 0.f;
+      }
+    };
+    load(0);
     for (int kc = 0; kc < d; kc += KC) {
       __syncthreads();
-      for (int e = tid; e < RT * KC; e += kThreads) {
-        const int r = e / KC, kk = e % KC;
-        xs[e] = (t0 + r < T && kc + kk < d) ? x[(size_t)(t0 + r) * d + kc + kk] : 0.f;
-      }
-      for (int e = tid; e < KC * NC; e += kThreads) {
-        const int kk = e / NC, n = c0 + e % NC;
-        ws[e] = (kc + kk < d && n < N) ? Wg[(size_t)(kc + kk) * N + n] : 0.f;
-      }
+#pragma unroll
+      for (int q = 0; q < XE; ++q) xs[tid + q * kThreads] = xr[q];
+#pragma unroll
+      for (int q = 0; q < WE; ++q) ws[tid + q * kThreads] = wr[q];
       __syncthreads();
+      if (kc + KC < d) load(kc + KC);
 #pragma unroll 8
       for (int kk = 0; kk < KC; ++kk) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float xv = xs[(rq + i) * KC + kk];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(xv, ws[kk * NC + cq + 64 * q], acc[i][q]);
+          for (int q = 0; q < NQ; ++q) acc[i][q] = fmaf(xv, ws[kk * NC + cq + 64 * q], acc[i][q]);
         }
       }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const int n = c0 + cq + 64 * q;
       if (n < N) {
         const float b = bias != nullptr ? bias[n] : 0.f;
@@ -523,9 +568,15 @@ __global__ __launch_bounds__(kThreads) void router_f32_kernel(
   }
   __syncthreads();
   const int wv = tid / kWave;
-  for (int r = wv; r < RT; r += 4) {
+  if (N <= 16) {
+    const int r = wv * 4 + (lane_id() >> 4);
     const int t = t0 + r;
-    if (t < T) topk_row(Ls + r * LS, N, k, t, logits, idx, w, key);
+    topk_row16(Ls + r * LS, t < T, N, k, t, logits, idx, w, key);
+  } else {
+    for (int r = wv; r < RT; r += 4) {
+      const int t = t0 + r;
+      if (t < T) topk_row(Ls + r * LS, N, k, t, logits, idx, w, key);
+    }
   }
 }
 
@@ -566,16 +617,29 @@ size_t route_scratch_bytes(int d, int N, int dtype) {
   return align_up((size_t)NP * d * sizeof(bf16), 256);
 }
 
+template <int NQ>
+void launch_route_f32(const void* x, const void* W_g, const float* bias, int T, int d, int N,
+                      int k, size_t lds, float* logits, int32_t* idx, float* w, double* key,
+                      hipStream_t st) {
+  MOE_SET_LDS_ONCE(router_f32_kernel<NQ>, 160 * 1024);
+  hipLaunchKernelGGL(router_f32_kernel<NQ>, dim3(cdiv(T, 16)), dim3(kThreads), lds, st,
+                     (const float*)x, (const float*)W_g, bias, T, d, N, k, logits, idx, w, key);
+}
+
 hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T, int d, int N,
                         int k, int dtype, float* logits, int32_t* idx, float* w, double* key,
                         void* scratch, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (dtype == kF32) {
     const int NP = cdiv(N, 16) * 16;
-    const size_t lds = (16 * 32 + 32 * 256 + 16 * (NP + 4)) * sizeof(float);
-    MOE_SET_LDS_ONCE(router_f32_kernel, 160 * 1024);
-    hipLaunchKernelGGL(router_f32_kernel, dim3(cdiv(T, 16)), dim3(kThreads), lds, st,
-                       (const float*)x, (const float*)W_g, bias, T, d, N, k, logits, idx, w, key);
+    const size_t lds = (size_t)16 * (NP + 4) * sizeof(float);
+    const int nq = cdiv(N, 64) < 4 ? cdiv(N, 64) : 4;
+    switch (nq) {
+      case 1: launch_route_f32<1>(x, W_g, bias, T, d, N, k, lds, logits, idx, w, key, st); break;
+      case 2: launch_route_f32<2>(x, W_g, bias, T, d, N, k, lds, logits, idx, w, key, st); break;
+      case 3: launch_route_f32<3>(x, W_g, bias, T, d, N, k, lds, logits, idx, w, key, st); break;
+      default: launch_route_f32<4>(x, W_g, bias, T, d, N, k, lds, logits, idx, w, key, st); break;
+    }
     return hipGetLastError();
   }
   const int NP = cdiv(N, 16) * 16;
