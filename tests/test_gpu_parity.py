@@ -48,6 +48,11 @@ CASES = [
     ("router_N13", 256, 64, 64, 13, 3, 1.0, "bf16", False, "normal0.5", 0),
     # N*d too large to stage W_g^T in LDS: the transposed-copy router path
     ("router_transposed_N64", 256, 768, 64, 64, 2, 1.0, "bf16", False, "normal0.5", 0),
+    # the documented maxima: N = 1024 experts with k = 16 (the widest top-k
+    # rows), d = 65536 (router and first GEMM over the longest K), d_ff = 65536
+    ("max_N_k", 256, 64, 64, 1024, 16, 1.0, "bf16", False, "normal0.5", 0),
+    ("max_d", 8, 65536, 64, 4, 2, 0.0, "bf16", False, "none", 0),
+    ("max_dff", 8, 64, 65536, 4, 2, 0.0, "bf16", True, "none", 0),
     ("dense_k_eq_N", 128, 64, 128, 4, 4, 0.0, "bf16", False, "none", 0),
     ("single_token", 1, 64, 64, 8, 2, 0.0, "bf16", False, "none", 0),
     ("capacity_one", 64, 64, 64, 8, 2, 0.01, "bf16", False, "zipf1.1", 0),
@@ -82,6 +87,29 @@ def test_parity_small(lib, case):
 def test_parity_tiny_f32_full(lib):
     from gpu_util import run_and_compare
     run_and_compare(WORKLOADS["tiny_f32"], lib, strict=True)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_empty_batch(lib, dt):
+    """T = 0 is a successful no-op through every entry point of the binding."""
+    from gpu_util import to_dev
+    from moe_inputs import make_inputs
+    w = Workload("empty", T=0, d=64, d_ff=128, N=8, k=2, capacity_factor=1.0, dtype=dt,
+                 ffn_bias=True, skew="none")
+    dv = to_dev(make_inputs(w))
+    args = (dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"], dv["b2"], 2, 1.0)
+    y = lib.moe_forward(*args)
+    y32, ex = lib.moe_forward(*args, flags=lib.MOE_FLAG_Y_F32, want_routing=True)
+    yec = lib.moe_forward(*args, flags=lib.MOE_FLAG_EXPERT_CHOICE | lib.MOE_FLAG_IDENTITY_FALLBACK)
+    ysh = lib.moe_forward(*args, shared_out=torch.empty((0, 64), dtype=torch.float32, device="cuda"))
+    logits, idx, gw, gkey = lib.moe_route(dv["x"], dv["W_g"], dv["logit_bias"], 2)
+    disp = lib.moe_dispatch(idx, gw, gkey, 8, 1.0)
+    stats = lib.moe_routing_stats(logits, idx)
+    torch.cuda.synchronize()
+    for t in (y, y32, yec, ysh):
+        assert t.shape == (0, 64)
+    assert logits.shape == (0, 8) and idx.shape == (0, 2)
+    assert disp["perm"].numel() >= 0 and stats.shape == (18,)
 
 
 def test_identical_tokens_tie_break(lib):
