@@ -52,6 +52,7 @@ class HipEvents:
                                                 ctypes.c_void_p]
         self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.made = []
 
     def create(self):
@@ -67,6 +68,10 @@ class HipEvents:
         if self.rt.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
             raise RuntimeError("hipEventElapsedTime failed")
         return float(out.value)
+
+    def record(self, h, stream):
+        if self.rt.hipEventRecord(ctypes.c_void_p(h), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def close(self):
         for h in self.made:
@@ -121,12 +126,21 @@ def cpu_baseline(w, inp, sample):
         pass
     if not threads:
         threads = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     what = (f"all {w.T} tokens" if len(toks) == w.T else
             f"{len(toks)} evenly spaced tokens (routing and capacity still over all {w.T})")
     return {
         "value": reps * len(toks) / dt,
         "unit": "tokens/s",
         "cores": int(threads),
+        "cpu_model": model,
         "kind": "oracle",
         "sample": f"fp64 numpy oracle, one layer forward over {what}, {reps} pass(es); "
                   f"{dt:.1f} s wall",
@@ -307,20 +321,28 @@ def main():
     dslot = 3 if dom == "expert_gemm1" else 4  # event slots before / after that GEMM
 
     marks = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    # one more event per step, before its router (slot 0), and one after the
+    # last step: step i lasts from its mark to the next one
+    starts = [ev.create() for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         slots = [None] * 7
+        slots[0] = starts[i]
         slots[dslot], slots[dslot + 1] = marks[i]
         moe.moe_set_profile_events(slots)
         step()
+    moe.moe_set_profile_events([])
+    ev.record(starts[-1], torch.cuda.current_stream(dev).cuda_stream)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
-    moe.moe_set_profile_events([])
     ms_step = (t_end - t_start) * 1e3 / args.steps
     dom_ms = sum(ev.ms(a, b) for a, b in marks) / args.steps
+    step_ms = sorted(ev.ms(starts[i], starts[i + 1]) for i in range(args.steps))
+    step_med = (step_ms[(args.steps - 1) // 2] + step_ms[args.steps // 2]) / 2
     ev.close()
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step; {dom} {dom_ms * 1e3:.1f}us (events in the "
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (GPU events: median {step_med:.3f}, "
+        f"min {step_ms[0]:.3f}); {dom} {dom_ms * 1e3:.1f}us (events in the "
         f"timed steps); stage breakdown (untimed pass with stage events): "
         + ", ".join(f"{n} {v * 1e3:.1f}us" for n, v in per.items()))
 
@@ -385,6 +407,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "step_ms_gpu": {"median": step_med, "min": step_ms[0], "max": step_ms[-1],
+                        "note": "per timed step, HIP events before each step's router"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -399,7 +423,9 @@ def main():
                   "alg_gbps": layer_bytes / (ms_step * 1e-3) / 1e9,
                   "frac_hbm_peak": layer_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                   "flop_per_byte": intensity, "S": S, "dropped_pairs": dropped,
-                  "touched_experts": touched},
+                  "drop_rate": dropped / max(1, w.T * w.k), "touched_experts": touched,
+                  "kept_per_expert": [int(c) for c in counts.tolist()],
+                  "requests_per_expert": [int(c) for c in ex["req_counts"].cpu().tolist()]},
         "kernels_us": {n: v * 1e3 for n, v in per.items()},
         "kernels_us_note": "stage times from an untimed pass with an event between stages",
         "extras": extras,
