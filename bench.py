@@ -252,8 +252,8 @@ def measure_extras(moe, torch, w, dv, ws, y, flags):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--flags", default=None, help="'split' for the bf16 hi+lo hidden layer, 'plain' for bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
