@@ -389,6 +389,108 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
   }
 }
 
+// ---------------------------------------------------------------- 16-lane groups, DPP
+// All-reduce within each 16-lane row of a wave with DPP register moves (no
+// LDS crossbar): xor 1 and xor 2 inside quads, then the half-row mirror pairs
+// the two quads of each 8-lane half, the row mirror the two halves. Every
+// lane of the row ends with the reduction of all 16 (any pairing pattern is
+// valid for an associative, commutative combine).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_i32<CTRL>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = (unsigned)dpp_i32<CTRL>((int)(unsigned)b);
+  const unsigned hi = (unsigned)dpp_i32<CTRL>((int)(unsigned)(b >> 32));
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& bn) {
+  const float ov = dpp_f32<CTRL>(bv);
+  const int on = dpp_i32<CTRL>(bn);
+  if (ov > bv || (ov == bv && on < bn)) {
+    bv = ov;
+    bn = on;
+  }
+}
+
+// Top-k of one logits row per 16-lane group (4 rows per wave), 64 < N <= 16*SL:
+// lane c of the group holds experts c, c+16, ..., the reductions are the DPP
+// row all-reduces above. Picks, their order and the gates are those of
+// topk_row (largest logit first, equal logits to the lower expert; gates from
+// the picks' probabilities summed in pick order); only the fp64 softmax sum is
+// added in another order. `active` gates loads and stores; every lane of the
+// wave takes part in the reductions.
+template <int SL>
+__device__ __forceinline__ void topk_row16x(const float* __restrict__ Lrow, bool active, int N,
+                                            int k, int t, int32_t* __restrict__ idx,
+                                            float* __restrict__ w, double* __restrict__ key) {
+  const int c = lane_id() & 15;
+  float v[SL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    const int n = c + 16 * i;
+    v[i] = (active && n < N) ? Lrow[n] : -INFINITY;
+    m = fmaxf(m, v[i]);
+  }
+  m = fmaxf(m, dpp_f32<kDppXor1>(m));
+  m = fmaxf(m, dpp_f32<kDppXor2>(m));
+  m = fmaxf(m, dpp_f32<kDppHalfMirror>(m));
+  m = fmaxf(m, dpp_f32<kDppMirror>(m));
+  const double md = (double)m;
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < SL; ++i)
+    if (c + 16 * i < N) s += exp((double)v[i] - md);
+  s += dpp_f64<kDppXor1>(s);
+  s += dpp_f64<kDppXor2>(s);
+  s += dpp_f64<kDppHalfMirror>(s);
+  s += dpp_f64<kDppMirror>(s);
+  const double lse = md + log(s);
+  unsigned taken = 0u;
+  float my_v = 0.f;
+  int my_n = 0;
+  double my_p = 0.0, psum = 0.0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bn = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      const int n = c + 16 * i;
+      if (n < N && !((taken >> i) & 1u) && (v[i] > bv || bn == 0x7fffffff)) {
+        bv = v[i];
+        bn = n;
+      }
+    }
+    argmax_step<kDppXor1>(bv, bn);
+    argmax_step<kDppXor2>(bv, bn);
+    argmax_step<kDppHalfMirror>(bv, bn);
+    argmax_step<kDppMirror>(bv, bn);
+    if (bn < N && (bn & 15) == c) taken |= 1u << (bn >> 4);  // (rows past T keep no pick)
+    const double pj = exp((double)bv - md);
+    psum += pj;
+    if (c == j) {
+      my_v = bv;
+      my_n = bn;
+      my_p = pj;
+    }
+  }
+  if (active && c < k) {
+    idx[(size_t)t * k + c] = my_n;
+    w[(size_t)t * k + c] = (float)(my_p / psum);
+    key[(size_t)t * k + c] = (double)my_v - lse;
+  }
+}
+
 // ---------------------------------------------------------------- top-k over logits rows
 // One wave per token; the logits are already in global memory.
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int N, int k,
@@ -397,6 +499,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
   topk_row(logits + (size_t)t * N, N, k, t, nullptr, idx, w, key);
+}
+
+// 64 < N <= 16*SL: a 16-lane group per row, 16 rows per block.
+template <int SL>
+__global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ logits, int T, int N,
+                                                     int k, int32_t* __restrict__ idx,
+                                                     float* __restrict__ w, double* __restrict__ key) {
+  const int t = blockIdx.x * 16 + threadIdx.x / 16;
+  const bool active = t < T;
+  topk_row16x<SL>(logits + (size_t)(active ? t : 0) * N, active, N, k, t, idx, w, key);
 }
 
 // ---------------------------------------------------------------- bf16
@@ -678,8 +790,15 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
                        dim3(256), lds, st, (const bf16*)x, nullptr, nullptr, 1, WgT,
                        (const void*)bias, nullptr, nullptr, nullptr, d, NP, (void*)logits, nullptr,
                        T, N, nullptr);
-    hipLaunchKernelGGL(topk_kernel, dim3(cdiv(T, 4)), dim3(256), 0, st, logits, T, N, k, idx, w,
-                       key);
+    if (N <= 128)
+      hipLaunchKernelGGL(topk16_kernel<8>, dim3(cdiv(T, 16)), dim3(256), 0, st, logits, T, N, k,
+                         idx, w, key);
+    else if (N <= 256)
+      hipLaunchKernelGGL(topk16_kernel<16>, dim3(cdiv(T, 16)), dim3(256), 0, st, logits, T, N, k,
+                         idx, w, key);
+    else
+      hipLaunchKernelGGL(topk_kernel, dim3(cdiv(T, 4)), dim3(256), 0, st, logits, T, N, k, idx, w,
+                         key);
     return hipGetLastError();
   }
   // d not a multiple of 32: LDS-transposing kernel with fused top-k

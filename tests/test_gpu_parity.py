@@ -48,6 +48,9 @@ CASES = [
     ("router_N13", 256, 64, 64, 13, 3, 1.0, "bf16", False, "normal0.5", 0),
     # N*d too large to stage W_g^T in LDS: the transposed-copy router path
     ("router_transposed_N64", 256, 768, 64, 64, 2, 1.0, "bf16", False, "normal0.5", 0),
+    # 64 < N <= 256: top-k rows in 16-lane groups (8 and 16 experts per lane)
+    ("router_N100_groups", 300, 64, 64, 100, 4, 1.0, "bf16", False, "zipf1.1", 0),
+    ("router_N256_groups", 333, 128, 64, 256, 8, 1.25, "bf16", False, "zipf1.1", 0),
     # the documented maxima: N = 1024 experts with k = 16 (the widest top-k
     # rows), d = 65536 (router and first GEMM over the longest K), d_ff = 65536
     ("max_N_k", 256, 64, 64, 1024, 16, 1.0, "bf16", False, "normal0.5", 0),
