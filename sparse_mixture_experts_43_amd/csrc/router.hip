@@ -114,12 +114,44 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, 
   else topk_row_s<kMaxN / kWave>(Lrow, N, k, t, logits, idx, w, key);
 }
 
-// N <= 16: the same as topk_row with one 16-lane group per token row (lane c
-// of the group holds expert c), so a wave serves 4 rows. The reductions are
-// the xor butterflies of topk_row restricted to the 16 lanes that can hold an
-// expert (the other lanes there only add zeros / lose every comparison), so
-// the results are identical. Every lane of the wave takes part in the
-// shuffles; `active` only gates the stores.
+// ---------------------------------------------------------------- 16-lane groups, DPP
+// All-reduce within each 16-lane row of a wave with DPP register moves (no
+// LDS crossbar): xor 1 and xor 2 inside quads, then the half-row mirror pairs
+// the two quads of each 8-lane half, the row mirror the two halves. Every
+// lane of the row ends with the reduction of all 16 (any pairing pattern is
+// valid for an associative, commutative combine).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_i32<CTRL>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = (unsigned)dpp_i32<CTRL>((int)(unsigned)b);
+  const unsigned hi = (unsigned)dpp_i32<CTRL>((int)(unsigned)(b >> 32));
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& bn) {
+  const float ov = dpp_f32<CTRL>(bv);
+  const int on = dpp_i32<CTRL>(bn);
+  if (ov > bv || (ov == bv && on < bn)) {
+    bv = ov;
+    bn = on;
+  }
+}
+
+// N <= 16: topk_row with one 16-lane group per token row (lane c of the group
+// holds expert c), so a wave serves 4 rows; the reductions are the DPP row
+// all-reduces above. Same picks and gates as topk_row; the fp64 softmax sum
+// is added in another order. Every lane of the wave takes part in the
+// reductions; `active` only gates the stores.
 __device__ __forceinline__ void topk_row16(const float* __restrict__ Lrow, bool active, int N,
                                            int k, int t, float* __restrict__ logits,
                                            int32_t* __restrict__ idx, float* __restrict__ w,
@@ -129,12 +161,16 @@ __device__ __forceinline__ void topk_row16(const float* __restrict__ Lrow, bool 
   const float v = has ? Lrow[c] : -INFINITY;
   if (active && has && logits != nullptr) logits[(size_t)t * N + c] = v;
   float m = v;
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+  m = fmaxf(m, dpp_f32<kDppXor1>(m));
+  m = fmaxf(m, dpp_f32<kDppXor2>(m));
+  m = fmaxf(m, dpp_f32<kDppHalfMirror>(m));
+  m = fmaxf(m, dpp_f32<kDppMirror>(m));
   const double md = (double)m;
   double s = has ? exp((double)v - md) : 0.0;
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
+  s += dpp_f64<kDppXor1>(s);
+  s += dpp_f64<kDppXor2>(s);
+  s += dpp_f64<kDppHalfMirror>(s);
+  s += dpp_f64<kDppMirror>(s);
   const double lse = md + log(s);
   bool taken = false;
   float my_v = 0.f;
@@ -144,15 +180,10 @@ __device__ __forceinline__ void topk_row16(const float* __restrict__ Lrow, bool 
     const bool cand = has && !taken;
     float bv = cand ? v : -INFINITY;
     int bn = cand ? c : 0x7fffffff;
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 16);
-      const int on = __shfl_xor(bn, o, 16);
-      if (ov > bv || (ov == bv && on < bn)) {
-        bv = ov;
-        bn = on;
-      }
-    }
+    argmax_step<kDppXor1>(bv, bn);
+    argmax_step<kDppXor2>(bv, bn);
+    argmax_step<kDppHalfMirror>(bv, bn);
+    argmax_step<kDppMirror>(bv, bn);
     if (bn == c) taken = true;
     const double pj = exp((double)bv - md);
     psum += pj;
@@ -386,39 +417,6 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
       const int t = t0 + r;
       if (t < T) topk_row(&Ls[r][0], N, k, t, logits, idx, w, key);
     }
-  }
-}
-
-// ---------------------------------------------------------------- 16-lane groups, DPP
-// All-reduce within each 16-lane row of a wave with DPP register moves (no
-// LDS crossbar): xor 1 and xor 2 inside quads, then the half-row mirror pairs
-// the two quads of each 8-lane half, the row mirror the two halves. Every
-// lane of the row ends with the reduction of all 16 (any pairing pattern is
-// valid for an associative, commutative combine).
-template <int CTRL>
-__device__ __forceinline__ int dpp_i32(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __builtin_bit_cast(float, dpp_i32<CTRL>(__builtin_bit_cast(int, v)));
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
-  const unsigned lo = (unsigned)dpp_i32<CTRL>((int)(unsigned)b);
-  const unsigned hi = (unsigned)dpp_i32<CTRL>((int)(unsigned)(b >> 32));
-  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
-}
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& bv, int& bn) {
-  const float ov = dpp_f32<CTRL>(bv);
-  const int on = dpp_i32<CTRL>(bn);
-  if (ov > bv || (ov == bv && on < bn)) {
-    bv = ov;
-    bn = on;
   }
 }
 
