@@ -26,94 +26,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// ---------------------------------------------------------------- phase 2
-// Row r of the block's logits tile (LDS, row stride ls_stride floats).
-// `logits` may be null (the row is already in global memory). S: 64-expert
-// slots per lane, S * 64 >= N (slots past N add nothing, so every S gives the
-// same bits; topk_row picks the smallest).
-template <int S>
-__device__ __forceinline__ void topk_row_s(const float* __restrict__ Lrow, int N, int k, int t,
-                                           float* __restrict__ logits, int32_t* __restrict__ idx,
-                                           float* __restrict__ w, double* __restrict__ key) {
-  static_assert(S >= 1 && S <= kMaxN / kWave, "slots");
-  const int l = lane_id();
-  float v[S];
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < S; ++i) {
-    const int n = l + kWave * i;
-    v[i] = (n < N) ? Lrow[n] : -INFINITY;
-    if (n < N) {
-      m = fmaxf(m, v[i]);
-      if (logits != nullptr) logits[(size_t)t * N + n] = v[i];
-    }
-  }
-  m = wave_max_f32(m);
-
-  // fp64 softmax denominator over all N experts.
-  double s = 0.0;
-  const double md = (double)m;
-#pragma unroll
-  for (int i = 0; i < S; ++i) {
-    const int n = l + kWave * i;
-    if (n < N) s += exp((double)v[i] - md);
-  }
-  s = wave_sum_f64(s);
-  const double lse = md + log(s);
-
-  // k rounds of argmax: larger value wins, equal values -> lower index. Lane j
-  // keeps pick j (value, expert, unnormalised probability); no local arrays,
-  // so nothing lands in scratch memory.
-  unsigned taken = 0u;
-  float my_v = 0.f;
-  int my_n = 0;
-  double my_p = 0.0, psum = 0.0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bn = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-      const int n = l + kWave * i;
-      if (n < N && !((taken >> i) & 1u) && (v[i] > bv || bn == 0x7fffffff)) {
-        bv = v[i];
-        bn = n;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = wave_shfl_xor(bv, o);
-      const int on = wave_shfl_xor(bn, o);
-      if (ov > bv || (ov == bv && on < bn)) {
-        bv = ov;
-        bn = on;
-      }
-    }
-    if ((bn & (kWave - 1)) == l) taken |= 1u << (bn / kWave);
-    const double pj = exp((double)bv - md);
-    psum += pj;
-    if (l == j) {
-      my_v = bv;
-      my_n = bn;
-      my_p = pj;
-    }
-  }
-  if (l < k) {
-    idx[(size_t)t * k + l] = my_n;
-    w[(size_t)t * k + l] = (float)(my_p / psum);
-    key[(size_t)t * k + l] = (double)my_v - lse;
-  }
-}
-
-__device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, int k, int t,
-                                         float* __restrict__ logits, int32_t* __restrict__ idx,
-                                         float* __restrict__ w, double* __restrict__ key) {
-  if (N <= 64) topk_row_s<1>(Lrow, N, k, t, logits, idx, w, key);
-  else if (N <= 128) topk_row_s<2>(Lrow, N, k, t, logits, idx, w, key);
-  else if (N <= 256) topk_row_s<4>(Lrow, N, k, t, logits, idx, w, key);
-  else if (N <= 512) topk_row_s<8>(Lrow, N, k, t, logits, idx, w, key);
-  else topk_row_s<kMaxN / kWave>(Lrow, N, k, t, logits, idx, w, key);
-}
-
 // ---------------------------------------------------------------- 16-lane groups, DPP
 // All-reduce within each 16-lane row of a wave with DPP register moves (no
 // LDS crossbar): xor 1 and xor 2 inside quads, then the half-row mirror pairs
@@ -145,6 +57,133 @@ __device__ __forceinline__ void argmax_step(float& bv, int& bn) {
     bv = ov;
     bn = on;
   }
+}
+
+// Wave-wide versions: the row all-reduce, then the four rows' results (lanes
+// 0, 16, 32, 48) read as scalars and combined in a fixed order; every lane
+// gets the same value.
+__device__ __forceinline__ float wave_max_dpp(float m) {
+  m = fmaxf(m, dpp_f32<kDppXor1>(m));
+  m = fmaxf(m, dpp_f32<kDppXor2>(m));
+  m = fmaxf(m, dpp_f32<kDppHalfMirror>(m));
+  m = fmaxf(m, dpp_f32<kDppMirror>(m));
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), lane);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_sum_dpp(double s) {
+  s += dpp_f64<kDppXor1>(s);
+  s += dpp_f64<kDppXor2>(s);
+  s += dpp_f64<kDppHalfMirror>(s);
+  s += dpp_f64<kDppMirror>(s);
+  return (readlane_f64(s, 0) + readlane_f64(s, 16)) + (readlane_f64(s, 32) + readlane_f64(s, 48));
+}
+__device__ __forceinline__ void wave_argmax_dpp(float& bv, int& bn) {
+  argmax_step<kDppXor1>(bv, bn);
+  argmax_step<kDppXor2>(bv, bn);
+  argmax_step<kDppHalfMirror>(bv, bn);
+  argmax_step<kDppMirror>(bv, bn);
+  float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 0));
+  int n = __builtin_amdgcn_readlane(bn, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) {
+    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), r));
+    const int on = __builtin_amdgcn_readlane(bn, r);
+    if (ov > v || (ov == v && on < n)) {
+      v = ov;
+      n = on;
+    }
+  }
+  bv = v;
+  bn = n;
+}
+
+// ---------------------------------------------------------------- phase 2
+// Row r of the block's logits tile (LDS, row stride ls_stride floats).
+// `logits` may be null (the row is already in global memory). S: 64-expert
+// slots per lane, S * 64 >= N (slots past N add nothing, so every S gives the
+// same bits; topk_row picks the smallest).
+template <int S>
+__device__ __forceinline__ void topk_row_s(const float* __restrict__ Lrow, int N, int k, int t,
+                                           float* __restrict__ logits, int32_t* __restrict__ idx,
+                                           float* __restrict__ w, double* __restrict__ key) {
+  static_assert(S >= 1 && S <= kMaxN / kWave, "slots");
+  const int l = lane_id();
+  float v[S];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int n = l + kWave * i;
+    v[i] = (n < N) ? Lrow[n] : -INFINITY;
+    if (n < N) {
+      m = fmaxf(m, v[i]);
+      if (logits != nullptr) logits[(size_t)t * N + n] = v[i];
+    }
+  }
+  m = wave_max_dpp(m);
+
+  // fp64 softmax denominator over all N experts.
+  double s = 0.0;
+  const double md = (double)m;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int n = l + kWave * i;
+    if (n < N) s += exp((double)v[i] - md);
+  }
+  s = wave_sum_dpp(s);
+  const double lse = md + log(s);
+
+  // k rounds of argmax: larger value wins, equal values -> lower index. Lane j
+  // keeps pick j (value, expert, unnormalised probability); no local arrays,
+  // so nothing lands in scratch memory.
+  unsigned taken = 0u;
+  float my_v = 0.f;
+  int my_n = 0;
+  double my_p = 0.0, psum = 0.0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bn = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const int n = l + kWave * i;
+      if (n < N && !((taken >> i) & 1u) && (v[i] > bv || bn == 0x7fffffff)) {
+        bv = v[i];
+        bn = n;
+      }
+    }
+    wave_argmax_dpp(bv, bn);
+    if ((bn & (kWave - 1)) == l) taken |= 1u << (bn / kWave);
+    const double pj = exp((double)bv - md);
+    psum += pj;
+    if (l == j) {
+      my_v = bv;
+      my_n = bn;
+      my_p = pj;
+    }
+  }
+  if (l < k) {
+    idx[(size_t)t * k + l] = my_n;
+    w[(size_t)t * k + l] = (float)(my_p / psum);
+    key[(size_t)t * k + l] = (double)my_v - lse;
+  }
+}
+
+__device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, int k, int t,
+                                         float* __restrict__ logits, int32_t* __restrict__ idx,
+                                         float* __restrict__ w, double* __restrict__ key) {
+  if (N <= 64) topk_row_s<1>(Lrow, N, k, t, logits, idx, w, key);
+  else if (N <= 128) topk_row_s<2>(Lrow, N, k, t, logits, idx, w, key);
+  else if (N <= 256) topk_row_s<4>(Lrow, N, k, t, logits, idx, w, key);
+  else if (N <= 512) topk_row_s<8>(Lrow, N, k, t, logits, idx, w, key);
+  else topk_row_s<kMaxN / kWave>(Lrow, N, k, t, logits, idx, w, key);
 }
 
 // N <= 16: topk_row with one 16-lane group per token row (lane c of the group
@@ -205,7 +244,7 @@ __device__ __forceinline__ void topk_row16(const float* __restrict__ Lrow, bool 
 // Language Models with Sparse Activation", "Expert Choice Routing"): pair
 // t*N + e gets expert e, weight p[t,e] (the softmax probability itself) and the
 // fp64 rank key L[t,e] - lse_t, computed as in topk_row (wave max, per-lane
-// sums of exp over the lane's experts, xor butterfly). One wave per token.
+// sums of exp over the lane's experts, DPP wave sum). One wave per token.
 template <int S>
 __device__ __forceinline__ void ec_route_row(const float* __restrict__ row, int t, int N,
                                              int32_t* __restrict__ idx, float* __restrict__ w,
@@ -219,7 +258,7 @@ __device__ __forceinline__ void ec_route_row(const float* __restrict__ row, int 
     v[i] = (n < N) ? row[n] : -INFINITY;
     if (n < N) m = fmaxf(m, v[i]);
   }
-  m = wave_max_f32(m);
+  m = wave_max_dpp(m);
   const double md = (double)m;
   double s = 0.0;
 #pragma unroll
@@ -227,7 +266,7 @@ __device__ __forceinline__ void ec_route_row(const float* __restrict__ row, int 
     const int n = l + kWave * i;
     if (n < N) s += exp((double)v[i] - md);
   }
-  s = wave_sum_f64(s);
+  s = wave_sum_dpp(s);
   const double lse = md + log(s);
 #pragma unroll
   for (int i = 0; i < S; ++i) {
