@@ -301,18 +301,36 @@ __global__ __launch_bounds__(256) void ec_route_kernel(const float* __restrict__
 // layout the MFMA B operand wants: 8 consecutive k of one expert per lane.
 __global__ __launch_bounds__(256) void transpose_wg_kernel(const bf16* __restrict__ Wg, int d, int N,
                                                            int NP, bf16* __restrict__ WgT) {
-  __shared__ bf16 tile[64][66];
+  // 64 x 64 tile through LDS; 16-byte loads (8 experts of one k) when N % 8 ==
+  // 0, 16-byte stores (8 k of one expert; d % 8 == 0)
+  __shared__ bf16 tile[64][72];  // [k][n]
   const int k0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int kk = i / 64, nn = i % 64;
-    const int kg = k0 + kk, ng = n0 + nn;
-    tile[kk][nn] = (kg < d && ng < N) ? Wg[(size_t)kg * N + ng] : (bf16)0.0f;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int kk = tid / 8 + 32 * q, nc = (tid % 8) * 8;
+    const int kg = k0 + kk, ng = n0 + nc;
+    bf16x8 v;
+    if (kg < d && ng + 8 <= N && (N % 8) == 0) {
+      v = *(const bf16x8*)(Wg + (size_t)kg * N + ng);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = (kg < d && ng + u < N) ? Wg[(size_t)kg * N + ng + u] : (bf16)0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) tile[kk][nc + u] = v[u];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int nn = i / 64, kk = i % 64;
-    const int kg = k0 + kk, ng = n0 + nn;
-    if (kg < d && ng < NP) WgT[(size_t)ng * d + kg] = tile[kk][nn];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int nn = tid / 8 + 32 * q, kc = (tid % 8) * 8;
+    const int ng = n0 + nn, kg = k0 + kc;
+    if (ng >= NP || kg >= d) continue;
+    bf16x8 v;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = tile[kc + u][nn];
+    *(bf16x8*)(WgT + (size_t)ng * d + kg) = v;
   }
 }
 
