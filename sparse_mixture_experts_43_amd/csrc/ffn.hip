@@ -46,9 +46,17 @@ namespace {
 // cost depends on where the experts' ragged last m-tiles fall. Group r has
 // c_r = #{nt < NT : nt % 8 == r} bands per expert, i.e. total_mt * c_r tiles,
 // so entry p decodes in closed form.
+// expert_major (bit 0: first GEMM, bit 1: second): the list is instead expert
+// by expert, each expert's m-tiles in order with all their n-tiles, so an XCD's
+// eighth holds whole experts and the token rows of an m-tile are fetched into
+// one L2 for all its n-tiles. Chosen for the 128x128 tiles of capacity-limited
+// layers (first GEMM always, second when no expert spans two m-tiles: with
+// skewed routing and several m-tiles per expert, contiguous experts load the
+// XCDs unevenly).
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ off, int N,
                                                         int BM, int NT1, int NT2, int max1,
-                                                        int max2, int4* __restrict__ tiles1,
+                                                        int max2, int expert_major,
+                                                        int4* __restrict__ tiles1,
                                                         int4* __restrict__ tiles2,
                                                         int32_t* __restrict__ counts) {
   __shared__ int mtoff[kMaxN + 1];
@@ -94,6 +102,19 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
     int4* tl = pass == 0 ? tiles1 : tiles2;
     const int total = min(total_mt * NTn, mx);
     for (int p = threadIdx.x; p < total; p += 1024) {
+      if ((expert_major >> pass) & 1) {
+        int lo = 0, hi = N - 1;  // expert: largest e with mtoff[e] * NTn <= p
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (mtoff[mid] * NTn <= p) lo = mid; else hi = mid - 1;
+        }
+        const int e = lo;
+        const int local = p - mtoff[e] * NTn;
+        const int mt = local / NTn, nt = local - mt * NTn;
+        const int cnt_e = off[e + 1] - off[e];
+        tl[p] = make_int4(e, off[e] + mt * BM, min(BM, cnt_e - mt * BM), nt);
+        continue;
+      }
       // residue group r of entry p (groups are never empty where p lands)
       int r = 0, base = 0, c = 0;
       for (; r < 8; ++r) {
@@ -736,8 +757,9 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
     return launch_decode<false>(x, perm, off, gate, W1, b1, W2, b2, d, d_ff, N, k, pl, S_max,
                                 s.hidden, nullptr, s.part, slot_out, st, defer);
   }
+  const int em = pl.path == kPathTiledM ? (1 | ((C < T ? C : T) <= pl.BM ? 2 : 0)) : 0;
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, off, N, pl.BM,
-                     cdiv(d_ff, pl.BN1), cdiv(d, pl.BN2), pl.max1, pl.max2, t1, t2, s.counts);
+                     cdiv(d_ff, pl.BN1), cdiv(d, pl.BN2), pl.max1, pl.max2, em, t1, t2, s.counts);
   if (pl.path == kPathF32) {
     profile_mark(3, st);
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(pl.max1 > 0 ? pl.max1 : 1), dim3(256), 0, st,
