@@ -227,6 +227,21 @@ def measure_extras(moe, torch, w, dv, ws, y, flags):
     torch.cuda.synchronize()
     ss_ms = (time.perf_counter() - ts0) * 1e3 / nx
     sh_tflops = 4.0 * w.T * w.d * w.d_ff / (sh_ms * 1e-3) / 1e12  # algorithmic flops
+    # the same step captured once in a HIP graph and replayed (the library
+    # enqueues kernels only, so the forward is capturable as it is)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"],
+                        dv["b2"], w.k, w.capacity_factor, workspace=ws, y=y, flags=flags)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    tg0 = time.perf_counter()
+    for _ in range(nx):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - tg0) * 1e3 / nx
+    del g
     C = moe.moe_capacity(w.T, w.N, w.k, w.capacity_factor)
     extras = {"routing_stats_us": stats_us, "aux_balance": float(st_h[2 * w.N]),
               "z_mean_lse_sq": float(st_h[2 * w.N + 1]),
@@ -236,16 +251,19 @@ def measure_extras(moe, torch, w, dv, ws, y, flags):
               "shared_expert_ms": sh_ms,
               "shared_expert_tflops": sh_tflops,
               "with_shared_expert_ms_per_step": ss_ms,
+              "graph_replay_ms_per_step": graph_ms,
               "note": "after the timed steps; moe_routing_stats averaged over 20 calls, the layer "
                       "with first-come capacity + survivor renormalisation + identity fallback "
                       "over 20 steps, with expert-choice routing (every expert takes "
                       "min(C, T) tokens) over 20 steps, a shared expert of width d_ff on every "
                       "token alone (HIP events, 20 calls; TFLOP/s = 4 T d d_ff / time) and "
-                      "added to the layer (20 steps)"}
+                      "added to the layer (20 steps), and the plain step captured in a HIP "
+                      "graph and replayed (20 replays)"}
     log(f"extras: routing stats {stats_us:.1f}us, aux {extras['aux_balance']:.4f}, "
         f"all drop policies {pol_ms:.3f} ms/step, expert choice {ec_ms:.3f} ms/step "
         f"({extras['expert_choice_slots']} slots), shared expert {sh_ms:.3f} ms "
-        f"({sh_tflops:.0f} TFLOP/s), layer + shared expert {ss_ms:.3f} ms/step")
+        f"({sh_tflops:.0f} TFLOP/s), layer + shared expert {ss_ms:.3f} ms/step, "
+        f"graph replay {graph_ms:.3f} ms/step")
     return extras
 
 

@@ -1,0 +1,68 @@
+"""The layer forward captured in a HIP graph (torch.cuda.CUDAGraph): the C ABI
+enqueues kernels only (no allocation, memset, copy or host read-back), so a
+caller can capture moe_forward with its workspace and output and replay it.
+
+Bar: every replay, with eager forwards and synchronisations between the
+replays, equals the eager forward bit for bit (deterministic kernels)."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from moe_inputs import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, T, d, d_ff, N, k, cf, dtype, bias, skew, flag names
+    ("switch_like_drops", 1024, 128, 256, 16, 1, 1.0, "bf16", False, "normal0.5", ("HIDDEN_SPLIT",)),
+    ("decode_splitk", 24, 512, 4096, 4, 2, 0.0, "bf16", True, "none", ()),
+    ("prefill_tiles", 2048, 256, 512, 2, 1, 0.0, "bf16", False, "none", ()),
+    ("expert_choice", 256, 64, 64, 16, 2, 0.5, "bf16", False, "zipf1.1",
+     ("EXPERT_CHOICE", "IDENTITY_FALLBACK")),
+    ("f32_policies", 300, 64, 96, 6, 2, 0.5, "f32", True, "none",
+     ("FIRST_COME", "RENORM_SURVIVORS")),
+]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_mixture_experts_43_amd as m
+    return m
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_forward_replays_in_graph(lib, case):
+    from gpu_util import say, to_dev
+    name, T, d, d_ff, N, k, cf, dt, bias, skew, fnames = case
+    flags = lib.MOE_FLAG_Y_F32
+    for f in fnames:
+        flags |= getattr(lib, "MOE_FLAG_" + f)
+    w = Workload(name, T=T, d=d, d_ff=d_ff, N=N, k=k, capacity_factor=cf, dtype=dt,
+                 ffn_bias=bias, skew=skew, seed=2)
+    say(f"[case] graph {name} flags={flags}")
+    dv = to_dev(make_inputs(w))
+    args = (dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"], dv["b2"], k, cf)
+    x_dtype = dv["x"].dtype
+    ws = lib.alloc_workspace(lib.moe_workspace_bytes(T, d, d_ff, N, k, cf, x_dtype), "cuda")
+    y_ref = lib.moe_forward(*args, flags=flags)  # eager (also the first call on these shapes)
+    y = torch.empty_like(y_ref)
+    lib.moe_forward(*args, workspace=ws, y=y, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.moe_forward(*args, workspace=ws, y=y, flags=flags)
+    for rep in range(4):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep} differs from the eager forward"
+        # eager work between replays (its own workspace and output)
+        y_e = lib.moe_forward(*args, flags=flags)
+        torch.cuda.synchronize()
+        assert torch.equal(y_e, y_ref)
+    say(f"[ok] graph {name}: 4 replays equal the eager forward")
