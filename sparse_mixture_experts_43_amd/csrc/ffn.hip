@@ -59,6 +59,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
                                                         int4* __restrict__ tiles1,
                                                         int4* __restrict__ tiles2,
                                                         int32_t* __restrict__ counts) {
+  // counts[4 .. 19]: the two GEMMs' per-XCD work-queue counters, zeroed here
+  if (threadIdx.x < 16) counts[4 + threadIdx.x] = 0;
   __shared__ int mtoff[kMaxN + 1];
   __shared__ int tmp[17];
   __shared__ int carry;
@@ -583,7 +585,8 @@ size_t ring_part_floats(int BM, int BN, bool alo, int max_tiles) {
 template <int BM, int BN, int WM, int WN, bool G1, bool SPLIT>
 void launch_gemm(const bf16* A, const bf16* A_lo, const int32_t* perm, int k, const bf16* W,
                  const bf16* bias, const float* gate, const int4* tl, const int32_t* cnt, int K,
-                 int Nout, int grid, void* out, bf16* out_lo, float* part, hipStream_t st) {
+                 int Nout, int grid, void* out, bf16* out_lo, float* part, hipStream_t st,
+                 int* wq = nullptr) {
   constexpr int NTH = (BM / WM) * (BN / WN) * kWave;
   constexpr bool ALO = SPLIT && !G1;
   if (K % kRK == 0) {
@@ -598,8 +601,8 @@ void launch_gemm(const bf16* A, const bf16* A_lo, const int32_t* perm, int k, co
     pgrid = pgrid < bound ? pgrid : bound;
     hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, R, EARLY>), dim3(pgrid),
                        dim3(NTH), lds, st, A, A_lo, perm, k, W, (const void*)bias, gate, tl, cnt, K,
-                       Nout, out, out_lo, 0, 0, part);
-    if (part != nullptr) {
+                       Nout, out, out_lo, 0, 0, wq != nullptr ? nullptr : part, wq);
+    if (part != nullptr && wq == nullptr) {
       // at most per-1 tail tiles per XCD, BM*BN/4/256 group blocks each
       const int work = 8 * (pgrid / 8) * (BM * BN / 4 / kReduceThreads);
       hipLaunchKernelGGL((ring_reduce_kernel<BM, BN, WM, WN, MODE, SPLIT>),
@@ -621,14 +624,21 @@ hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, c
                         const int32_t* cnts, void* slot_out, float* part, hipStream_t st) {
   const int g1 = cdiv(pl.max1 > 0 ? pl.max1 : 1, 8) * 8;
   const int g2 = cdiv(pl.max2 > 0 ? pl.max2 : 1, 8) * 8;
+  // Prefill tiles with many rounds (the first GEMM at the Mixtral shape: about 8
+  // rounds of 128-stage tiles) take them from per-XCD work queues (counters
+  // zeroed by the schedule kernel): -6% there. With few rounds of long tiles
+  // (its second GEMM: about 2 rounds of 448 stages) the static shares and their
+  // split tail are better (+9% with the queue), so they stay.
+  int* wq1 = (BM == 256 && pl.max1 >= 4 * 256) ? (int*)cnts + 4 : nullptr;
+  int* wq2 = (BM == 256 && pl.max2 >= 4 * 256) ? (int*)cnts + 12 : nullptr;
   profile_mark(3, st);
   launch_gemm<BM, BN, WM, WN, true, SPLIT>((const bf16*)x, nullptr, perm, k, (const bf16*)W1,
                                            (const bf16*)b1, nullptr, t1, cnts + 0, d, d_ff, g1,
-                                           hid, hid_lo, part, st);
+                                           hid, hid_lo, part, st, wq1);
   profile_mark(4, st);
   launch_gemm<BM, BN, WM, WN, false, SPLIT>((const bf16*)hid, hid_lo, nullptr, k,
                                             (const bf16*)W2, (const bf16*)b2, gate, t2, cnts + 1,
-                                            d_ff, d, g2, slot_out, nullptr, part, st);
+                                            d_ff, d, g2, slot_out, nullptr, part, st, wq2);
   profile_mark(5, st);
   return hipGetLastError();
 }
@@ -725,7 +735,7 @@ void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max
   s->hidden = c.take<unsigned char>(rows * d_ff * es);
   s->hidden_lo = pl.split ? (void*)c.take<bf16>(rows * d_ff) : nullptr;
   s->tiles = (int32_t*)c.take<int4>((size_t)(pl.max1 > 0 ? pl.max1 : 1) + (pl.max2 > 0 ? pl.max2 : 1));
-  s->counts = c.take<int32_t>(4);
+  s->counts = c.take<int32_t>(20);
   // decode: split-K partials; tiled bf16 on the ring: split-tail partial tiles
   size_t pn = 0;
   if (pl.path == kPathDecode) {

@@ -255,7 +255,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
     int kpairs, const bf16* __restrict__ W, const void* __restrict__ bias,
     const float* __restrict__ gate, const int4* __restrict__ tiles,
     const int32_t* __restrict__ ntiles_p, int K, int Nout, void* __restrict__ out,
-    bf16* __restrict__ out_lo, int M_total, int ldo, float* __restrict__ part) {
+    bf16* __restrict__ out_lo, int M_total, int ldo, float* __restrict__ part,
+    int* __restrict__ wq) {
   constexpr bool G1 = MODE == kEpiGelu;
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int NTH = NW * kWave;
@@ -286,7 +287,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   const int nk = K / kRK;
   const int xcd = blockIdx.x & 7;
   const int jw = blockIdx.x >> 3;
-  const RingSplit sp(ntiles, xcd, gridDim.x, part != nullptr);
+  // wq (not null): a work queue per XCD (8 counters, zero at launch); each
+  // workgroup claims its next tile of the XCD's share with one integer atomic,
+  // so the share's tiles finish roughly in list order and co-scheduled tiles
+  // stay close in K (their shared rows meet in L2). No split tail then.
+  const bool dyn = wq != nullptr;
+  const RingSplit sp(ntiles, xcd, gridDim.x, part != nullptr && !dyn);
   int n_whole = sp.rounds;  // whole tiles jw + r*per that exist
   if (n_whole > 0 && jw + (n_whole - 1) * sp.per >= sp.cx) n_whole -= 1;
   int t_lo = 0, t_hi = 0;
@@ -300,8 +306,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
     }
   }
   const int n_items = n_whole + n_seg;
-  if (n_items == 0) return;
+  if (n_items == 0 && !dyn) return;
   const int base_tile = xcd * sp.chunk;
+  __shared__ int sh_claim;
+  // no copy is in flight where this is called (the barriers wait for them)
+  auto claim = [&]() -> int {
+    __syncthreads();
+    if (threadIdx.x == 0) sh_claim = atomicAdd(wq + xcd, 1);
+    __syncthreads();
+    const int c = sh_claim;
+    return c < sp.cx ? c : -1;
+  };
   // item it -> tile, stage range [kb, ke), partial slot (-1: whole tile)
   auto item = [&](int it, int& tile, int& kb, int& ke, int& ps) {
     if (it < n_whole) {
@@ -502,7 +517,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   };
 
   int tile, ke, ps, e, m0, mcount, n0;
-  item(0, tile, kb, ke, ps);
+  if (dyn) {
+    const int c = claim();
+    if (c < 0) return;
+    tile = base_tile + c;
+    kb = 0;
+    ke = nk;
+    ps = -1;
+  } else {
+    item(0, tile, kb, ke, ps);
+  }
   nks = ke - kb;
   ring_decode_tile<MODE, BM, BN>(tile, tiles, M_total, Nout, e, m0, mcount, n0);
   set_ptrs(e, m0, mcount, n0);
@@ -549,10 +573,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
 
     // ---- next item: request its first stages before this item's epilogue
     const int ce = e, cm0 = m0, cmcount = mcount, cn0 = n0, cps = ps;
-    ++it;
-    const bool more = it < n_items;
+    bool more;
+    if (dyn) {
+      const int c = claim();
+      more = c >= 0;
+      if (more) {
+        tile = base_tile + c;
+        kb = 0;
+        ke = nk;
+        ps = -1;
+      }
+    } else {
+      ++it;
+      more = it < n_items;
+      if (more) item(it, tile, kb, ke, ps);
+    }
     if (more) {
-      item(it, tile, kb, ke, ps);
       nks = ke - kb;
       ring_decode_tile<MODE, BM, BN>(tile, tiles, M_total, Nout, e, m0, mcount, n0);
       set_ptrs(e, m0, mcount, n0);

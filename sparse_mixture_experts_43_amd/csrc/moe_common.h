@@ -121,7 +121,8 @@ struct FfnScratch {
   void* hidden;       // [S_max, d_ff] activation dtype
   void* hidden_lo;    // [S_max, d_ff] bf16 residual of the hidden layer (split mode) or null
   int32_t* tiles;     // GEMM tile tables (int4 entries) for both GEMMs
-  int32_t* counts;    // [4] tile counts written by the schedule kernel
+  int32_t* counts;    // [20]: tile counts written by the schedule kernel, then the
+                      // GEMMs' per-XCD work-queue counters (zeroed by it)
   float* part;        // split-K partial sums of the decode GEMMs, or null
 };
 constexpr int kFlagHiddenSplit = 1;  // MOE_FLAG_HIDDEN_SPLIT

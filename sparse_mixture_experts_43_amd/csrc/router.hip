@@ -844,7 +844,7 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
     hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false, kRing>), dim3(grid),
                        dim3(256), lds, st, (const bf16*)x, nullptr, nullptr, 1, WgT,
                        (const void*)bias, nullptr, nullptr, nullptr, d, NP, (void*)logits, nullptr,
-                       T, N, nullptr);
+                       T, N, nullptr, nullptr);
     if (N <= 128)
       hipLaunchKernelGGL(topk16_kernel<8>, dim3(cdiv(T, 16)), dim3(256), 0, st, logits, T, N, k,
                          idx, w, key);

@@ -115,6 +115,15 @@ def test_empty_batch(lib, dt):
     assert disp["perm"].numel() >= 0 and stats.shape == (18,)
 
 
+def test_parity_prefill_work_queue(lib):
+    """Enough 256x256 tiles in the first GEMM (at least four per resident
+    workgroup) for the per-XCD work queue; checked on sampled tokens."""
+    from gpu_util import run_and_compare
+    w = Workload("prefill_queue", T=4096, d=256, d_ff=16384, N=2, k=2, capacity_factor=0.0,
+                 dtype="bf16", ffn_bias=True, skew="none", seed=0)
+    run_and_compare(w, lib, sample_tokens=32)
+
+
 def test_identical_tokens_tie_break(lib):
     """Every token identical: equal keys at the cut keep the lowest tokens."""
     from gpu_util import run_and_compare
