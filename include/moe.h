@@ -54,8 +54,9 @@
  *    clamped to [1, T] (capacity formula in "Communication cost in distributed
  *    settings" of the wiki page; the small guard absorbs the representation
  *    error of cf). cf <= 0 means no limit (C = T).
- *  - Results are deterministic: no floating-point atomics anywhere, so equal
- *    inputs give bit-identical outputs from run to run.
+ *  - Results are deterministic: no floating-point atomics anywhere (integer
+ *    atomics only count and hand out tiles, which does not change any value
+ *    computed), so equal inputs give bit-identical outputs from run to run.
  *  - Thread safety: concurrent calls are safe when they use distinct
  *    workspaces and outputs. Calls that share a workspace must be ordered on
  *    one stream.
