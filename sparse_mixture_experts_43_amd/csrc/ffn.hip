@@ -624,12 +624,13 @@ hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, c
                         const int32_t* cnts, void* slot_out, float* part, hipStream_t st) {
   const int g1 = cdiv(pl.max1 > 0 ? pl.max1 : 1, 8) * 8;
   const int g2 = cdiv(pl.max2 > 0 ? pl.max2 : 1, 8) * 8;
-  // Prefill tiles with many rounds (the first GEMM at the Mixtral shape: about 8
-  // rounds of 128-stage tiles) take them from per-XCD work queues (counters
-  // zeroed by the schedule kernel): -6% there. With few rounds of long tiles
-  // (its second GEMM: about 2 rounds of 448 stages) the static shares and their
-  // split tail are better (+9% with the queue), so they stay.
-  int* wq1 = (BM == 256 && pl.max1 >= 4 * 256) ? (int*)cnts + 4 : nullptr;
+  // A first GEMM with many tiles (at least four per CU: about 8 rounds at the
+  // Mixtral shape, 2-4 rounds of 128x128 tiles in the capacity-limited layers)
+  // takes them from per-XCD work queues (counters zeroed by the schedule
+  // kernel): Mixtral-shaped -4%, fine-grained -7%. With few rounds of long
+  // tiles (the Mixtral-shaped second GEMM: about 2 rounds of 448 stages) the
+  // static shares and their split tail are better (+9% with the queue).
+  int* wq1 = pl.max1 >= 4 * 256 ? (int*)cnts + 4 : nullptr;
   int* wq2 = (BM == 256 && pl.max2 >= 4 * 256) ? (int*)cnts + 12 : nullptr;
   profile_mark(3, st);
   launch_gemm<BM, BN, WM, WN, true, SPLIT>((const bf16*)x, nullptr, perm, k, (const bf16*)W1,
