@@ -624,14 +624,14 @@ hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, c
                         const int32_t* cnts, void* slot_out, float* part, hipStream_t st) {
   const int g1 = cdiv(pl.max1 > 0 ? pl.max1 : 1, 8) * 8;
   const int g2 = cdiv(pl.max2 > 0 ? pl.max2 : 1, 8) * 8;
-  // A first GEMM with many tiles (at least four per CU: about 8 rounds at the
-  // Mixtral shape, 2-4 rounds of 128x128 tiles in the capacity-limited layers)
-  // takes them from per-XCD work queues (counters zeroed by the schedule
-  // kernel): Mixtral-shaped -4%, fine-grained -7%. With few rounds of long
-  // tiles (the Mixtral-shaped second GEMM: about 2 rounds of 448 stages) the
-  // static shares and their split tail are better (+9% with the queue).
+  // A GEMM with many tiles (at least four per CU: the Mixtral-shaped first
+  // GEMM's 8 rounds, the capacity-limited layers' 128x128 tiles) takes them from
+  // per-XCD work queues (counters zeroed by the schedule kernel): Mixtral-shaped
+  // first GEMM -4%, fine-grained first -7% and second -9%. With few rounds of
+  // long tiles (the Mixtral-shaped second GEMM: about 2 rounds of 448 stages)
+  // the static shares and their split tail are better (+9% with the queue).
   int* wq1 = pl.max1 >= 4 * 256 ? (int*)cnts + 4 : nullptr;
-  int* wq2 = (BM == 256 && pl.max2 >= 4 * 256) ? (int*)cnts + 12 : nullptr;
+  int* wq2 = pl.max2 >= 4 * 256 ? (int*)cnts + 12 : nullptr;
   profile_mark(3, st);
   launch_gemm<BM, BN, WM, WN, true, SPLIT>((const bf16*)x, nullptr, perm, k, (const bf16*)W1,
                                            (const bf16*)b1, nullptr, t1, cnts + 0, d, d_ff, g1,

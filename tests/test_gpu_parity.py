@@ -125,12 +125,12 @@ def test_parity_prefill_work_queue(lib):
 
 
 def test_parity_tiled128_work_queue(lib):
-    """Capacity-limited layer whose 128x128 first GEMM has enough tiles for the
-    per-XCD work queue; checked on sampled tokens."""
+    """Capacity-limited layer whose 128x128 GEMMs both have enough tiles for
+    the per-XCD work queues (with the split hidden layer); sampled tokens."""
     from gpu_util import run_and_compare
-    w = Workload("tiled128_queue", T=4096, d=128, d_ff=4096, N=16, k=2, capacity_factor=1.0,
+    w = Workload("tiled128_queue", T=4096, d=2048, d_ff=4096, N=16, k=2, capacity_factor=1.0,
                  dtype="bf16", ffn_bias=True, skew="normal0.5", seed=0)
-    run_and_compare(w, lib, sample_tokens=32)
+    run_and_compare(w, lib, sample_tokens=32, flags=1)
 
 
 def test_identical_tokens_tie_break(lib):
