@@ -49,10 +49,10 @@ namespace {
 // expert_major (bit 0: first GEMM, bit 1: second): the list is instead expert
 // by expert, each expert's m-tiles in order with all their n-tiles, so an XCD's
 // eighth holds whole experts and the token rows of an m-tile are fetched into
-// one L2 for all its n-tiles. Chosen for the 128x128 tiles of capacity-limited
-// layers (first GEMM always, second when no expert spans two m-tiles: with
-// skewed routing and several m-tiles per expert, contiguous experts load the
-// XCDs unevenly).
+// one L2 for all its n-tiles. Used for the 128x128 tiles of capacity-limited
+// layers: the first GEMM when experts span several m-tiles, the second when
+// each expert fits one m-tile (measured; with skewed routing and several
+// m-tiles per expert, contiguous experts load the second GEMM's XCDs unevenly).
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ off, int N,
                                                         int BM, int NT1, int NT2, int max1,
                                                         int max2, int expert_major,
@@ -768,7 +768,11 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
     return launch_decode<false>(x, perm, off, gate, W1, b1, W2, b2, d, d_ff, N, k, pl, S_max,
                                 s.hidden, nullptr, s.part, slot_out, st, defer);
   }
-  const int em = pl.path == kPathTiledM ? (1 | ((C < T ? C : T) <= pl.BM ? 2 : 0)) : 0;
+  // tile order of the 128x128 GEMMs (measured with the work queues): experts of
+  // one m-tile (capacity <= 128) take band-residue order for the first GEMM and
+  // expert-major for the second, experts of several m-tiles the reverse
+  const bool single_mt = (C < T ? C : T) <= pl.BM;
+  const int em = pl.path == kPathTiledM ? (single_mt ? 2 : 1) : 0;
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, off, N, pl.BM,
                      cdiv(d_ff, pl.BN1), cdiv(d, pl.BN2), pl.max1, pl.max2, em, t1, t2, s.counts);
   if (pl.path == kPathF32) {
