@@ -38,21 +38,8 @@ __device__ __forceinline__ unsigned long long lanemask_lt() {
 }
 
 // Lanes of this wave whose `v` equals mine (only among `valid` lanes), for
-// values below 2^BITS.
-template <int BITS>
-__device__ __forceinline__ unsigned long long match_peers(int v, bool valid) {
-  unsigned long long peers = __ballot(valid);
-#pragma unroll
-  for (int b = 0; b < BITS; ++b) {
-    const bool bit = (v >> b) & 1;
-    const unsigned long long m = __ballot(bit);
-    peers &= bit ? m : ~m;
-  }
-  return peers;
-}
-
-// The same for values below 2^nbits, nbits <= 10 uniform across the wave:
-// expert ids need only ceil(log2 N) bits.
+// values below 2^nbits, nbits <= 10 uniform across the wave: expert ids need
+// only ceil(log2 N) bits.
 __device__ __forceinline__ unsigned long long match_peers_n(int v, bool valid, int nbits) {
   unsigned long long peers = __ballot(valid);
   for (int b = 0; b < nbits; ++b) {
@@ -224,6 +211,11 @@ __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
     } else {
       bucket[s] = p;
       codes[s] = rank_code(key, p, fc_k);
+      // a pair of an expert over capacity starts dropped; the selection
+      // writes only the kept ones
+      const int e = idx[p];
+      const int r = (e + 1 < N ? sh_reqoff[e + 1] : carry[0]) - sh_reqoff[e];
+      if (r > C) inv[p] = -1;
     }
   }
 }
@@ -304,6 +296,7 @@ __global__ __launch_bounds__(256) void bucket_kernel(
     const int32_t* __restrict__ idx, const double* __restrict__ key, int fc_k, int P, int N,
     int ntiles,
     const int32_t* __restrict__ tbase, const int32_t* __restrict__ reqoff,
+    const int32_t* __restrict__ req, int C,
     int32_t* __restrict__ bucket, unsigned long long* __restrict__ codes,
     int32_t* __restrict__ inv) {
   extern __shared__ int bsm[];  // [4][N]
@@ -320,8 +313,12 @@ __global__ __launch_bounds__(256) void bucket_kernel(
     bucket[pos] = p;
     codes[pos] = rank_code(key, p, fc_k);
   });
-  for (int p = p0 + l; p < p1; p += kWave)
-    if ((unsigned)idx[p] >= (unsigned)N) inv[p] = -1;
+  // invalid pairs, and every pair of an expert over capacity (the selection
+  // then writes only its kept ones): coalesced here, scattered there
+  for (int p = p0 + l; p < p1; p += kWave) {
+    const int e = idx[p];
+    if ((unsigned)e >= (unsigned)N || req[e] > C) inv[p] = -1;
+  }
 }
 
 // ------------------------------------------------------------ select + scatter
@@ -331,33 +328,14 @@ __global__ __launch_bounds__(256) void bucket_kernel(
 // the highest bit in which the expert's keys differ are common (block min/max);
 // 256-bin passes on 8-bit digits from there down each pick the bin holding
 // the C-th largest key, and once the remaining candidates fit in a short LDS
-// list they are compacted into it, so the later passes scan only them. The
-// pairs with key above U and the first (lowest-token) ones equal to U are
-// kept, in token order. Up to kSelLds keys are held in LDS.
+// list they are compacted into it, so the later passes scan only them; the
+// passes stop early once the picked bin holds exactly the keys still wanted.
+// The pairs with key above U and the first (lowest-token) ones equal to U are
+// kept, in token order. The dispatch kernels before it have already marked
+// every pair of an over-capacity expert dropped (inv = -1), so only the kept
+// pairs are written here. Up to kSelLds keys are held in LDS.
 constexpr int kSelLds = 16384;
 constexpr int kSelList = 1024;  // compacted candidates
-
-// Wave-aggregated histogram add: lanes with the same digit add once. The
-// distinct digits of the wave are peeled off one at a time (the high digits of
-// one expert's keys take few values); after 4 rounds the remaining lanes group
-// by bit-wise ballots.
-template <int BITS>
-__device__ __forceinline__ void hist_add(int* hist, int dig, bool cand) {
-  unsigned long long rem = __ballot(cand);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (rem == 0ull) return;
-    const int lead = __builtin_amdgcn_readfirstlane(__ffsll((long long)rem) - 1);
-    const int d0 = __shfl(dig, lead, kWave);
-    const unsigned long long same = __ballot(cand && dig == d0) & rem;
-    if (lane_id() == lead) atomicAdd(&hist[d0], __popcll(same));
-    rem &= ~same;
-  }
-  if (rem == 0ull) return;
-  const bool mine = (rem >> lane_id()) & 1ull;
-  const unsigned long long peers = match_peers<BITS>(dig, mine);
-  if (mine && __popcll(peers & lanemask_lt()) == 0) atomicAdd(&hist[dig], __popcll(peers));
-}
 
 // Threshold digit of a histogram of `bins` (<= 2048) bins: the digit whose
 // suffix count (from the top) first reaches `want`; run by one wave.
@@ -491,7 +469,7 @@ __device__ __forceinline__ void select_body(
         for (int r = 0; r < 4; ++r) {
           if (rem == 0ull) break;
           const int lead = __builtin_amdgcn_readfirstlane(__ffsll((long long)rem) - 1);
-          const int d0 = __shfl(dig, lead, kWave);
+          const int d0 = __builtin_amdgcn_readlane(dig, lead);
           const unsigned long long same = __ballot(cand && dig == d0) & rem;
           if (l == lead) hw[d0] += __popcll(same);
           rem &= ~same;
@@ -512,7 +490,9 @@ __device__ __forceinline__ void select_body(
       pmask |= dmask << sh;
       want = sh_want;
       const int m_next = hist[sh_dig];
-      if (sh == 0) break;
+      // every candidate left in the bin is kept: the bin's lowest code, the
+      // prefix with zeros below, already splits kept from dropped
+      if (sh == 0 || m_next == want) break;
       s_hi = sh - 1;
       if (!compact && m_next <= kSelList) {
         // the remaining candidates fit in the list: compact them once
@@ -577,7 +557,6 @@ __device__ __forceinline__ void select_body(
       const bool keep = in && (u > U || (u == U && r + __popcll(eqm & lt) < want));
       const unsigned long long km = __ballot(keep);
       if (keep) write_slot(perm, inv, gate, w, p, ks + __popcll(km & lt));
-      else if (in) inv[p] = -1;
       ks += __popcll(km);
       r += __popcll(eqm);
     }
@@ -669,7 +648,7 @@ hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key
     hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, st, req, N, P, C, cnt,
                        s.reqoff, off, n_dropped);
     hipLaunchKernelGGL(bucket_kernel, dim3(nblk), dim3(256), lds, st, idx, key, fc_k, P, N,
-                       ntiles, s.tilebase, s.reqoff, s.bucket, s.codes, inv);
+                       ntiles, s.tilebase, s.reqoff, req, C, s.bucket, s.codes, inv);
   }
   if (can_drop || !fused)
   {
