@@ -835,13 +835,15 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
     return hipGetLastError();
   }
   if (d % kRK == 0) {
-    // many experts: logits as a plain GEMM on the LDS-DMA ring, then top-k rows
+    // many experts: logits as a plain GEMM on the LDS-DMA ring (each step issues
+    // a whole stage: one 4-wave block per CU has little else to overlap), then
+    // top-k rows
     constexpr int BM = 128, BN = 128;
     const size_t lds = (size_t)kRing * (BM + BN) * kRowB;
-    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false, kRing>), lds);
-    const int grid = ring_grid((const void*)gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false, kRing>,
+    MOE_SET_LDS_ONCE((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false, kRing, true>), lds);
+    const int grid = ring_grid((const void*)gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false, kRing, true>,
                                256, lds, cdiv(T, BM) * cdiv(NP, BN));
-    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false, kRing>), dim3(grid),
+    hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, 64, 64, kEpiLogit, false, kRing, true>), dim3(grid),
                        dim3(256), lds, st, (const bf16*)x, nullptr, nullptr, 1, WgT,
                        (const void*)bias, nullptr, nullptr, nullptr, d, NP, (void*)logits, nullptr,
                        T, N, nullptr, nullptr);
