@@ -8,6 +8,8 @@ rule) and check that at least one pin fails for it.
 Pins used (none of them re-types the oracle's own formula):
   * the worked example of the "Mixture-of-Experts" wiki page (N=4, k=2, T=5,
     C=2): drop set, final dispatch and the partial combine of x2 and x4;
+  * the router with the per-expert logit bias as a torch nn.Linear(d, N)
+    (weight W_g^T, bias the logit bias) in float64;
   * the capacity formula of the same page at the five workloads' numbers;
   * textbook values of the exact GELU, z * Phi(z);
   * the top-k-on-logits-then-softmax router of the "Scaling Language Models
@@ -117,6 +119,34 @@ def pin_gelu_textbook():
     phi = np.array([0.5, 0.8413447460685429, 0.15865525393145707, 0.9772498680518208,
                     0.0013498980316300933, 0.6914624612740131])
     np.testing.assert_allclose(M.gelu(z), z * phi, rtol=1e-14, atol=1e-300)
+
+
+def pin_router_logits_linear():
+    # Router step of the wiki page (logits = x W_g) with the workloads' per-
+    # expert logit bias, stated as the pages' router module: a torch
+    # nn.Linear(d, N) whose weight is W_g^T and whose bias is the logit bias,
+    # evaluated in float64. A zero bias must give x W_g exactly as a Linear
+    # without bias does.
+    rng = np.random.default_rng(17)
+    for (T, d, N) in ((7, 5, 4), (33, 16, 9), (64, 8, 64)):
+        x = torch.from_numpy(rng.standard_normal((T, d)))
+        W_g = torch.from_numpy(rng.standard_normal((d, N)) * 0.3)
+        b = torch.from_numpy(rng.standard_normal(N) * 0.7)
+        lin = torch.nn.Linear(d, N, bias=True, dtype=torch.float64)
+        lin0 = torch.nn.Linear(d, N, bias=False, dtype=torch.float64)
+        with torch.no_grad():
+            lin.weight.copy_(W_g.T)
+            lin.bias.copy_(b)
+            lin0.weight.copy_(W_g.T)
+            ref = lin(x).numpy()
+            ref0 = lin0(x).numpy()
+        np.testing.assert_allclose(M.router_logits(x, W_g, b), ref, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(M.router_logits(x, W_g, None), ref0, rtol=1e-13, atol=1e-13)
+        # through the layer: the bias moves the top-1 choice to the favoured expert
+        big = torch.full((N,), -50.0, dtype=torch.float64)
+        big[N - 1] = 50.0
+        r = M.route_topk(M.router_logits(x, W_g, big), 1)
+        assert np.all(r.idx[:, 0] == N - 1)
 
 
 def pin_topk_then_softmax_router():
@@ -465,8 +495,8 @@ def pin_shared_expert():
     np.testing.assert_allclose(res_t["y"], ref[[0, 4, 8]], rtol=1e-12, atol=1e-13)
 
 
-PINS = [pin_worked_example, pin_capacity_formula, pin_gelu_textbook, pin_topk_then_softmax_router,
-        pin_topk_ties_lower_expert, pin_k1_gates_exactly_one, pin_dense_mixture_k_equals_n,
+PINS = [pin_worked_example, pin_router_logits_linear, pin_capacity_formula, pin_gelu_textbook,
+        pin_topk_then_softmax_router, pin_topk_ties_lower_expert, pin_k1_gates_exactly_one, pin_dense_mixture_k_equals_n,
         pin_single_expert_is_mlp, pin_brute_force, pin_linear_experts_closed_form,
         pin_dispatch_invariants, pin_capacity_ties_lower_token, pin_routing_stats_uniform,
         pin_routing_stats_collapse, pin_routing_stats_code_form, pin_first_come_worked_example,
@@ -480,10 +510,18 @@ def test_pin(pin):
 
 
 # ------------------------------------------------------------- mutants ----
-_orig = {n: getattr(M, n) for n in ("gelu", "route_topk", "capacity", "capacity_dispatch",
+_orig = {n: getattr(M, n) for n in ("router_logits", "gelu", "route_topk", "capacity", "capacity_dispatch",
                                     "expert_ffn_rows", "combine", "routing_stats",
                                     "renormalise_survivors", "expert_choice_dispatch",
                                     "shared_expert_out")}
+
+
+def _mut_logit_bias_ignored(x, W_g, logit_bias=None):
+    return _orig["router_logits"](x, W_g, None)
+
+
+def _mut_logit_bias_negated(x, W_g, logit_bias=None):
+    return _orig["router_logits"](x, W_g, None if logit_bias is None else -M.to_f64(logit_bias))
 
 
 def _mut_gelu_tanh(z):
@@ -640,6 +678,8 @@ def _mut_shared_no_b2(x, shared, tokens=None):
 
 
 MUTANTS = {
+    "logit_bias_ignored": ("router_logits", _mut_logit_bias_ignored),
+    "logit_bias_negated": ("router_logits", _mut_logit_bias_negated),
     "gelu_tanh_approx": ("gelu", _mut_gelu_tanh),
     "no_renormalisation": ("route_topk", _mut_no_renorm),
     "ties_to_higher_expert": ("route_topk", _mut_ties_high),
