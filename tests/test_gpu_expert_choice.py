@@ -3,8 +3,9 @@ against the CPU oracle fed the GPU's fp32 logits.
 
 Bars: the oracle's expert-choice dispatch from the GPU logits reproduces the
 GPU's per-expert counts (all equal to min(C, T)) and inverse map bit for bit;
-every output element within the arithmetic error bound of tests/gpu_util.py
-(pairs t*N + e, gate p[t,e]); the activation-dtype output is the fp32 output
+every output element of every token within the arithmetic error bound of
+tests/gpu_util.py (pairs t*N + e, gate p[t,e]) and within 2e-2 x RMS(y) (bf16)
+or 1e-4 x RMS(y) (fp32); the activation-dtype output is the fp32 output
 rounded once; tokens no expert took are 0, or their input row with the
 identity fallback; repeated runs are bit-identical.
 """
@@ -38,7 +39,7 @@ def lib():
     return m
 
 
-def run_ec(w: Workload, lib, identity=False, sample_tokens=None, extra_flags=0):
+def run_ec(w: Workload, lib, identity=False, extra_flags=0, strict=True):
     from gpu_util import EPS32, U_BF16, output_error_bound, say, to_dev
     say(f"[case] expert choice {w.name} T={w.T} d={w.d} d_ff={w.d_ff} N={w.N} k={w.k} "
         f"cf={w.capacity_factor} dtype={w.dtype} identity={identity}")
@@ -66,14 +67,11 @@ def run_ec(w: Workload, lib, identity=False, sample_tokens=None, extra_flags=0):
     assert np.array_equal(ex["req_counts"].cpu().numpy(), od.req_counts)
     assert int(ex["n_dropped"].item()) == od.n_dropped
     assert np.array_equal(ex["inv"].cpu().numpy()[:T * N], od.inv), "inverse map differs"
-    toks = np.arange(T) if sample_tokens is None else np.unique(
-        np.linspace(0, T - 1, min(sample_tokens, T)).astype(np.int64))
-    pairs = (toks[:, None] * N + np.arange(N)[None, :]).reshape(-1)
-    sl = od.inv[pairs]
-    sl = sl[sl >= 0]
-    O = M.expert_slots_out(inp["x"], od, N, inp["W1"], inp["b1"], inp["W2"], inp["b2"], slots=sl)
-    y_ref = M.combine(O, od, T, N, w.d, tokens=toks, x_fallback=inp["x"] if identity else None)
-    y_gpu = y32.cpu().double().numpy()[toks]
+    toks = np.arange(T)
+    O = M.expert_slots_out(inp["x"], od, N, inp["W1"], inp["b1"], inp["W2"], inp["b2"])
+    y_ref = M.combine(O, od, T, N, w.d, x_fallback=inp["x"] if identity else None)
+    del O
+    y_gpu = y32.cpu().double().numpy()
     diff = np.abs(y_gpu - y_ref)
     u_h = EPS32 if w.dtype == "f32" else U_BF16
     split = bool(extra_flags & lib.MOE_FLAG_HIDDEN_SPLIT)
@@ -89,8 +87,10 @@ def run_ec(w: Workload, lib, identity=False, sample_tokens=None, extra_flags=0):
         else:
             assert torch.count_nonzero(y32[sel]) == 0
     rms = float(np.sqrt(np.mean(y_ref ** 2)))
-    say(f"[ok] {w.name} C={C} S={od.S} untaken={int(untaken.sum())} "
-        f"max|dy|/rms={float(np.max(diff)) / rms if rms else 0.0:.2e}")
+    ratio = float(np.max(diff)) / rms if rms else 0.0
+    if strict:
+        assert ratio <= (1e-4 if w.dtype == "f32" else 2e-2), ratio
+    say(f"[ok] {w.name} C={C} S={od.S} untaken={int(untaken.sum())} max|dy|/rms={ratio:.2e}")
     return {"C": C, "S": od.S, "untaken": int(untaken.sum())}
 
 
@@ -107,5 +107,4 @@ def test_expert_choice(lib, case, identity):
 
 @pytest.mark.slow
 def test_expert_choice_fine_grained_full(lib):
-    run_ec(WORKLOADS["fine_grained"], lib, sample_tokens=24,
-           extra_flags=lib.MOE_FLAG_HIDDEN_SPLIT)
+    run_ec(WORKLOADS["fine_grained"], lib, extra_flags=lib.MOE_FLAG_HIDDEN_SPLIT)

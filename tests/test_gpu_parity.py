@@ -1,16 +1,16 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Small and medium cases get a full element-by-element comparison; the five
-full-size workloads run in the launch configuration the benchmark times and
-are checked on every routing decision and on sampled output rows.
+Every case, the five full-size workloads included (in the launch
+configuration the benchmark times), is compared element by element on every
+token: every logit, every routing decision, every output element.
 Bars:
   * logits within 1e-5 relative (max |dL| / max(|L|, rms L));
   * top-k indices, request/kept counts, offsets, permutation, inverse map and
     drop set bit-exact against the oracle fed the GPU's fp32 logits;
   * every output element within the a-priori error bound of the path's
     arithmetic (tests/gpu_util.py, output_error_bound);
-  * for the named workloads, max |dy| <= 2e-2 x RMS(y) (bf16) or
-    1e-4 x RMS(y) (fp32) on the fp32 output;
+  * max |dy| <= 2e-2 x RMS(y) (bf16) or 1e-4 x RMS(y) (fp32) on the fp32
+    output, for every case;
   * the activation-dtype output equals the fp32 output rounded once;
   * sub-calls compose to the forward's bits; repeated runs are bit-identical.
 """
@@ -117,20 +117,20 @@ def test_empty_batch(lib, dt):
 
 def test_parity_prefill_work_queue(lib):
     """Enough 256x256 tiles in the first GEMM (at least four per resident
-    workgroup) for the per-XCD work queue; checked on sampled tokens."""
+    workgroup) for the per-XCD work queue."""
     from gpu_util import run_and_compare
     w = Workload("prefill_queue", T=4096, d=256, d_ff=16384, N=2, k=2, capacity_factor=0.0,
                  dtype="bf16", ffn_bias=True, skew="none", seed=0)
-    run_and_compare(w, lib, sample_tokens=32)
+    run_and_compare(w, lib)
 
 
 def test_parity_tiled128_work_queue(lib):
     """Capacity-limited layer whose 128x128 GEMMs both have enough tiles for
-    the per-XCD work queues (with the split hidden layer); sampled tokens."""
+    the per-XCD work queues (with the split hidden layer)."""
     from gpu_util import run_and_compare
     w = Workload("tiled128_queue", T=4096, d=2048, d_ff=4096, N=16, k=2, capacity_factor=1.0,
                  dtype="bf16", ffn_bias=True, skew="normal0.5", seed=0)
-    run_and_compare(w, lib, sample_tokens=32, flags=1)
+    run_and_compare(w, lib, flags=1)
 
 
 def test_identical_tokens_tie_break(lib):
@@ -157,13 +157,28 @@ def test_few_distinct_tokens_select(lib):
     inp = make_inputs(w)
     rows = inp["x"][:3]
     inp["x"] = rows[torch.arange(w.T) % 3].contiguous()
-    res = run_and_compare(w, lib, inputs=inp, sample_tokens=64)
+    res = run_and_compare(w, lib, inputs=inp)
     assert res["n_dropped"] > 0
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", sorted(FULL))
 def test_parity_full_size(lib, name):
+    """Every token of the full-size workload, with the sub-call composition."""
     from gpu_util import run_and_compare
-    run_and_compare(WORKLOADS[name], lib, sample_tokens=24, flags=FULL[name], strict=True,
-                    check_compose=(name != "mixtral_prefill"))
+    run_and_compare(WORKLOADS[name], lib, flags=FULL[name])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["switch_top1", "fine_grained"])
+def test_plain_bf16_full_size(lib, name):
+    """The library's default (plain bf16 hidden layer) at the two capacity-
+    limited workloads: routing bit-exact and every output element within the
+    arithmetic error bound of that path. Not held to 2e-2 x RMS(y): with most
+    picks dropped, RMS(y) is small against the rows that keep a large gate, and
+    the hidden layer's bf16 rounding alone reaches that bar there (the measured
+    ratio is printed)."""
+    from gpu_util import run_and_compare, say
+    res = run_and_compare(WORKLOADS[name], lib, flags=0, strict=False, check_compose=False)
+    say(f"[plain-bf16] {name} max|dy|/rms(y) = {res['y_err_over_rms']:.4e} "
+        f"(bar {res['strict_tol']:.0e})")

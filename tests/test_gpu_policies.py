@@ -129,5 +129,4 @@ def test_identity_fallback_fully_dropped(lib):
 def test_drop_policies_full_size(lib, name):
     from gpu_util import run_and_compare
     flags = lib.MOE_FLAG_HIDDEN_SPLIT | _flags(lib, "all")
-    run_and_compare(WORKLOADS[name], lib, sample_tokens=24, flags=flags, strict=True,
-                    check_compose=False)
+    run_and_compare(WORKLOADS[name], lib, flags=flags)

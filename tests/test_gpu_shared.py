@@ -1,8 +1,9 @@
 """GPU parity of the shared expert (moe_shared_expert, and moe_forward /
 moe_combine with shared_out) against the CPU oracle.
 
-Bars: the shared expert's fp32 output within the arithmetic error bound of
-tests/gpu_util.py (one expert holding every token with weight 1); the layer
+Bars: the shared expert's fp32 output on every token within the arithmetic
+error bound of tests/gpu_util.py (one expert holding every token with weight
+1) and within 2e-2 x RMS (bf16) or 1e-4 x RMS (fp32); the layer
 with a shared expert is, bit for bit, the fp32 sum of the layer without it and
 the shared output, for token choice, the drop policies, the split-K decode
 combine and expert choice; the separately called combine with shared_out gives
@@ -75,7 +76,7 @@ def shared_bound(x, sh, toks, u_h, gelu_abs):
     return output_error_bound(inp, od, 1, toks, u_h, gelu_abs=gelu_abs)
 
 
-def check_shared_out(lib, w: Workload, d_fs: int, flags=0, sample_tokens=None):
+def check_shared_out(lib, w: Workload, d_fs: int, flags=0):
     from gpu_util import say, to_dev
     say(f"[case] shared expert {w.name} T={w.T} d={w.d} d_fs={d_fs} dtype={w.dtype} "
         f"bias={w.ffn_bias} flags={flags}")
@@ -88,8 +89,7 @@ def check_shared_out(lib, w: Workload, d_fs: int, flags=0, sample_tokens=None):
     torch.cuda.synchronize()
     assert torch.equal(out, again), "not deterministic"
     T = w.T
-    toks = np.arange(T) if sample_tokens is None else np.unique(
-        np.linspace(0, T - 1, min(sample_tokens, T)).astype(np.int64))
+    toks = np.arange(T)
     ref = M.shared_expert_out(inp["x"], _shared_tuple(sh), tokens=toks)
     got = out.cpu().double().numpy()[toks]
     split = bool(flags & lib.MOE_FLAG_HIDDEN_SPLIT)
@@ -98,6 +98,7 @@ def check_shared_out(lib, w: Workload, d_fs: int, flags=0, sample_tokens=None):
     diff = np.abs(got - ref)
     assert not (diff > bound).any(), float(np.max(diff / np.maximum(bound, 1e-300)))
     rms = float(np.sqrt(np.mean(ref ** 2)))
+    assert float(np.max(diff)) <= (1e-4 if w.dtype == "f32" else 2e-2) * rms
     say(f"[ok] shared {w.name} max|d|/rms={float(np.max(diff)) / rms:.2e} "
         f"max|d|/bound={float(np.max(diff / np.maximum(bound, 1e-300))):.2e}")
     return inp, sh, out
@@ -185,6 +186,8 @@ def test_layer_with_shared_expert(lib, case):
              + shared_bound(inp["x"], sh, toks, u_h, ga) + 2 * EPS32 * np.abs(ref["y"]))
     diff = np.abs(y32.cpu().double().numpy() - ref["y"])
     assert not (diff > bound).any(), float(np.max(diff / np.maximum(bound, 1e-300)))
+    rms = float(np.sqrt(np.mean(ref["y"] ** 2)))
+    assert float(np.max(diff)) <= (1e-4 if dt == "f32" else 2e-2) * rms
     say(f"[ok] {name} max|d|/bound={float(np.max(diff / np.maximum(bound, 1e-300))):.2e}")
 
 
@@ -192,4 +195,4 @@ def test_layer_with_shared_expert(lib, case):
 @pytest.mark.parametrize("name", ["mixtral_prefill", "decode"])
 def test_shared_expert_full_size(lib, name):
     w = WORKLOADS[name]
-    check_shared_out(lib, w, w.d_ff, sample_tokens=16)
+    check_shared_out(lib, w, w.d_ff)
