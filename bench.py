@@ -1,6 +1,6 @@
 """Benchmark of the sparse MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--configs all]
 
 A step is one moe_forward call (router, dispatch, both expert GEMMs, combine)
 on one batch of seeded synthetic inputs already resident in HBM. W untimed
@@ -9,7 +9,8 @@ per-stage breakdown, which also names the dominant expert GEMM), then exactly
 K timed steps between two device synchronisations, each carrying only the two
 events the library records around the dominant GEMM on its stream. Prints ONE
 JSON line (metric, value in tokens/s, roofline of the dominant kernel from
-those events, and the CPU oracle timed on a bounded sample on the host).
+those events, and the CPU oracle timed on a bounded sample on the host). The
+other workloads are then timed the same way and reported under "configs".
 Progress goes to stderr.
 """
 from __future__ import annotations
@@ -104,15 +105,15 @@ def load_traffic(workload, kernel):
     return None if m is None else float(m.group(1))
 
 
-def cpu_baseline(w, inp, sample):
+def cpu_baseline(w, inp, sample, budget_s=10.0):
     import numpy as np
     import oracle
 
     toks = np.unique(np.linspace(0, w.T - 1, min(sample, w.T)).astype(np.int64))
-    # repeat the same sample until about 10 s of host work (at most 8 passes)
+    # repeat the same sample until about budget_s of host work (at most 8 passes)
     reps = 0
     t0 = time.perf_counter()
-    while reps < 8 and (reps == 0 or time.perf_counter() - t0 < 10.0):
+    while reps < 8 and (reps == 0 or time.perf_counter() - t0 < budget_s):
         oracle.moe_forward(inp["x"], inp["W_g"], inp["logit_bias"], inp["W1"], inp["b1"], inp["W2"],
                            inp["b2"], w.k, w.capacity_factor, tokens=toks)
         reps += 1
@@ -267,36 +268,12 @@ def measure_extras(moe, torch, w, dv, ws, y, flags):
     return extras
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mixtral_prefill")
-    ap.add_argument("--flags", default=None, help="'split' for the bf16 hi+lo hidden layer, 'plain' for bf16")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true",
-                    help="skip the routing-statistics and drop-policy measurements after timing")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="after timing, run one plain device copy of this many MiB (the "
-                         "reference dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE)")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
-              "(expert parallelism is a design note only); use --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def run_workload(moe, torch, w, fl, steps, warmup, want_extras, cpu_budget_s, copy_probe_mib=0):
+    """Times one workload: W warm-up steps, an untimed pass with stage events,
+    then exactly K timed steps. Returns the workload's record (value, roofline
+    of the dominant expert GEMM, layer figures, CPU oracle baseline)."""
+    from moe_inputs import make_inputs
 
-    import torch
-
-    import sparse_mixture_experts_43_amd as moe
-    from moe_inputs import get_workload, make_inputs
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    w = get_workload(args.workload)
-    fl = args.flags or DEFAULT_FLAGS.get(w.name, "plain")
     flags = moe.MOE_FLAG_Y_F32 | (moe.MOE_FLAG_HIDDEN_SPLIT if fl == "split" else 0)
     log(f"workload {w.name}: T={w.T} d={w.d} d_ff={w.d_ff} N={w.N} k={w.k} cf={w.capacity_factor} "
         f"dtype={w.dtype} flags={fl}+y_f32")
@@ -313,17 +290,17 @@ def main():
         moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"], dv["W2"], dv["b2"],
                         w.k, w.capacity_factor, workspace=ws, y=y, flags=flags)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warm-up done ({args.warmup} steps)")
+    log(f"warm-up done ({warmup} steps)")
 
     names = ["router", "dispatch", "schedule", "expert_gemm1", "expert_gemm2", "combine"]
     ev = HipEvents()
     # Per-stage breakdown from an untimed pass: an event between every stage
     # adds a few microseconds per event, so the timed steps below carry only
     # the two events around the dominant expert GEMM.
-    nprof = max(3, min(args.steps, 10))
+    nprof = max(3, min(steps, 10))
     pmarks = [[ev.create() for _ in range(7)] for _ in range(nprof)]
     for i in range(nprof):
         moe.moe_set_profile_events(pmarks[i])
@@ -338,13 +315,13 @@ def main():
     dom = "expert_gemm1" if per["expert_gemm1"] >= per["expert_gemm2"] else "expert_gemm2"
     dslot = 3 if dom == "expert_gemm1" else 4  # event slots before / after that GEMM
 
-    marks = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    marks = [(ev.create(), ev.create()) for _ in range(steps)]
     # one more event per step, before its router (slot 0), and one after the
     # last step: step i lasts from its mark to the next one
-    starts = [ev.create() for _ in range(args.steps + 1)]
+    starts = [ev.create() for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         slots = [None] * 7
         slots[0] = starts[i]
         slots[dslot], slots[dslot + 1] = marks[i]
@@ -354,30 +331,28 @@ def main():
     ev.record(starts[-1], torch.cuda.current_stream(dev).cuda_stream)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
-    ms_step = (t_end - t_start) * 1e3 / args.steps
-    dom_ms = sum(ev.ms(a, b) for a, b in marks) / args.steps
-    step_ms = sorted(ev.ms(starts[i], starts[i + 1]) for i in range(args.steps))
-    step_med = (step_ms[(args.steps - 1) // 2] + step_ms[args.steps // 2]) / 2
+    ms_step = (t_end - t_start) * 1e3 / steps
+    dom_ms = sum(ev.ms(a, b) for a, b in marks) / steps
+    step_ms = sorted(ev.ms(starts[i], starts[i + 1]) for i in range(steps))
+    step_med = (step_ms[(steps - 1) // 2] + step_ms[steps // 2]) / 2
     ev.close()
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (GPU events: median {step_med:.3f}, "
+    log(f"timed {steps} steps: {ms_step:.3f} ms/step (GPU events: median {step_med:.3f}, "
         f"min {step_ms[0]:.3f}); {dom} {dom_ms * 1e3:.1f}us (events in the "
         f"timed steps); stage breakdown (untimed pass with stage events): "
         + ", ".join(f"{n} {v * 1e3:.1f}us" for n, v in per.items()))
 
     # extras, after the timed region: the routing statistics pass (from this
     # input's logits and top-k ids) and the layer with every drop-policy flag
-    extras = None
-    if not args.no_extras:
-        extras = measure_extras(moe, torch, w, dv, ws, y, flags)
+    extras = measure_extras(moe, torch, w, dv, ws, y, flags) if want_extras else None
 
-    if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib << 18  # fp32 elements
+    if copy_probe_mib > 0:
+        n = copy_probe_mib << 18  # fp32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
+        log(f"copy probe: {copy_probe_mib} MiB read + {copy_probe_mib} MiB written")
         del src, dst
 
     # routing statistics of the timed input (read back after timing)
@@ -416,30 +391,24 @@ def main():
                 "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "kernel": dom,
                 "launch_us": dom_ms * 1e3,
                 "per_launch": f"{kb:.4g} B (touched-expert weights + activations in/out)"}
-    tokens_per_s = w.T / (ms_step * 1e-3)
-    out = {
-        "metric": METRIC,
-        "value": tokens_per_s,
+    layer_tflops = layer_flops / (ms_step * 1e-3) / 1e12
+    layer_gbps = layer_bytes / (ms_step * 1e-3) / 1e9
+    rec = {
+        "value": w.T / (ms_step * 1e-3),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_step,
         "step_ms_gpu": {"median": step_med, "min": step_ms[0], "max": step_ms[-1],
                         "note": "per timed step, HIP events before each step's router"},
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16",
-        "data": "synthetic (seeded normal draws of the workload's shapes and distributions)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "N": w.N, "k": w.k,
                    "capacity_factor": w.capacity_factor, "hidden": fl, "y_dtype": "f32",
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "layer": {"tflops": layer_flops / (ms_step * 1e-3) / 1e12,
-                  "frac_bf16_peak": layer_flops / (ms_step * 1e-3) / 1e12 / peak_f,
-                  "alg_gbps": layer_bytes / (ms_step * 1e-3) / 1e9,
-                  "frac_hbm_peak": layer_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "layer": {"tflops": layer_tflops, "frac_bf16_peak": layer_tflops / peak_f,
+                  "alg_gbps": layer_gbps, "frac_hbm_peak": layer_gbps / PEAK_HBM_GBPS,
+                  "bound": bound,
+                  "frac_of_bound": (layer_tflops / peak_f if bound == "mfma"
+                                    else layer_gbps / PEAK_HBM_GBPS),
                   "flop_per_byte": intensity, "S": S, "dropped_pairs": dropped,
                   "drop_rate": dropped / max(1, w.T * w.k), "touched_experts": touched,
                   "kept_per_expert": [int(c) for c in counts.tolist()],
@@ -447,13 +416,96 @@ def main():
         "kernels_us": {n: v * 1e3 for n, v in per.items()},
         "kernels_us_note": "stage times from an untimed pass with an event between stages",
         "extras": extras,
-        "source_hash": source_hash(),
     }
-    if not args.no_cpu_baseline:
+    log(f"{w.name}: {ms_step:.3f} ms/step, {rec['value']:.4g} tokens/s, {dom} "
+        f"{roof['frac']:.3f} of {roof['bound']} peak; layer {rec['layer']['frac_of_bound']:.3f} "
+        f"of {bound} peak")
+    del dv, ws, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if cpu_budget_s > 0:
         log(f"timing the CPU oracle on a {CPU_SAMPLE.get(w.name, 32)}-token sample")
-        out["cpu_baseline"] = cpu_baseline(w, inp, CPU_SAMPLE.get(w.name, 32))
+        rec["cpu_baseline"] = cpu_baseline(w, inp, CPU_SAMPLE.get(w.name, 32), cpu_budget_s)
     else:
-        out["cpu_baseline"] = None
+        rec["cpu_baseline"] = None
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral_prefill",
+                    help="the headline workload (value, roofline, cpu_baseline of the line)")
+    ap.add_argument("--configs", default="all",
+                    help="other workloads timed after the headline, under 'configs': 'all' "
+                         "(every other workload), 'none', or a comma-separated list")
+    ap.add_argument("--flags", default=None,
+                    help="'split' for the bf16 hi+lo hidden layer, 'plain' for bf16 (headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the routing-statistics and drop-policy measurements after timing")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (the "
+                         "reference dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(expert parallelism is a design note only); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_mixture_experts_43_amd as moe
+    from moe_inputs import WORKLOADS, get_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = get_workload(args.workload)
+    fl = args.flags or DEFAULT_FLAGS.get(w.name, "plain")
+    head = run_workload(moe, torch, w, fl, args.steps, args.warmup, not args.no_extras,
+                        0 if args.no_cpu_baseline else 10.0, args.copy_probe_mib)
+    if args.configs == "all":
+        others = [n for n in WORKLOADS if n != w.name]
+    elif args.configs in ("", "none"):
+        others = []
+    else:
+        others = [n for n in args.configs.split(",") if n and n != w.name]
+    configs = {}
+    for name in others:
+        wo = get_workload(name)
+        configs[name] = run_workload(moe, torch, wo, DEFAULT_FLAGS.get(name, "plain"), args.steps,
+                                     args.warmup, False, 0 if args.no_cpu_baseline else 5.0)
+    out = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "step_ms_gpu": head["step_ms_gpu"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic (seeded normal draws of the workload's shapes and distributions)",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "layer": head["layer"],
+        "kernels_us": head["kernels_us"],
+        "kernels_us_note": head["kernels_us_note"],
+        "extras": head["extras"],
+        "source_hash": source_hash(),
+        "cpu_baseline": head["cpu_baseline"],
+        "configs": configs,
+        "configs_note": "each other workload timed the same way after the headline (same steps "
+                        "and warm-up; value, roofline of its dominant expert GEMM, the layer's "
+                        "fraction of its bound, CPU oracle on a bounded sample)",
+    }
     print(json.dumps(out), flush=True)
 
 
