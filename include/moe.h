@@ -222,7 +222,12 @@ int moe_dispatch(const int32_t* topk_idx, const float* topk_w, const double* top
  *        gate-scaled outputs stay fp32 so that only y is rounded once more).
  * flags: MOE_FLAG_HIDDEN_SPLIT is honoured (bf16); MOE_FLAG_Y_F32 has no
  * effect here. T, k, capacity_factor bound S (S <= min(T*k, N*C)) for launch
- * sizing. Needs workspace (the hidden activations live there). */
+ * sizing: perm, offsets and slot_gate must come from moe_dispatch called with
+ * the same T, N, k and capacity_factor. With other offsets the kernels clamp
+ * each expert's rows to C and all rows to min(T*k, N*C), so every access
+ * stays inside the buffers, but the rows past those bounds are not computed
+ * (their slot_out rows are left as they were). Needs workspace (the hidden
+ * activations live there). */
 int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
                    const float* slot_gate,
                    const void* W1, const void* b1, const void* W2, const void* b2,

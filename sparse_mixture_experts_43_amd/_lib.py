@@ -222,8 +222,10 @@ def moe_dispatch(topk_idx: torch.Tensor, topk_w: torch.Tensor, topk_key: Optiona
 
 
 def moe_expert_ffn(x, perm, offsets, slot_gate, W1, b1, W2, b2, k: int, capacity_factor: float,
-                   workspace: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
-    """Step 6 with the gate folded in. Returns fp32 slot_out [T*k, d] (rows past S unspecified)."""
+                   workspace: Optional[torch.Tensor] = None, flags: int = 0,
+                   slot_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Step 6 with the gate folded in. Returns fp32 slot_out [T*k, d] (rows past S
+    unspecified; a given slot_out keeps the rows the call does not write)."""
     dev = x.device
     T, d = x.shape
     N, d_ff, _ = W1.shape
@@ -235,7 +237,9 @@ def moe_expert_ffn(x, perm, offsets, slot_gate, W1, b1, W2, b2, k: int, capacity
     _check(W2, "W2", dev, x.dtype, (N, d, d_ff))
     _check(b1, "b1", dev, x.dtype, (N, d_ff))
     _check(b2, "b2", dev, x.dtype, (N, d))
-    slot_out = torch.empty((max(T * k, 1), d), dtype=torch.float32, device=dev)
+    if slot_out is None:
+        slot_out = torch.empty((max(T * k, 1), d), dtype=torch.float32, device=dev)
+    _check(slot_out, "slot_out", dev, torch.float32, (max(T * k, 1), d))
     if workspace is None:
         workspace = alloc_workspace(moe_workspace_bytes(T, d, d_ff, N, k, capacity_factor, x.dtype), dev)
     st = _lib.moe_expert_ffn(_ptr(x), _ptr(perm), _ptr(offsets), _ptr(slot_gate), _ptr(W1), _ptr(b1),

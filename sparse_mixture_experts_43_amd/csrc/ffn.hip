@@ -54,21 +54,30 @@ namespace {
 // each expert fits one m-tile (measured; with skewed routing and several
 // m-tiles per expert, contiguous experts load the second GEMM's XCDs unevenly).
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ off, int N,
-                                                        int BM, int NT1, int NT2, int max1,
-                                                        int max2, int expert_major,
+                                                        int S_max, int Ccap, int BM, int NT1,
+                                                        int NT2, int max1, int max2,
+                                                        int expert_major,
                                                         int4* __restrict__ tiles1,
                                                         int4* __restrict__ tiles2,
                                                         int32_t* __restrict__ counts) {
   // counts[4 .. 19]: the two GEMMs' per-XCD work-queue counters, zeroed here
   if (threadIdx.x < 16) counts[4 + threadIdx.x] = 0;
   __shared__ int mtoff[kMaxN + 1];
+  __shared__ int rbeg[kMaxN], rcnt[kMaxN];  // each expert's rows, clamped to the plan
   __shared__ int tmp[17];
   __shared__ int carry;
   if (threadIdx.x == 0) carry = 0;
   const int l = lane_id(), wv = threadIdx.x / kWave;
   for (int e0 = 0; e0 < N; e0 += 1024) {
     const int e = e0 + threadIdx.x;
-    const int mt = (e < N) ? cdiv(off[e + 1] - off[e], BM) : 0;
+    int mt = 0;
+    if (e < N) {
+      int m0, mc;
+      expert_rows(off, e, S_max, Ccap, m0, mc);
+      rbeg[e] = m0;
+      rcnt[e] = mc;
+      mt = cdiv(mc, BM);
+    }
     // block exclusive scan
     int x = mt;
 #pragma unroll
@@ -113,8 +122,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
         const int e = lo;
         const int local = p - mtoff[e] * NTn;
         const int mt = local / NTn, nt = local - mt * NTn;
-        const int cnt_e = off[e + 1] - off[e];
-        tl[p] = make_int4(e, off[e] + mt * BM, min(BM, cnt_e - mt * BM), nt);
+        tl[p] = make_int4(e, rbeg[e] + mt * BM, min(BM, rcnt[e] - mt * BM), nt);
         continue;
       }
       // residue group r of entry p (groups are never empty where p lands)
@@ -136,8 +144,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
       const int band = local / me;  // the expert's band-th n-tile of residue r
       const int mt = local - band * me;
       const int nt = band * 8 + r;
-      const int cnt_e = off[e + 1] - off[e];
-      tl[p] = make_int4(e, off[e] + mt * BM, min(BM, cnt_e - mt * BM), nt);
+      tl[p] = make_int4(e, rbeg[e] + mt * BM, min(BM, rcnt[e] - mt * BM), nt);
     }
     if (threadIdx.x == 0) counts[pass] = total;
   }
@@ -320,12 +327,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
     const bf16* __restrict__ X, const bf16* __restrict__ X_lo, const int32_t* __restrict__ perm,
     int kpairs, const int32_t* __restrict__ off, const bf16* __restrict__ W,
     const bf16* __restrict__ bias, const float* __restrict__ gate, int K, int Nout, int nblk_n,
-    void* __restrict__ out, bf16* __restrict__ out_lo) {
+    void* __restrict__ out, bf16* __restrict__ out_lo, int S_cap, int cap) {
   constexpr bool XLO = SPLIT && !G1;
   const int e = blockIdx.x / nblk_n;
   const int nb = blockIdx.x - e * nblk_n;
-  const int m0 = off[e];
-  const int mcount = off[e + 1] - m0;
+  int m0, mcount;
+  expert_rows(off, e, S_cap, cap < 64 ? cap : 64, m0, mcount);
   if (mcount <= 0) return;
   const int l = lane_id();
   const int wv = threadIdx.x / kWave;
@@ -504,6 +511,7 @@ struct Plan {
   int ks1, ks2;    // decode split-K factors (1 = none)
   bool dma1, dma2; // decode GEMMs on the LDS-DMA stream kernel
   int xg;          // decode: 16-slot groups an expert can hold (capacity / 16, rounded up to 1, 2, 4)
+  int cap;         // slots an expert can hold: min(C, T)
 };
 
 // Split-K factor for a decode GEMM: enough blocks to cover the CUs a few times.
@@ -525,6 +533,7 @@ Plan make_plan(int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype
   Plan p{};
   p.ks1 = p.ks2 = 1;
   const int Ccap = C < T ? C : T;
+  p.cap = Ccap;
   p.split = dtype == kBF16 && (flags & kFlagHiddenSplit);
   if (dtype == kF32) {
     p.path = kPathF32;
@@ -648,7 +657,7 @@ template <bool G1, bool SPLIT, int XG, int KC>
 void launch_decode_dma(int nsplit, const bf16* X, const bf16* X_lo, const int32_t* perm, int k,
                        const int32_t* off, const bf16* W, const bf16* bias, const float* gate,
                        int K, int Nout, int N, void* out, bf16* out_lo, float* part, int S_cap,
-                       hipStream_t st, bool reduce) {
+                       int cap, hipStream_t st, bool reduce) {
   constexpr int RING = decode_ring(XG, SPLIT && !G1, KC);
   using Geo = DecodeGeom<G1, SPLIT, XG, RING, KC>;
   const int nb = cdiv(Nout, kDWRows);
@@ -657,10 +666,11 @@ void launch_decode_dma(int nsplit, const bf16* X, const bf16* X_lo, const int32_
                              Geo::LDS, N * nb * nsplit);
   hipLaunchKernelGGL((decode_dma_kernel<G1, SPLIT, XG, RING, KC>), dim3(grid), dim3(256), Geo::LDS,
                      st, X, X_lo, perm, k, off, W, bias, gate, K, Nout, nb, nsplit, out, out_lo,
-                     part, S_cap, N);
+                     part, S_cap, cap, N);
   if (nsplit > 1 && reduce)
     hipLaunchKernelGGL((decode_reduce_kernel<G1, SPLIT>), dim3(N * nb), dim3(256), 0, st, part,
-                       nsplit, S_cap, off, bias, gate, Nout, nb, out, out_lo);
+                       nsplit, S_cap, cap < 16 * XG ? cap : 16 * XG, off, bias, gate, Nout, nb,
+                       out, out_lo);
 }
 
 // One decode GEMM: LDS-DMA stream kernel (+ split-K reduce) when K % 128 == 0,
@@ -669,7 +679,7 @@ template <bool G1, bool SPLIT>
 void launch_decode_gemm(bool dma, int nsplit, int xg, const bf16* X, const bf16* X_lo,
                         const int32_t* perm, int k, const int32_t* off, const bf16* W,
                         const bf16* bias, const float* gate, int K, int Nout, int N, void* out,
-                        bf16* out_lo, float* part, int S_cap, hipStream_t st,
+                        bf16* out_lo, float* part, int S_cap, int cap, hipStream_t st,
                         bool reduce = true) {
   if (dma) {
     // the first GEMM (shorter K) streams better in 512-byte row chunks, one
@@ -677,25 +687,25 @@ void launch_decode_gemm(bool dma, int nsplit, int xg, const bf16* X, const bf16*
     if (G1 && K % 256 == 0 && xg <= 2) {
       if (xg <= 1)
         launch_decode_dma<G1, SPLIT, 1, 256>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K,
-                                             Nout, N, out, out_lo, part, S_cap, st, reduce);
+                                             Nout, N, out, out_lo, part, S_cap, cap, st, reduce);
       else
         launch_decode_dma<G1, SPLIT, 2, 256>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K,
-                                             Nout, N, out, out_lo, part, S_cap, st, reduce);
+                                             Nout, N, out, out_lo, part, S_cap, cap, st, reduce);
     } else if (xg <= 1) {
       launch_decode_dma<G1, SPLIT, 1, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
-                                           N, out, out_lo, part, S_cap, st, reduce);
+                                           N, out, out_lo, part, S_cap, cap, st, reduce);
     } else if (xg == 2) {
       launch_decode_dma<G1, SPLIT, 2, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
-                                           N, out, out_lo, part, S_cap, st, reduce);
+                                           N, out, out_lo, part, S_cap, cap, st, reduce);
     } else {
       launch_decode_dma<G1, SPLIT, 4, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
-                                           N, out, out_lo, part, S_cap, st, reduce);
+                                           N, out, out_lo, part, S_cap, cap, st, reduce);
     }
     return;
   }
   const int nb = cdiv(Nout, kDecRows);
   hipLaunchKernelGGL((decode_bf16_kernel<G1, SPLIT>), dim3(N * nb), dim3(256), 0, st, X, X_lo,
-                     perm, k, off, W, bias, gate, K, Nout, nb, out, out_lo);
+                     perm, k, off, W, bias, gate, K, Nout, nb, out, out_lo, S_cap, cap);
 }
 
 template <bool SPLIT>
@@ -708,11 +718,11 @@ hipError_t launch_decode(const void* x, const int32_t* perm, const int32_t* off,
   profile_mark(3, st);
   launch_decode_gemm<true, SPLIT>(pl.dma1, pl.ks1, pl.xg, (const bf16*)x, nullptr, perm, k, off,
                                   (const bf16*)W1, (const bf16*)b1, nullptr, d, d_ff, N, hid,
-                                  hid_lo, part, S_cap, st);
+                                  hid_lo, part, S_cap, pl.cap, st);
   profile_mark(4, st);
   launch_decode_gemm<false, SPLIT>(pl.dma2, pl.ks2, pl.xg, (const bf16*)hid, hid_lo, perm, k, off,
                                    (const bf16*)W2, (const bf16*)b2, gate, d_ff, d, N, slot_out,
-                                   nullptr, part, S_cap, st, !defer2);
+                                   nullptr, part, S_cap, pl.cap, st, !defer2);
   if (defer2) {
     defer->part = part;
     defer->nsplit = pl.ks2;
@@ -773,8 +783,9 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
   // expert-major for the second, experts of several m-tiles the reverse
   const bool single_mt = (C < T ? C : T) <= pl.BM;
   const int em = pl.path == kPathTiledM ? (single_mt ? 2 : 1) : 0;
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, off, N, pl.BM,
-                     cdiv(d_ff, pl.BN1), cdiv(d, pl.BN2), pl.max1, pl.max2, em, t1, t2, s.counts);
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, off, N, S_max, C < T ? C : T,
+                     pl.BM, cdiv(d_ff, pl.BN1), cdiv(d, pl.BN2), pl.max1, pl.max2, em, t1, t2,
+                     s.counts);
   if (pl.path == kPathF32) {
     profile_mark(3, st);
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(pl.max1 > 0 ? pl.max1 : 1), dim3(256), 0, st,

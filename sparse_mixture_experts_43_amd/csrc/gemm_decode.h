@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
     int kpairs, const int32_t* __restrict__ off, const bf16* __restrict__ W,
     const bf16* __restrict__ bias, const float* __restrict__ gate, int K, int Nout, int nblk_n,
     int nsplit, void* __restrict__ out, bf16* __restrict__ out_lo, float* __restrict__ part,
-    int S_cap, int n_experts) {
+    int S_cap, int cap, int n_experts) {
   using Geo = DecodeGeom<G1, SPLIT, XG, RING, KC>;
   constexpr bool XLO = Geo::XLO;
   constexpr int ROWB = Geo::ROWB, CPR = Geo::CPR, RPI = Geo::RPI, WLD = Geo::WLD, XLD = Geo::XLD;
@@ -78,8 +78,7 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
     const int rest = i / nsplit;
     e = rest / nblk_n;
     n0 = (rest - e * nblk_n) * kDWRows;
-    m0 = off[e];
-    mcount = off[e + 1] - m0;
+    expert_rows(off, e, S_cap, cap < 16 * XG ? cap : 16 * XG, m0, mcount);
     c0 = ks * per;
     nch = min(nch_all, c0 + per) - c0;
     ng = (mcount + 15) / 16;
@@ -245,13 +244,13 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
 // block per (expert, 64-row block), threads over (slot, row).
 template <bool G1, bool SPLIT>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(
-    const float* __restrict__ part, int nsplit, int S_cap, const int32_t* __restrict__ off,
+    const float* __restrict__ part, int nsplit, int S_cap, int cap, const int32_t* __restrict__ off,
     const bf16* __restrict__ bias, const float* __restrict__ gate, int Nout, int nblk_n,
     void* __restrict__ out, bf16* __restrict__ out_lo) {
   const int e = blockIdx.x / nblk_n;
   const int nb = blockIdx.x - e * nblk_n;
-  const int m0 = off[e];
-  const int mcount = off[e + 1] - m0;
+  int m0, mcount;
+  expert_rows(off, e, S_cap, cap, m0, mcount);
   const int n0 = nb * kDWRows;
   for (int i = threadIdx.x; i < mcount * kDWRows; i += 256) {
     const int sl = i / kDWRows, n = n0 + i % kDWRows;

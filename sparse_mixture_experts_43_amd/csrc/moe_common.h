@@ -68,6 +68,20 @@ __device__ __forceinline__ unsigned long long key_code(double k) {
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ __forceinline__ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Slot rows [m0, m0 + mcount) of expert e for an expert GEMM planned for at
+// most S_cap slots in all and `cap` per expert. Offsets from moe_dispatch with
+// the same sizes and capacity factor are within both bounds already; other
+// offsets are clamped so every access stays inside the plan's buffers (the
+// rows past the bounds are then not computed).
+__device__ __forceinline__ void expert_rows(const int32_t* __restrict__ off, int e, int S_cap,
+                                            int cap, int& m0, int& mcount) {
+  int a = off[e], b = off[e + 1];
+  a = a < 0 ? 0 : (a > S_cap ? S_cap : a);
+  b = b < a ? a : (b > S_cap ? S_cap : b);
+  m0 = a;
+  mcount = b - a < cap ? b - a : cap;
+}
+
 // ---------------------------------------------------------------- host side
 // Raise a kernel's dynamic-LDS limit to all the LDS a workgroup may have
 // (160 KB on gfx950) minus its static LDS. Once per call site (idempotent; a

@@ -191,3 +191,52 @@ def test_plain_bf16_full_size(lib, name):
         f"(bar {res['strict_tol']:.0e})")
     record("plain_bf16_full", name, res)
 
+
+MISMATCH = [
+    # name, T, d, d_ff, N, k, capacity factor of the dispatch, of the FFN call
+    ("decode_path", 96, 256, 384, 8, 2, 0.0, 1.0),
+    ("tiled_path", 600, 256, 320, 4, 2, 0.0, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", MISMATCH, ids=[c[0] for c in MISMATCH])
+def test_ffn_offsets_from_larger_capacity(lib, case):
+    """moe_expert_ffn given the dispatch of a larger capacity factor than its
+    own (an API misuse): the kernels clamp each expert's rows to the call's
+    capacity C and all rows to min(T*k, N*C), so every access stays inside the
+    buffers planned for the call. The rows inside those bounds equal the
+    consistent call's (up to fp32 summation order); every other slot_out row
+    keeps the value it held before the call."""
+    import numpy as np
+    from gpu_util import say, to_dev
+    from moe_inputs import make_inputs
+    name, T, d, d_ff, N, k, cf_disp, cf_ffn = case
+    w = Workload(name, T=T, d=d, d_ff=d_ff, N=N, k=k, capacity_factor=cf_disp, dtype="bf16",
+                 ffn_bias=True, skew="normal0.5", seed=2)
+    say(f"[case] mismatched capacity {name} T={T} d={d} d_ff={d_ff} N={N} k={k} "
+        f"dispatch cf={cf_disp} ffn cf={cf_ffn}")
+    dv = to_dev(make_inputs(w))
+    _, idx, gw, gkey = lib.moe_route(dv["x"], dv["W_g"], dv["logit_bias"], k)
+    disp = lib.moe_dispatch(idx, gw, gkey, N, cf_disp)
+    args = (dv["x"], disp["perm"], disp["offsets"], disp["slot_gate"], dv["W1"], dv["b1"],
+            dv["W2"], dv["b2"], k)
+    good = lib.moe_expert_ffn(*args, cf_disp)
+    sentinel = torch.full((T * k, d), float("nan"), dtype=torch.float32, device="cuda")
+    so = lib.moe_expert_ffn(*args, cf_ffn, slot_out=sentinel.clone())
+    torch.cuda.synchronize()
+    off = disp["offsets"].cpu().numpy().astype(np.int64)
+    C = lib.moe_capacity(T, N, k, cf_ffn)
+    S_max = min(T * k, N * C)
+    computed = np.zeros(T * k, dtype=bool)
+    for e in range(N):
+        a = min(off[e], S_max)
+        b = min(off[e + 1], S_max)
+        computed[a:a + min(b - a, C)] = True
+    assert off[-1] > S_max or np.any(np.diff(off) > C), "the case must need the clamp"
+    got = so.cpu().numpy()
+    ref = good.cpu().numpy()
+    assert np.all(np.isnan(got[~computed])), "a row outside the call's bounds was written"
+    assert np.all(np.isfinite(got[computed]))
+    np.testing.assert_allclose(got[computed], ref[computed], rtol=1e-4,
+                               atol=1e-4 * float(np.abs(ref[computed]).max()))
+    say(f"[ok] {name}: {int(computed.sum())} of {int(off[-1])} rows computed")
