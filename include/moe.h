@@ -25,7 +25,9 @@
  *  - Every tensor pointer is a DEVICE pointer owned by the caller. The library
  *    never allocates or frees device memory and keeps no state between calls.
  *    Scratch memory comes from the caller's `workspace` (device memory of at
- *    least moe_workspace_bytes(...) bytes, 256-byte aligned).
+ *    least moe_workspace_bytes(...) bytes, 256-byte aligned). The one
+ *    exception is moe_forward_noalloc, whose scratch is a static device array
+ *    of MOE_NOALLOC_SCRATCH_BYTES per GPU (see there).
  *  - Inputs are never written. Outputs are fully overwritten (rows past the
  *    kept-slot count S of slot-indexed outputs are left untouched).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
@@ -263,6 +265,38 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias,
                 float* logits_opt, int32_t* topk_idx_opt, int32_t* inv_opt,
                 int32_t* req_counts_opt, int32_t* counts_opt, int32_t* n_dropped_opt,
                 void* workspace, size_t ws_bytes, void* stream);
+
+/* Size of the static per-GPU scratch array behind moe_forward_noalloc: 64 MiB. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results, flags and errors are those of moe_forward without
+ * `workspace` / `ws_bytes`; the same kernels run and give the same bits.
+ * Scratch: one static device array of MOE_NOALLOC_SCRATCH_BYTES per GPU,
+ * reserved when the library's code is loaded on that GPU and held until the
+ * process ends; its address on the current device is looked up on the first
+ * call there (make that first call outside graph capture, as the first
+ * moe_forward of a shape should be) and cached. Nothing is allocated or freed
+ * (no hipMalloc, hipFree or allocating library call) by this entry point.
+ * Limit: a call whose moe_forward workspace for these sizes and flags
+ * (moe_workspace_bytes gives an upper bound) exceeds the array returns
+ * MOE_ERR_WORKSPACE before any launch; decode-sized calls fit (for example
+ * 32 tokens of the Mixtral-shaped layer, d = 4096, d_ff = 14336, N = 8,
+ * top-2, with any flags).
+ * Every call on one GPU uses that GPU's one array, which keeps the last call's
+ * contents; no part of it needs to start at zero (every kernel writes what it
+ * later reads, and the work-queue counters are zeroed by the launch sequence).
+ * Calls that overlap on one GPU (other streams, or other host threads, without
+ * ordering between them) race on the array and give wrong results: order them
+ * on one stream. */
+int moe_forward_noalloc(const void* x, const void* W_g, const float* logit_bias,
+                        const void* W1, const void* b1, const void* W2, const void* b2,
+                        int T, int d, int d_ff, int N, int k, double capacity_factor, int dtype,
+                        int flags, const float* shared_out, void* y,
+                        float* logits_opt, int32_t* topk_idx_opt, int32_t* inv_opt,
+                        int32_t* req_counts_opt, int32_t* counts_opt, int32_t* n_dropped_opt,
+                        void* stream);
 
 /* Instrumentation for timing (not part of the layer): registers up to 7
  * hipEvent_t handles (as void*, entries may be NULL) for the calling thread;

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     MOE_FLAG_IDENTITY_FALLBACK,
     MOE_FLAG_RENORM_SURVIVORS,
     MOE_FLAG_Y_F32,
+    MOE_NOALLOC_SCRATCH_BYTES,
     MoeError,
     alloc_workspace,
     moe_capacity,
@@ -22,6 +23,7 @@ from ._lib import (  # noqa: F401
     moe_dispatch,
     moe_expert_ffn,
     moe_forward,
+    moe_forward_noalloc,
     moe_route,
     moe_routing_stats,
     moe_set_profile_events,

@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
         "moe_combine": (_c_int, [_vp] * 4 + [_c_int] * 5 + [_vp, _vp]),
         "moe_forward": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_c_double, _c_int, _c_int]
                         + [_vp] * 8 + [_vp, _c_size, _vp]),
+        "moe_forward_noalloc": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_c_double, _c_int, _c_int]
+                                + [_vp] * 8 + [_vp]),
         "moe_shared_workspace_bytes": (_c_size, [_c_int] * 4),
         "moe_shared_expert": (_c_int, [_vp] * 5 + [_c_int] * 5 + [_vp] + [_vp, _c_size, _vp]),
         "moe_set_profile_events": (_c_int, [ctypes.POINTER(_vp), _c_int]),
@@ -75,7 +77,8 @@ _lib = _load()
 
 EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_capacity",
             "moe_workspace_bytes", "moe_route", "moe_routing_stats", "moe_dispatch",
-            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_set_profile_events",
+            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc",
+            "moe_set_profile_events",
             "moe_shared_workspace_bytes", "moe_shared_expert")
 
 
@@ -339,6 +342,53 @@ def moe_forward(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: flo
                           _ptr(ex.get("req_counts")), _ptr(ex.get("counts")), _ptr(ex.get("n_dropped")),
                           _ptr(workspace), workspace.numel(), _stream(dev))
     _raise(st, "moe_forward")
+    return (y, ex) if want_routing else y
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(x, W_g, logit_bias, W1, b1, W2, b2, k: int, capacity_factor: float,
+                        y: Optional[torch.Tensor] = None, want_routing: bool = False,
+                        flags: int = 0, shared_out: Optional[torch.Tensor] = None):
+    """moe_forward without a workspace: the library's static per-GPU scratch
+    array (MOE_NOALLOC_SCRATCH_BYTES) holds the intermediates. Pass y (and
+    shared_out) preallocated to keep the call free of allocation; the routing
+    extras, when asked for, are allocated here as for moe_forward."""
+    dev = x.device
+    T, d = x.shape
+    N, d_ff, _ = W1.shape
+    _check(x, "x", dev)
+    _check(W_g, "W_g", dev, x.dtype, (d, N))
+    _check(logit_bias, "logit_bias", dev, torch.float32, (N,))
+    _check(W1, "W1", dev, x.dtype, (N, d_ff, d))
+    _check(W2, "W2", dev, x.dtype, (N, d, d_ff))
+    _check(b1, "b1", dev, x.dtype, (N, d_ff))
+    _check(b2, "b2", dev, x.dtype, (N, d))
+    _check(shared_out, "shared_out", dev, torch.float32, (T, d))
+    y_dtype = torch.float32 if (flags & MOE_FLAG_Y_F32) else x.dtype
+    if y is None:
+        y = torch.empty((T, d), dtype=y_dtype, device=dev)
+    _check(y, "y", dev, y_dtype, (T, d))
+    ex = {}
+    ec = bool(flags & MOE_FLAG_EXPERT_CHOICE)
+    kp = N if ec else k
+    if want_routing:
+        ex = {
+            "logits": torch.empty((T, N), dtype=torch.float32, device=dev),
+            "topk_idx": None if ec else torch.empty((T, k), dtype=torch.int32, device=dev),
+            "inv": torch.empty(max(T * kp, 1), dtype=torch.int32, device=dev),
+            "req_counts": torch.empty(N, dtype=torch.int32, device=dev),
+            "counts": torch.empty(N, dtype=torch.int32, device=dev),
+            "n_dropped": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+    st = _lib.moe_forward_noalloc(_ptr(x), _ptr(W_g), _ptr(logit_bias), _ptr(W1), _ptr(b1),
+                                  _ptr(W2), _ptr(b2), T, d, d_ff, N, k, float(capacity_factor),
+                                  _dtype_code(x.dtype), int(flags), _ptr(shared_out), _ptr(y),
+                                  _ptr(ex.get("logits")), _ptr(ex.get("topk_idx")),
+                                  _ptr(ex.get("inv")), _ptr(ex.get("req_counts")),
+                                  _ptr(ex.get("counts")), _ptr(ex.get("n_dropped")), _stream(dev))
+    _raise(st, "moe_forward_noalloc")
     return (y, ex) if want_routing else y
 
 

@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace moe {
 
 static thread_local int g_last_hip = 0;
@@ -104,6 +106,107 @@ static size_t ffn_bytes(int T, int d, int d_ff, int N, int k, int C, int dtype, 
   const int S_max = (int)((long long)T * k < (long long)N * C ? (long long)T * k : (long long)N * C);
   carve_ffn(c, T, d, d_ff, N, k, C, S_max, dtype, flags, &fs);
   return align_up(c.off, 256);
+}
+
+// ---------------------------------------------------------------- no-alloc scratch
+// Scratch of moe_forward_noalloc: one static device array, which each GPU the
+// library's code is loaded on holds until the process ends. In host code the
+// array's name is not a device address: its address on the current device
+// comes from hipGetSymbolAddress, looked up once per device and cached; only
+// that address is ever handed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_status(e != hipSuccess ? e : hipErrorUnknown);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// The layer forward behind moe_forward (caller workspace) and
+// moe_forward_noalloc (noalloc: the device's static scratch array, whose
+// address replaces workspace once the sizes are known to fit).
+static int forward_impl(const void* x, const void* W_g, const float* logit_bias, const void* W1,
+                        const void* b1, const void* W2, const void* b2, int T, int d, int d_ff,
+                        int N, int k, double capacity_factor, int dtype, int flags,
+                        const float* shared_out, void* y, float* logits_opt,
+                        int32_t* topk_idx_opt, int32_t* inv_opt, int32_t* req_counts_opt,
+                        int32_t* counts_opt, int32_t* n_dropped_opt, void* workspace,
+                        size_t ws_bytes, void* stream, bool noalloc) {
+  int st = check_shape(T, d, d_ff, N, k, dtype, true);
+  if (st != MOE_OK) return st;
+  if (isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (flags & ~(MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32 | MOE_FLAG_FIRST_COME |
+                MOE_FLAG_RENORM_SURVIVORS | MOE_FLAG_IDENTITY_FALLBACK | MOE_FLAG_EXPERT_CHOICE))
+    return MOE_ERR_INVALID_ARG;
+  const bool ec = (flags & MOE_FLAG_EXPERT_CHOICE) != 0;
+  if (ec && ((flags & (MOE_FLAG_FIRST_COME | MOE_FLAG_RENORM_SURVIVORS)) || topk_idx_opt))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !W_g || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(W_g, 16) || !aligned(W1, 16) || !aligned(W2, 16) ||
+      !aligned(y, 16) || (b1 && !aligned(b1, 16)) || (b2 && !aligned(b2, 16)) ||
+      (logit_bias && !aligned(logit_bias, 4)) || (logits_opt && !aligned(logits_opt, 4)) ||
+      (shared_out && !aligned(shared_out, 16)))
+    return MOE_ERR_UNSUPPORTED;
+  const int C = capacity_host(T, N, k, capacity_factor);
+  // pairs per token: k picks, or with expert choice every expert (pair t*N + e)
+  const int kp = ec ? N : k;
+  ForwardWs f;
+  carve_forward(nullptr, T, d, d_ff, N, kp, C, dtype, flags, &f);
+  if (noalloc) {
+    if (f.bytes > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+    const int ss = noalloc_scratch(&workspace);
+    if (ss != MOE_OK) return ss;
+    ws_bytes = kNoAllocScratchBytes;
+  }
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < f.bytes) return MOE_ERR_WORKSPACE;
+  carve_forward(workspace, T, d, d_ff, N, kp, C, dtype, flags, &f);
+  if (logits_opt) f.logits = logits_opt;
+  if (topk_idx_opt) f.idx = topk_idx_opt;
+  if (inv_opt) f.inv = inv_opt;
+  if (req_counts_opt) f.req = req_counts_opt;
+  if (counts_opt) f.cnt = counts_opt;
+  if (n_dropped_opt) f.ndrop = n_dropped_opt;
+  const int S_max =
+      (int)((long long)T * kp < (long long)N * C ? (long long)T * kp : (long long)N * C);
+  hipStream_t s = (hipStream_t)stream;
+  profile_mark(0, s);
+  // expert choice: the router's logits (its top-1 outputs are scratch), then
+  // every pair as a candidate
+  hipError_t e = launch_route(x, W_g, logit_bias, T, d, N, ec ? 1 : k, dtype, f.logits, f.idx,
+                              f.w, f.key, f.wgt, s);
+  if (e == hipSuccess && ec) e = launch_route_expert_choice(f.logits, T, N, f.idx, f.w, f.key, s);
+  if (e != hipSuccess) return hip_status(e);
+  profile_mark(1, s);
+  e = launch_dispatch(f.idx, f.w, f.key, T, N, kp, C, flags, f.req, f.cnt, f.off, f.perm, f.inv,
+                      f.gate, f.ndrop, f.ds, s);
+  if (e != hipSuccess) return hip_status(e);
+  profile_mark(2, s);
+  SplitK sk;  // a K-split second GEMM hands its partials straight to the combine
+  e = launch_expert_ffn(x, f.perm, f.off, f.gate, W1, b1, W2, b2, T, d, d_ff, N, kp, C, S_max,
+                        dtype, flags, f.slot_out, f.fs, s, &sk);
+  if (e != hipSuccess) return hip_status(e);
+  const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
+  const void* xf = (flags & MOE_FLAG_IDENTITY_FALLBACK) ? x : nullptr;
+  e = sk.nsplit > 1
+          ? launch_combine_splitk(sk, f.inv, T, d, kp, y_dtype, xf, dtype, shared_out, y, s)
+          : launch_combine(f.slot_out, f.inv, T, d, kp, y_dtype, xf, dtype, shared_out, y, s);
+  profile_mark(6, s);
+  return hip_status(e);
 }
 
 }  // namespace moe
@@ -298,61 +401,21 @@ int moe_forward(const void* x, const void* W_g, const float* logit_bias, const v
                 int32_t* topk_idx_opt, int32_t* inv_opt, int32_t* req_counts_opt,
                 int32_t* counts_opt, int32_t* n_dropped_opt, void* workspace, size_t ws_bytes,
                 void* stream) {
-  int st = check_shape(T, d, d_ff, N, k, dtype, true);
-  if (st != MOE_OK) return st;
-  if (isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
-  if (flags & ~(MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32 | MOE_FLAG_FIRST_COME |
-                MOE_FLAG_RENORM_SURVIVORS | MOE_FLAG_IDENTITY_FALLBACK | MOE_FLAG_EXPERT_CHOICE))
-    return MOE_ERR_INVALID_ARG;
-  const bool ec = (flags & MOE_FLAG_EXPERT_CHOICE) != 0;
-  if (ec && ((flags & (MOE_FLAG_FIRST_COME | MOE_FLAG_RENORM_SURVIVORS)) || topk_idx_opt))
-    return MOE_ERR_INVALID_ARG;
-  if (T == 0) return MOE_OK;
-  if (!x || !W_g || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(W_g, 16) || !aligned(W1, 16) || !aligned(W2, 16) ||
-      !aligned(y, 16) || (b1 && !aligned(b1, 16)) || (b2 && !aligned(b2, 16)) ||
-      (logit_bias && !aligned(logit_bias, 4)) || (logits_opt && !aligned(logits_opt, 4)) ||
-      (shared_out && !aligned(shared_out, 16)))
-    return MOE_ERR_UNSUPPORTED;
-  const int C = capacity_host(T, N, k, capacity_factor);
-  // pairs per token: k picks, or with expert choice every expert (pair t*N + e)
-  const int kp = ec ? N : k;
-  ForwardWs f;
-  carve_forward(nullptr, T, d, d_ff, N, kp, C, dtype, flags, &f);
-  if (!workspace || !aligned(workspace, 256) || ws_bytes < f.bytes) return MOE_ERR_WORKSPACE;
-  carve_forward(workspace, T, d, d_ff, N, kp, C, dtype, flags, &f);
-  if (logits_opt) f.logits = logits_opt;
-  if (topk_idx_opt) f.idx = topk_idx_opt;
-  if (inv_opt) f.inv = inv_opt;
-  if (req_counts_opt) f.req = req_counts_opt;
-  if (counts_opt) f.cnt = counts_opt;
-  if (n_dropped_opt) f.ndrop = n_dropped_opt;
-  const int S_max =
-      (int)((long long)T * kp < (long long)N * C ? (long long)T * kp : (long long)N * C);
-  hipStream_t s = (hipStream_t)stream;
-  profile_mark(0, s);
-  // expert choice: the router's logits (its top-1 outputs are scratch), then
-  // every pair as a candidate
-  hipError_t e = launch_route(x, W_g, logit_bias, T, d, N, ec ? 1 : k, dtype, f.logits, f.idx,
-                              f.w, f.key, f.wgt, s);
-  if (e == hipSuccess && ec) e = launch_route_expert_choice(f.logits, T, N, f.idx, f.w, f.key, s);
-  if (e != hipSuccess) return hip_status(e);
-  profile_mark(1, s);
-  e = launch_dispatch(f.idx, f.w, f.key, T, N, kp, C, flags, f.req, f.cnt, f.off, f.perm, f.inv,
-                      f.gate, f.ndrop, f.ds, s);
-  if (e != hipSuccess) return hip_status(e);
-  profile_mark(2, s);
-  SplitK sk;  // a K-split second GEMM hands its partials straight to the combine
-  e = launch_expert_ffn(x, f.perm, f.off, f.gate, W1, b1, W2, b2, T, d, d_ff, N, kp, C, S_max,
-                        dtype, flags, f.slot_out, f.fs, s, &sk);
-  if (e != hipSuccess) return hip_status(e);
-  const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
-  const void* xf = (flags & MOE_FLAG_IDENTITY_FALLBACK) ? x : nullptr;
-  e = sk.nsplit > 1
-          ? launch_combine_splitk(sk, f.inv, T, d, kp, y_dtype, xf, dtype, shared_out, y, s)
-          : launch_combine(f.slot_out, f.inv, T, d, kp, y_dtype, xf, dtype, shared_out, y, s);
-  profile_mark(6, s);
-  return hip_status(e);
+  return forward_impl(x, W_g, logit_bias, W1, b1, W2, b2, T, d, d_ff, N, k, capacity_factor,
+                      dtype, flags, shared_out, y, logits_opt, topk_idx_opt, inv_opt,
+                      req_counts_opt, counts_opt, n_dropped_opt, workspace, ws_bytes, stream,
+                      false);
+}
+
+int moe_forward_noalloc(const void* x, const void* W_g, const float* logit_bias, const void* W1,
+                        const void* b1, const void* W2, const void* b2, int T, int d, int d_ff,
+                        int N, int k, double capacity_factor, int dtype, int flags,
+                        const float* shared_out, void* y, float* logits_opt,
+                        int32_t* topk_idx_opt, int32_t* inv_opt, int32_t* req_counts_opt,
+                        int32_t* counts_opt, int32_t* n_dropped_opt, void* stream) {
+  return forward_impl(x, W_g, logit_bias, W1, b1, W2, b2, T, d, d_ff, N, k, capacity_factor,
+                      dtype, flags, shared_out, y, logits_opt, topk_idx_opt, inv_opt,
+                      req_counts_opt, counts_opt, n_dropped_opt, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

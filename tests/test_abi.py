@@ -143,3 +143,25 @@ def test_argument_checks_return_before_launch():
     assert raw.moe_routing_stats(p, p, 4, 8, 2, nul, p, 1 << 30, nul) == -1
     assert raw.moe_routing_stats(p, p, 4, 8, 2, p, p, 16, nul) == -3
     assert raw.moe_routing_stats(nul, nul, 0, 8, 2, nul, nul, 0, nul) == 0
+
+
+def test_noalloc_host_checks(lib):
+    """moe_forward_noalloc: the argument checks of moe_forward, and a call whose
+    scratch would exceed the static array is refused with MOE_ERR_WORKSPACE,
+    all before any HIP call (no GPU needed)."""
+    from sparse_mixture_experts_43_amd._lib import _lib as raw
+    nul = None
+    p = ctypes.c_void_p(4096)
+    fargs = [p] * 7
+    tail = [nul, p, nul, nul, nul, nul, nul, nul, nul]
+    assert raw.moe_forward_noalloc(*fargs, -1, 64, 64, 8, 2, 1.0, 1, 0, *tail) == -1
+    assert raw.moe_forward_noalloc(*fargs, 4, 64, 64, 8, 2, float("nan"), 1, 0, *tail) == -1
+    assert raw.moe_forward_noalloc(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 64, *tail) == -1
+    assert raw.moe_forward_noalloc(*fargs, 4, 60, 64, 8, 2, 1.0, 1, 0, *tail) == -2
+    assert raw.moe_forward_noalloc(nul, nul, nul, nul, nul, nul, nul, 0, 64, 64, 8, 2, 1.0, 1, 0,
+                                   nul, nul, nul, nul, nul, nul, nul, nul, nul) == 0
+    # the Mixtral-shaped prefill: hundreds of MiB of scratch, far above the array
+    import torch
+    assert lib.moe_workspace_bytes(4096, 4096, 14336, 8, 2, 0.0, torch.bfloat16) > \
+        lib.MOE_NOALLOC_SCRATCH_BYTES
+    assert raw.moe_forward_noalloc(*fargs, 4096, 4096, 14336, 8, 2, 0.0, 1, 0, *tail) == -3
