@@ -6,11 +6,13 @@ A step is one moe_forward call (router, dispatch, both expert GEMMs, combine)
 on one batch of seeded synthetic inputs already resident in HBM. W untimed
 warm-up steps, an untimed pass with a HIP event between every stage (the
 per-stage breakdown, which also names the dominant expert GEMM), then exactly
-K timed steps between two device synchronisations, each carrying only the two
-events the library records around the dominant GEMM on its stream. Prints ONE
-JSON line (metric, value in tokens/s, roofline of the dominant kernel from
-those events, and the CPU oracle timed on a bounded sample on the host). The
-other workloads are then timed the same way and reported under "configs".
+K timed steps between two device synchronisations with nothing else on the
+stream (value, ms_per_step), then K more steps each carrying the events the
+library records around the dominant GEMM on its stream (the roofline's launch
+duration). Prints ONE JSON line (metric, value in tokens/s, roofline of the
+dominant kernel from those events, and the CPU oracle timed on a bounded
+sample on the host). The other workloads are then timed the same way and
+reported under "configs".
 Progress goes to stderr.
 """
 from __future__ import annotations
@@ -44,11 +46,19 @@ def log(msg):
 
 
 class HipEvents:
-    """Raw hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+    """Raw hipEvent_t handles from the process's HIP runtime (the one torch loaded).
+
+    Created with hipEventDisableSystemFence: they only time work, and are read
+    (hipEventElapsedTime) after a full device synchronisation, so they need no
+    system-scope fence. With the default flags every record between two
+    kernels writes back and invalidates the caches, which held the GPU idle for
+    about 6 us per event in kernel traces of this benchmark."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
     def __init__(self):
         self.rt = ctypes.CDLL("libamdhip64.so.7")
-        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                 ctypes.c_void_p]
         self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
@@ -58,8 +68,8 @@ class HipEvents:
 
     def create(self):
         h = ctypes.c_void_p()
-        if self.rt.hipEventCreate(ctypes.byref(h)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if self.rt.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         self.made.append(h.value)
         return h.value
 
@@ -315,12 +325,25 @@ def run_workload(moe, torch, w, fl, steps, warmup, want_extras, cpu_budget_s, co
     dom = "expert_gemm1" if per["expert_gemm1"] >= per["expert_gemm2"] else "expert_gemm2"
     dslot = 3 if dom == "expert_gemm1" else 4  # event slots before / after that GEMM
 
-    marks = [(ev.create(), ev.create()) for _ in range(steps)]
-    # one more event per step, before its router (slot 0), and one after the
-    # last step: step i lasts from its mark to the next one
-    starts = [ev.create() for _ in range(steps + 1)]
+    # Timed region: exactly K steps between two device synchronisations, with
+    # nothing else on the stream. (An event recorded between two kernels held
+    # the GPU idle about 4.5 us in kernel traces even without a system fence,
+    # so no event is recorded here.)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_step = (t_end - t_start) * 1e3 / steps
+
+    # Second region, the same K steps, each carrying the two events the library
+    # records around the dominant expert GEMM on its stream, and one before its
+    # router: the GEMM's average launch duration (the roofline) and each step's
+    # GPU time.
+    marks = [(ev.create(), ev.create()) for _ in range(steps)]
+    starts = [ev.create() for _ in range(steps + 1)]
+    torch.cuda.synchronize()
     for i in range(steps):
         slots = [None] * 7
         slots[0] = starts[i]
@@ -330,15 +353,13 @@ def run_workload(moe, torch, w, fl, steps, warmup, want_extras, cpu_budget_s, co
     moe.moe_set_profile_events([])
     ev.record(starts[-1], torch.cuda.current_stream(dev).cuda_stream)
     torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    ms_step = (t_end - t_start) * 1e3 / steps
     dom_ms = sum(ev.ms(a, b) for a, b in marks) / steps
     step_ms = sorted(ev.ms(starts[i], starts[i + 1]) for i in range(steps))
     step_med = (step_ms[(steps - 1) // 2] + step_ms[steps // 2]) / 2
     ev.close()
-    log(f"timed {steps} steps: {ms_step:.3f} ms/step (GPU events: median {step_med:.3f}, "
-        f"min {step_ms[0]:.3f}); {dom} {dom_ms * 1e3:.1f}us (events in the "
-        f"timed steps); stage breakdown (untimed pass with stage events): "
+    log(f"timed {steps} steps: {ms_step:.3f} ms/step; event region: {dom} {dom_ms * 1e3:.1f}us, "
+        f"steps median {step_med:.3f} ms (min {step_ms[0]:.3f}, with 3 events each); "
+        f"stage breakdown (untimed pass with stage events): "
         + ", ".join(f"{n} {v * 1e3:.1f}us" for n, v in per.items()))
 
     # extras, after the timed region: the routing statistics pass (from this
@@ -398,7 +419,9 @@ def run_workload(moe, torch, w, fl, steps, warmup, want_extras, cpu_budget_s, co
         "unit": "tokens/s",
         "ms_per_step": ms_step,
         "step_ms_gpu": {"median": step_med, "min": step_ms[0], "max": step_ms[-1],
-                        "note": "per timed step, HIP events before each step's router"},
+                        "note": "per step of the event region (K more steps after the timed "
+                                "region, each with an event before its router and two around "
+                                "the dominant GEMM; the events add a few us per step)"},
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "N": w.N, "k": w.k,
                    "capacity_factor": w.capacity_factor, "hidden": fl, "y_dtype": "f32",

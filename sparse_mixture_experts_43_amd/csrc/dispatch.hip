@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 constexpr int kFusedMaxPairs = 32768;  // pairs one block buckets by itself
+constexpr int kBatch = 8;              // global loads per thread in flight together
 
 __device__ __forceinline__ unsigned long long lanemask_lt() {
   const int l = lane_id();
@@ -152,9 +153,19 @@ __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
   int* my = fsm + wv * N;
   int* sh_reqoff = fsm + NWV * N;
   int16_t* sid = (int16_t*)(fsm + NWV * N + N);
-  for (int p = threadIdx.x; p < P; p += kScanThreads) {
-    const int e = idx[p];
-    sid[p] = (unsigned)e < (unsigned)N ? (int16_t)e : (int16_t)-1;
+  // global loads in batches of kBatch per thread, issued before any is used
+  for (int q0 = 0; q0 < P; q0 += kBatch * kScanThreads) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = q0 + u * kScanThreads + (int)threadIdx.x;
+      ev[u] = p < P ? idx[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = q0 + u * kScanThreads + (int)threadIdx.x;
+      if (p < P) sid[p] = (unsigned)ev[u] < (unsigned)N ? (int16_t)ev[u] : (int16_t)-1;
+    }
   }
   const int span = cdiv(cdiv(P, NWV), kWave) * kWave;
   const int p0 = min(P, wv * span), p1 = min(P, p0 + span);
@@ -202,20 +213,60 @@ __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
   // positions (< P <= 32768) replace the ids of valid pairs
   walk_pairs(sid, p0, p1, N, my, [&](int p, int, int pos) { sid[p] = (int16_t)pos; });
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += kScanThreads) {
-    const int s = sid[p];
-    if (s < 0) {
-      inv[p] = -1;
-    } else if (direct) {
-      write_slot(perm, inv, gate, w, p, s);
+  for (int q0 = 0; q0 < P; q0 += kBatch * kScanThreads) {
+    int sv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = q0 + u * kScanThreads + (int)threadIdx.x;
+      sv[u] = p < P ? (int)sid[p] : -1;
+    }
+    if (direct) {
+      float wv_[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = q0 + u * kScanThreads + (int)threadIdx.x;
+        wv_[u] = sv[u] >= 0 ? w[p] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = q0 + u * kScanThreads + (int)threadIdx.x;
+        if (p >= P) continue;
+        const int s = sv[u];
+        if (s < 0) {
+          inv[p] = -1;
+        } else {
+          perm[s] = p;
+          gate[s] = wv_[u];
+          inv[p] = s;
+        }
+      }
     } else {
-      bucket[s] = p;
-      codes[s] = rank_code(key, p, fc_k);
-      // a pair of an expert over capacity starts dropped; the selection
-      // writes only the kept ones
-      const int e = idx[p];
-      const int r = (e + 1 < N ? sh_reqoff[e + 1] : carry[0]) - sh_reqoff[e];
-      if (r > C) inv[p] = -1;
+      unsigned long long cv[kBatch];
+      int ev[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = q0 + u * kScanThreads + (int)threadIdx.x;
+        const bool live = sv[u] >= 0;
+        cv[u] = live ? rank_code(key, p, fc_k) : 0ull;
+        ev[u] = live ? idx[p] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = q0 + u * kScanThreads + (int)threadIdx.x;
+        if (p >= P) continue;
+        const int s = sv[u];
+        if (s < 0) {
+          inv[p] = -1;
+          continue;
+        }
+        bucket[s] = p;
+        codes[s] = cv[u];
+        // a pair of an expert over capacity starts dropped; the selection
+        // writes only the kept ones
+        const int e = ev[u];
+        const int r = (e + 1 < N ? sh_reqoff[e + 1] : carry[0]) - sh_reqoff[e];
+        if (r > C) inv[p] = -1;
+      }
     }
   }
 }

@@ -64,6 +64,11 @@ CASES = [
     ("max_d", 8, 65536, 64, 4, 2, 0.0, "bf16", False, "none", 0),
     ("max_dff", 8, 64, 65536, 4, 2, 0.0, "bf16", True, "none", 0),
     ("dense_k_eq_N", 128, 64, 128, 4, 4, 0.0, "bf16", False, "none", 0),
+    # small batches without capacity limit, 3 and 4 column tiles of 16 experts
+    # in the skinny router, 1024 pairs
+    ("small_route_N40", 48, 256, 128, 40, 4, 0.0, "bf16", True, "normal0.5", 0),
+    ("small_route_N64_k16", 64, 128, 64, 64, 16, 0.0, "bf16", False, "zipf1.1", 0),
+    ("small_route_T17_split", 17, 512, 256, 8, 2, 0.0, "bf16", True, "none", SPLIT),
     ("single_token", 1, 64, 64, 8, 2, 0.0, "bf16", False, "none", 0),
     ("capacity_one", 64, 64, 64, 8, 2, 0.01, "bf16", False, "zipf1.1", 0),
     ("many_experts_N1000", 512, 64, 64, 1000, 16, 1.0, "bf16", False, "none", 0),
