@@ -20,6 +20,8 @@
 #include "gemm_ring.h"
 #include "moe_common.h"
 
+#include <utility>
+
 namespace moe {
 
 namespace {
@@ -48,6 +50,8 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// Shift right by one lane within each 16-lane row; lane 0 of a row reads 0.
+constexpr int kDppRowShr1 = 0x111;
 
 template <int CTRL>
 __device__ __forceinline__ void argmax_step(float& bv, int& bn) {
@@ -130,14 +134,12 @@ __device__ __forceinline__ void topk_row_s(const float* __restrict__ Lrow, int N
   }
   m = wave_max_dpp(m);
 
-  // fp64 softmax denominator over all N experts.
+  // fp64 softmax denominator over all N experts (no branch: v = -inf past N
+  // and exp(-inf) is exactly 0).
   double s = 0.0;
   const double md = (double)m;
 #pragma unroll
-  for (int i = 0; i < S; ++i) {
-    const int n = l + kWave * i;
-    if (n < N) s += exp((double)v[i] - md);
-  }
+  for (int i = 0; i < S; ++i) s += exp((double)v[i] - md);
   s = wave_sum_dpp(s);
   const double lse = md + log(s);
 
@@ -484,6 +486,12 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
 // the picks' probabilities summed in pick order); only the fp64 softmax sum is
 // added in another order. `active` gates loads and stores; every lane of the
 // wave takes part in the reductions.
+//
+// The code has no data-dependent branch: every selection is a compare and a
+// conditional move. A pick is struck out by setting its value to NaN, which
+// no `>=` admits; slots past N are NaN for the scans too, after the softmax
+// (which needs them at -inf, whose exponential is exactly 0). A real -inf
+// logit is still pickable, as in topk_row.
 template <int SL>
 __device__ __forceinline__ void topk_row16x(const float* __restrict__ Lrow, bool active, int N,
                                             int k, int t, int32_t* __restrict__ idx,
@@ -502,43 +510,53 @@ __device__ __forceinline__ void topk_row16x(const float* __restrict__ Lrow, bool
   m = fmaxf(m, dpp_f32<kDppHalfMirror>(m));
   m = fmaxf(m, dpp_f32<kDppMirror>(m));
   const double md = (double)m;
+  // fp64 softmax denominator. (Rows past T, all -inf, get NaN; nothing of
+  // theirs is stored.)
   double s = 0.0;
 #pragma unroll
-  for (int i = 0; i < SL; ++i)
-    if (c + 16 * i < N) s += exp((double)v[i] - md);
+  for (int i = 0; i < SL; ++i) s += exp((double)v[i] - md);
   s += dpp_f64<kDppXor1>(s);
   s += dpp_f64<kDppXor2>(s);
   s += dpp_f64<kDppHalfMirror>(s);
   s += dpp_f64<kDppMirror>(s);
   const double lse = md + log(s);
-  unsigned taken = 0u;
+#pragma unroll
+  for (int i = 0; i < SL; ++i)
+    if (c + 16 * i >= N) v[i] = __builtin_nanf("");
+  // Lane c of the group keeps pick c.
   float my_v = 0.f;
   int my_n = 0;
-  double my_p = 0.0, psum = 0.0;
+  constexpr int kNone = 1 << 24;  // slot of a lane with nothing left: expert >= 2^28
   for (int j = 0; j < k; ++j) {
+    // this lane's best: scanning down with >= leaves equal values to the
+    // lowest slot, i.e. the lowest expert
     float bv = -INFINITY;
-    int bn = 0x7fffffff;
+    int bi = kNone;
 #pragma unroll
-    for (int i = 0; i < SL; ++i) {
-      const int n = c + 16 * i;
-      if (n < N && !((taken >> i) & 1u) && (v[i] > bv || bn == 0x7fffffff)) {
-        bv = v[i];
-        bn = n;
-      }
+    for (int i = SL - 1; i >= 0; --i) {
+      const bool p = v[i] >= bv;
+      bv = p ? v[i] : bv;
+      bi = p ? i : bi;
     }
+    int bn = c + 16 * bi;
     argmax_step<kDppXor1>(bv, bn);
     argmax_step<kDppXor2>(bv, bn);
     argmax_step<kDppHalfMirror>(bv, bn);
     argmax_step<kDppMirror>(bv, bn);
-    if (bn < N && (bn & 15) == c) taken |= 1u << (bn >> 4);  // (rows past T keep no pick)
-    const double pj = exp((double)bv - md);
-    psum += pj;
-    if (c == j) {
-      my_v = bv;
-      my_n = bn;
-      my_p = pj;
-    }
+    // strike the pick out in its lane
+    const int q = (bn & 15) == c ? (bn >> 4) : -1;
+#pragma unroll
+    for (int i = 0; i < SL; ++i) v[i] = q == i ? __builtin_nanf("") : v[i];
+    my_v = c == j ? bv : my_v;
+    my_n = c == j ? bn : my_n;
   }
+  // The picks' unnormalised probabilities, then their sum in pick order: after
+  // k steps of "shift right one lane, add own", lane k-1 of the group holds
+  // (((p_0 + p_1) + p_2) + ...) + p_{k-1}.
+  const double my_p = exp((double)my_v - md);
+  double acc = 0.0;
+  for (int j = 0; j < k; ++j) acc = dpp_f64<kDppRowShr1>(acc) + my_p;
+  const double psum = __shfl(acc, (lane_id() & ~15) | (k - 1), kWave);
   if (active && c < k) {
     idx[(size_t)t * k + c] = my_n;
     w[(size_t)t * k + c] = (float)(my_p / psum);
@@ -564,6 +582,189 @@ __global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ l
   const int t = blockIdx.x * 16 + threadIdx.x / 16;
   const bool active = t < T;
   topk_row16x<SL>(logits + (size_t)(active ? t : 0) * N, active, N, k, t, idx, w, key);
+}
+
+// ---------------------------------------------------------------- wide router (64 < N <= 256)
+// Logits, softmax statistics, top-k, gates and keys of 64 tokens per block
+// for up to 256 experts (NP = 128 * NB, padded), in one launch. The block's
+// 8 waves share the 64 token rows, which stream through an LDS ring (64-wide K
+// stages, global_load_lds, rows of 128 bytes with the 16-byte chunk c of row r
+// at position c ^ ((r >> 1) & 7), so the fragment reads of 16 rows hit
+// distinct banks); wave w multiplies them against its own 16 * NB experts,
+// whose fragments come straight from W_g^T [NP, d] (K-contiguous,
+// L2-resident) into registers. Both are requested kWrLook stages ahead: every
+// block reads all of W_g^T from L2, and with only a stage or two in flight the
+// loop waits out the L2 latency at every stage. v_mfma_f32_16x16x32_bf16 with
+// the weight fragment as the A operand: each lane accumulates 4 consecutive
+// experts of one token. The finished logits tile goes to LDS (plus the bias),
+// then each 16-lane group runs topk_row16x on one token row: the same picks,
+// order and gates as the other router kernels, the fp64 softmax sum in the
+// 16-lane order.
+// ---------------------------------------------------------------- wide router (64 < N <= 256)
+// Logits, softmax statistics, top-k, gates and keys of 64 tokens per block
+// for up to 256 experts (NP = 128 * NB, padded), in one launch. Wave w of the
+// block's 8 owns experts 16*NB*w .. +16*NB for all 64 tokens. Everything
+// streams through LDS with global_load_lds in 64-wide K stages (rows of 128
+// bytes, the 16-byte chunk c of row r at position c ^ ((r >> 1) & 7), so the
+// fragment reads of 16 rows hit distinct banks):
+//   token rows : shared by the 8 waves (each copies 8 of the 64 rows), a
+//                kWrRingA-slot ring requested kWrLookA stages ahead (they
+//                come from HBM);
+//   weight rows: W_g^T [NP, d] (K-contiguous, L2-resident); each wave copies
+//                and reads only its own experts' rows, so these need no
+//                barrier, a kWrRingB-slot ring requested kWrLookB ahead.
+// v_mfma_f32_16x16x32_bf16 with the weight fragment as the A operand: each
+// lane accumulates 4 consecutive experts of one token. The finished logits
+// tile goes to LDS (plus the bias), then each 16-lane group runs the top-k of
+// one token row (topk_row16x): the same picks, order and gates as the other
+// router kernels, the fp64 softmax sum in the 16-lane order.
+constexpr int kWrTok = 64;   // tokens per block
+constexpr int kWrKS = 64;    // K per stage
+constexpr int kWrRowB = kWrKS * 2;
+constexpr int kWrLookA = 4, kWrRingA = 6;
+constexpr int kWrLookB = 2, kWrRingB = 3;
+template <int NB>
+__host__ __device__ constexpr size_t wide_router_lds() {
+  return (size_t)kWrRingA * kWrTok * kWrRowB + (size_t)kWrRingB * 128 * NB * kWrRowB;
+}
+
+template <int NB>
+__global__ __launch_bounds__(512) void router_wide_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ WgT, const float* __restrict__ bias,
+    int T, int d, int N, int k, float* __restrict__ logits, int32_t* __restrict__ idx,
+    float* __restrict__ w, double* __restrict__ key) {
+  constexpr int NP = 128 * NB;
+  constexpr int LDL = NP + 4;                    // logits tile row stride (floats)
+  constexpr int SLOT_A = kWrTok * kWrRowB;       // 8 KB
+  constexpr int WROWS = 16 * NB;                 // weight rows of one wave
+  constexpr int SLOT_B = 8 * WROWS * kWrRowB;    // all waves' rows of one stage
+  static_assert(kWrRingA >= kWrLookA + 1 && kWrRingB >= kWrLookB + 1, "slot reuse");
+  static_assert(kWrLookA >= kWrLookB, "token rows go out first");
+  static_assert((size_t)kWrTok * LDL * sizeof(float) <= wide_router_lds<NB>(),
+                "the logits tile reuses the rings");
+  extern __shared__ __align__(16) unsigned char wr_smem[];
+  MOE_LDS unsigned char* ldsp = (MOE_LDS unsigned char*)wr_smem;
+  const int l = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t0 = blockIdx.x * kWrTok;
+  const int nst = d / kWrKS;  // d % 64 == 0
+
+  // DMA lanes: lane l lands at row 8q + l/8 (q: the instruction), position
+  // l%8, which holds chunk (l%8) ^ ((row>>1)&7) of the row
+  const int drow = l >> 3;
+  // token rows 8*wv .. 8*wv+7
+  const int arow = 8 * wv + drow;
+  const unsigned char* asrc = (const unsigned char*)(x + (size_t)min(t0 + arow, T - 1) * d) +
+                              16 * ((l & 7) ^ ((arow >> 1) & 7));
+  // this wave's weight rows (experts e0 + r, r < WROWS), 8 per instruction
+  const int e0 = wv * WROWS;
+  const unsigned char* bsrc[2 * NB];
+#pragma unroll
+  for (int q = 0; q < 2 * NB; ++q) {
+    const int r = 8 * q + drow;
+    bsrc[q] = (const unsigned char*)(WgT + (size_t)(e0 + r) * d) + 16 * ((l & 7) ^ ((r >> 1) & 7));
+  }
+  // past the last stage the copies repeat it (dead data into a free slot)
+  auto issue_a = [&](int s) {
+    const int sc = s < nst ? s : nst - 1;
+    dma16(asrc + (size_t)sc * kWrRowB, ldsp + (s % kWrRingA) * SLOT_A + wv * 1024);
+  };
+  auto issue_b = [&](int s) {
+    const int sc = s < nst ? s : nst - 1;
+    MOE_LDS unsigned char* dst =
+        ldsp + kWrRingA * SLOT_A + (s % kWrRingB) * SLOT_B + wv * (WROWS * kWrRowB);
+#pragma unroll
+    for (int q = 0; q < 2 * NB; ++q) dma16(bsrc[q] + (size_t)sc * kWrRowB, dst + q * 1024);
+  };
+  // fragment reads: row 16b + (l&15), chunk 4h + (l>>4)
+  int aoff[4][2], boff[NB][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = 4 * h + (l >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * i + (l & 15);
+      aoff[i][h] = r * kWrRowB + 16 * (c ^ ((r >> 1) & 7));
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int r = 16 * j + (l & 15);
+      boff[j][h] = kWrRingA * SLOT_A + wv * (WROWS * kWrRowB) + r * kWrRowB +
+                   16 * (c ^ ((r >> 1) & 7));
+    }
+  }
+
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // Step j issues the token rows of stage j + kWrLookA, then the weight rows
+  // of stage j + kWrLookB; the prologue is steps -kWrLookA .. -1 of that
+  // pattern. At step s only what was issued after stage s's weight rows may
+  // still fly: the token rows of stage s + kWrLookA - 1 and the weight rows of
+  // stage s + 1 ... s + kWrLookB - 1, i.e. (kWrLookB - 1) steps of 1 + 2*NB
+  // operations (kWrLookB = 2: 1 + 2*NB).
+  for (int j = -kWrLookA; j < 0; ++j) {
+    issue_a(j + kWrLookA);
+    if (j + kWrLookB >= 0) issue_b(j + kWrLookB);
+  }
+  constexpr int kWait = (kWrLookB - 1) * (1 + 2 * NB);
+  static_assert(kWait < 64, "vmcnt range");
+  for (int s = 0; s < nst; ++s) {
+    // this wave's copies of stage s have landed; after the barrier every
+    // wave's token rows of stage s have, and every wave is done with stage
+    // s-1, whose token-row slot the copies below may reuse
+    vm_wait_n<kWait>();
+    wg_barrier();
+    issue_a(s + kWrLookA);
+    issue_b(s + kWrLookB);
+    const unsigned char* sa = wr_smem + (s % kWrRingA) * SLOT_A;
+    const unsigned char* sb = wr_smem + (s % kWrRingB) * SLOT_B;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 af[4], bf[NB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(sa + aoff[i][h]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bf[j] = *(const bf16x8*)(sb + boff[j][h]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    }
+  }
+  vm_wait_n<0>();  // the dead copies too
+  wg_barrier();    // no wave still reads the rings, which the tile now reuses
+
+  // logits tile (+ bias) into LDS: lane holds token 16i + (l&15), experts
+  // e0 + 16j + 4(l>>4) .. +3
+  float* Lt = (float*)wr_smem;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int r = 16 * i + (l & 15);
+      const int c = e0 + 16 * j + 4 * (l >> 4);
+      f32x4 v = acc[i][j];
+      if (bias != nullptr) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += c + q < N ? bias[c + q] : 0.f;
+      }
+      *(f32x4*)(Lt + r * LDL + c) = v;
+    }
+  __syncthreads();
+  // logits out: a wave per row, coalesced
+  for (int r = wv; r < kWrTok && t0 + r < T; r += 8)
+    for (int c = l; c < N; c += kWave) logits[(size_t)(t0 + r) * N + c] = Lt[r * LDL + c];
+  // top-k: a 16-lane group per row, 32 rows per pass of the block
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int r = pass * 32 + threadIdx.x / 16;
+    const int t = t0 + r;
+    topk_row16x<8 * NB>(Lt + r * LDL, t < T, N, k, t, idx, w, key);
+  }
 }
 
 // ---------------------------------------------------------------- bf16
@@ -831,6 +1032,21 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
       case 2: launch_skinny<2, false>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
       case 3: launch_skinny<3, false>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
       default: launch_skinny<4, false>(wide, x, WgT, bias, T, d, N, k, logits, idx, w, key, st); break;
+    }
+    return hipGetLastError();
+  }
+  if (NP <= 256 && d % kWrKS == 0) {
+    // up to 256 experts: logits and top-k of 64 tokens per block in one launch
+    if (NP <= 128) {
+      MOE_SET_LDS_ONCE(router_wide_kernel<1>, (int)wide_router_lds<1>());
+      hipLaunchKernelGGL(router_wide_kernel<1>, dim3(cdiv(T, kWrTok)), dim3(512),
+                         wide_router_lds<1>(), st, (const bf16*)x, WgT, bias, T, d, N, k, logits,
+                         idx, w, key);
+    } else {
+      MOE_SET_LDS_ONCE(router_wide_kernel<2>, (int)wide_router_lds<2>());
+      hipLaunchKernelGGL(router_wide_kernel<2>, dim3(cdiv(T, kWrTok)), dim3(512),
+                         wide_router_lds<2>(), st, (const bf16*)x, WgT, bias, T, d, N, k, logits,
+                         idx, w, key);
     }
     return hipGetLastError();
   }
