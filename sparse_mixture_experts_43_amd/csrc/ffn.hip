@@ -10,18 +10,23 @@
 // Models with Sparse Activation" page is what grouping slots by expert buys:
 // one dense GEMM per expert instead of per-token work.
 //
-// Three code paths, chosen on the host from sizes only (no device sync):
-//   tiled bf16  : grouped GEMM on v_mfma_f32_32x32x16_bf16, LDS double-buffered
-//                 tiles (BM x BN x 64), token gather fused into the A-tile load
-//                 of GEMM1, GELU fused into GEMM1's epilogue, bias and gate
-//                 fused into GEMM2's (fp32 output). Tiles come from a device-built schedule
-//                 (expert, n-tile, m-tile fastest) walked in an XCD-aware
-//                 order: each of the 8 XCDs takes one contiguous run of tiles
-//                 so m-tiles sharing a weight tile share that XCD's L2.
+// Code paths, chosen on the host from sizes only (no device sync, make_plan):
+//   tiled bf16  : the grouped GEMM of gemm_ring.h (K % 32 == 0):
+//                 v_mfma_f32_16x16x32_bf16 on an LDS ring filled by
+//                 global_load_lds, persistent workgroups walking an XCD-aware
+//                 tile list written by schedule_kernel (static shares with a
+//                 split K tail, or per-XCD work queues), token gather fused
+//                 into the copies of the first GEMM, GELU fused into its
+//                 epilogue, bias and gate into the second's (fp32 output);
+//                 256x256 tiles (eight waves of 128x64) for large experts
+//                 without capacity limit, 128x128 (four waves of 64x64)
+//                 otherwise. gemm_bf16_kernel below (32x32x16, register-staged
+//                 tiles) serves K % 32 != 0.
 //   decode bf16 : when an expert can hold at most 64 slots, weights are
-//                 streamed once with v_mfma_f32_16x16x32_bf16 (weight rows as
-//                 the 16-row operand, slots as the 16-column operand), 128-byte
-//                 row segments per 4 lanes.
+//                 streamed once by decode_dma_kernel (gemm_decode.h: weight
+//                 rows as the 16-row operand, slots as the 16-column operand,
+//                 LDS-DMA ring, split K with a fixed-order reduction), or by
+//                 decode_bf16_kernel below when K % 128 != 0.
 //   fp32        : FMA tiles (64 x 64), same schedule mechanism.
 // With the hidden-split flag, GEMM1 also stores the bf16 residual h - bf16(h)
 // of each hidden activation and GEMM2 runs a second MFMA on it, so GEMM2 sees
