@@ -38,7 +38,9 @@ PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 # sized for roughly 10-30 s of host work; routing always covers every token.
 CPU_SAMPLE = {"tiny_f32": 256, "switch_top1": 8192, "mixtral_prefill": 4096, "decode": 32,
               "fine_grained": 16384}
-DEFAULT_FLAGS = {"switch_top1": "split", "fine_grained": "split"}
+# Hidden layer per workload: the hi+lo pair where the plain bf16 hidden layer
+# misses 2e-2 x RMS(y) at full size (the fine-grained layer), plain bf16 elsewhere.
+DEFAULT_FLAGS = {"fine_grained": "split"}
 
 
 def log(msg):

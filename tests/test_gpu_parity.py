@@ -74,9 +74,10 @@ CASES = [
     ("many_experts_N1000", 512, 64, 64, 1000, 16, 1.0, "bf16", False, "none", 0),
 ]
 
-# Named workloads: hidden-split where the weight stream bounds the time and the
-# plain bf16 hidden layer cannot meet 2e-2 x RMS (heavy drops skew y).
-FULL = {"switch_top1": SPLIT, "decode": 0, "fine_grained": SPLIT, "mixtral_prefill": 0}
+# Named workloads in the configuration the benchmark times: the hi+lo hidden
+# layer where the plain bf16 one misses 2e-2 x RMS(y) (the fine-grained layer,
+# 82% of picks dropped), plain bf16 elsewhere.
+FULL = {"switch_top1": 0, "decode": 0, "fine_grained": SPLIT, "mixtral_prefill": 0}
 
 
 def _wl(c) -> Workload:
@@ -183,18 +184,21 @@ def test_parity_full_size(lib, name):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["switch_top1", "fine_grained"])
-def test_plain_bf16_full_size(lib, name):
-    """The library's default (plain bf16 hidden layer) at the two capacity-
-    limited workloads: routing bit-exact and every output element within the
-    arithmetic error bound of that path. Not held to 2e-2 x RMS(y): with most
+def test_other_hidden_full_size(lib, name):
+    """The other hidden-layer form at the two capacity-limited workloads: the
+    hi+lo pair at the Switch-style layer (held to 2e-2 x RMS(y)), the plain
+    bf16 layer at the fine-grained one (routing bit-exact, every element within
+    the arithmetic error bound, not held to 2e-2 x RMS(y): with 82% of the
     picks dropped, RMS(y) is small against the rows that keep a large gate, and
-    the hidden layer's bf16 rounding alone reaches that bar there (the measured
-    ratio is printed)."""
+    the hidden layer's bf16 rounding alone reaches that bar; the measured ratio
+    is recorded)."""
     from gpu_util import record, run_and_compare, say
-    res = run_and_compare(WORKLOADS[name], lib, flags=0, strict=False, check_compose=False)
-    say(f"[plain-bf16] {name} max|dy|/rms(y) = {res['y_err_over_rms']:.4e} "
-        f"(bar {res['strict_tol']:.0e})")
-    record("plain_bf16_full", name, res)
+    plain = FULL[name] == SPLIT
+    res = run_and_compare(WORKLOADS[name], lib, flags=0 if plain else SPLIT,
+                          strict=None if plain else True, check_compose=False)
+    say(f"[{'plain-bf16' if plain else 'hi+lo'}] {name} max|dy|/rms(y) = "
+        f"{res['y_err_over_rms']:.4e} (bar {res['strict_tol']:.0e})")
+    record("plain_bf16_full" if plain else "split_full", name, res)
 
 
 MISMATCH = [
