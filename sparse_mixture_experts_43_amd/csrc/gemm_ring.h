@@ -167,12 +167,15 @@ struct RingSplit {
 
 // Epilogue of one tile from the accumulators. Lane l holds, for token block i
 // and weight block j, token row (2i + wr)*16 + (l & 15) of the tile and the 4
-// consecutive output columns wn0 + 16j + 4*(l >> 4) + r (r = 0..3).
+// consecutive output columns wn0 + 16j + 4*(l >> 4) + r (r = 0..3). The
+// tile's gates (second expert GEMM) and biases are read from LDS, where the
+// kernel staged them (sh_gate[row], sh_bias[column - n0]); the logits mode
+// reads its fp32 bias from global memory.
 template <int BM, int BN, int WM, int WN, int MODE, bool SPLIT>
-__device__ __forceinline__ void ring_epilogue(const f32x4 (&acc)[WM / 16][WN / 16], int e, int m0,
-                                              int mcount, int n0, int wr, int wn0, int l,
-                                              const void* __restrict__ bias,
-                                              const float* __restrict__ gate, int Nout,
+__device__ __forceinline__ void ring_epilogue(const f32x4 (&acc)[WM / 16][WN / 16],
+                                              const float* sh_gate, const float* sh_bias,
+                                              int m0, int mcount, int n0, int wr, int wn0, int l,
+                                              const void* __restrict__ bias, int Nout,
                                               void* __restrict__ out, bf16* __restrict__ out_lo,
                                               int ldo) {
   constexpr bool G1 = MODE == kEpiGelu;
@@ -183,7 +186,7 @@ __device__ __forceinline__ void ring_epilogue(const f32x4 (&acc)[WM / 16][WN / 1
     if (r >= mcount) continue;
     const int slot = m0 + r;
     float g = 1.f;
-    if constexpr (MODE == kEpiGate) g = gate[slot];
+    if constexpr (MODE == kEpiGate) g = sh_gate[r];
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       const int col = n0 + wn0 + j * 16 + 4 * (l >> 4);
@@ -199,11 +202,11 @@ __device__ __forceinline__ void ring_epilogue(const f32x4 (&acc)[WM / 16][WN / 1
       }
       if (col >= Nout) continue;  // Nout % 4 == 0: a group is all in or all out
       if (bias != nullptr) {
-        const uint2 bb = *(const uint2*)((const bf16*)bias + (size_t)e * Nout + col);
-        v0 += __builtin_bit_cast(float, bb.x << 16);
-        v1 += __builtin_bit_cast(float, bb.x & 0xFFFF0000u);
-        v2 += __builtin_bit_cast(float, bb.y << 16);
-        v3 += __builtin_bit_cast(float, bb.y & 0xFFFF0000u);
+        const f32x4 bb = *(const f32x4*)(sh_bias + (col - n0));
+        v0 += bb[0];
+        v1 += bb[1];
+        v2 += bb[2];
+        v3 += bb[3];
       }
       const size_t o = (size_t)slot * Nout + col;
       if constexpr (G1) {
@@ -250,7 +253,10 @@ __device__ __forceinline__ void ring_decode_tile(int tile, const int4* __restric
 // capacity-limited layers, where it also lets a 3-slot ring (the split hidden
 // layer's extra token rows) keep one stage in flight with two workgroups per CU.
 template <int BM, int BN, int WM, int WN, int MODE, bool SPLIT, int RING, bool EARLY = false>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kernel(
+// Two waves per SIMD: at most 256 VGPRs (two 128x128 workgroups per CU, or
+// one 256x256 workgroup of eight waves).
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave)
+__attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ A_lo, const int32_t* __restrict__ perm,
     int kpairs, const bf16* __restrict__ W, const void* __restrict__ bias,
     const float* __restrict__ gate, const int4* __restrict__ tiles,
@@ -274,6 +280,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   static_assert(EARLY || RING >= 4, "the two-step copies need a stage of slack");
   static_assert(BM / WM == 2, "two wave rows (token blocks alternate between them)");
   static_assert(MT % 2 == 0, "token blocks are skipped in pairs");
+  static_assert(NTH >= BM && NTH >= BN, "one thread per staged gate / bias");
 
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -309,6 +316,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
   if (n_items == 0 && !dyn) return;
   const int base_tile = xcd * sp.chunk;
   __shared__ int sh_claim;
+  __shared__ __align__(16) float sh_gate[BM];  // the finished tile's gates (second expert GEMM)
+  __shared__ __align__(16) float sh_bias[BN];  // and biases by column, for its epilogue
   // no copy is in flight where this is called (the barriers wait for them)
   auto claim = [&]() -> int {
     __syncthreads();
@@ -570,9 +579,24 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
     }
     // all copies (the dead ones too) have landed: the ring is free
     vm_wait_n<0>();
+    // This tile's gates and biases, one per thread, go to LDS after the wait
+    // below: loaded now, before the next tile's copies go out (vmcnt retires
+    // in issue order, so a load issued after them would make the epilogue's
+    // stores wait for those copies), and held in one register each instead of
+    // per-lane copies live across the K loop.
+    float stg = 1.f, stb = 0.f;
+    if constexpr (MODE != kEpiLogit) {
+      const int tid = threadIdx.x;
+      if (ps < 0) {
+        if constexpr (MODE == kEpiGate)
+          if (tid < BM && tid < mcount) stg = gate[m0 + tid];
+        if (bias != nullptr && tid < BN && n0 + tid < Nout)
+          stb = (float)((const bf16*)bias)[(size_t)e * Nout + n0 + tid];
+      }
+    }
 
     // ---- next item: request its first stages before this item's epilogue
-    const int ce = e, cm0 = m0, cmcount = mcount, cn0 = n0, cps = ps;
+    const int cm0 = m0, cmcount = mcount, cn0 = n0, cps = ps;
     bool more;
     if (dyn) {
       const int c = claim();
@@ -588,6 +612,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
       more = it < n_items;
       if (more) item(it, tile, kb, ke, ps);
     }
+    // the gates and biases have landed before the next tile's copies go out
+    // (with the work queue the claim's round trip covers most of their
+    // latency); every wave finished reading the previous tile's values in its
+    // epilogue, before this tile's K loop barriers
+    vm_wait_n<0>();
+    if constexpr (MODE != kEpiLogit) {
+      if (threadIdx.x < BM) sh_gate[threadIdx.x] = stg;
+      if (threadIdx.x < BN) sh_bias[threadIdx.x] = stb;
+      wg_barrier();
+    }
     if (more) {
       nks = ke - kb;
       ring_decode_tile<MODE, BM, BN>(tile, tiles, M_total, Nout, e, m0, mcount, n0);
@@ -596,8 +630,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * kWave) void gemm_ring_kerne
     }
 
     if (cps < 0) {
-      ring_epilogue<BM, BN, WM, WN, MODE, SPLIT>(acc, ce, cm0, cmcount, cn0, wr, wn0, l, bias,
-                                                 gate, Nout, out, out_lo, ldo);
+      ring_epilogue<BM, BN, WM, WN, MODE, SPLIT>(acc, sh_gate, sh_bias, cm0, cmcount, cn0, wr,
+                                                 wn0, l, bias, Nout, out, out_lo, ldo);
     } else {
       // raw partial accumulators, one float4 per lane and block, lane-major
       // so every store is one contiguous 1 KB
