@@ -656,13 +656,16 @@ __global__ __launch_bounds__(512) void router_wide_kernel(
   const int arow = 8 * wv + drow;
   const unsigned char* asrc = (const unsigned char*)(x + (size_t)min(t0 + arow, T - 1) * d) +
                               16 * ((l & 7) ^ ((arow >> 1) & 7));
-  // this wave's weight rows (experts e0 + r, r < WROWS), 8 per instruction
+  // this wave's weight rows (experts e0 + r, r < WROWS), 8 per instruction;
+  // the transposed weight holds N rows rounded up to 16, so columns past N
+  // repeat row N-1 (their logits are never read)
   const int e0 = wv * WROWS;
   const unsigned char* bsrc[2 * NB];
 #pragma unroll
   for (int q = 0; q < 2 * NB; ++q) {
     const int r = 8 * q + drow;
-    bsrc[q] = (const unsigned char*)(WgT + (size_t)(e0 + r) * d) + 16 * ((l & 7) ^ ((r >> 1) & 7));
+    const int er = e0 + r < N ? e0 + r : N - 1;
+    bsrc[q] = (const unsigned char*)(WgT + (size_t)er * d) + 16 * ((l & 7) ^ ((r >> 1) & 7));
   }
   // past the last stage the copies repeat it (dead data into a free slot)
   auto issue_a = [&](int s) {
