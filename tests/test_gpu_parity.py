@@ -72,6 +72,9 @@ CASES = [
     ("single_token", 1, 64, 64, 8, 2, 0.0, "bf16", False, "none", 0),
     ("capacity_one", 64, 64, 64, 8, 2, 0.01, "bf16", False, "zipf1.1", 0),
     ("many_experts_N1000", 512, 64, 64, 1000, 16, 1.0, "bf16", False, "none", 0),
+    # the one-kernel wide router with fewer than 64 experts (columns padded to
+    # 128; W_g too large to stage in LDS) and a ragged last block of 64 tokens
+    ("wide_router_N40", 4100, 1408, 64, 40, 3, 1.0, "bf16", False, "normal0.5", 0),
 ]
 
 # Named workloads in the configuration the benchmark times: the hi+lo hidden
