@@ -249,11 +249,24 @@ def measure_extras(moe, torch, w, dv, ws, y, flags):
     for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
-    tg0 = time.perf_counter()
-    for _ in range(nx):
-        g.replay()
-    torch.cuda.synchronize()
-    graph_ms = (time.perf_counter() - tg0) * 1e3 / nx
+    # eager and graph blocks alternate (two of each): the clock drifts over a
+    # run by a few percent, which a single graph block timed after the others
+    # would read as a graph cost
+    blk = {"eager": [], "graph": []}
+    for _ in range(2):
+        for mode in ("eager", "graph"):
+            tg0 = time.perf_counter()
+            for _ in range(nx):
+                if mode == "graph":
+                    g.replay()
+                else:
+                    moe.moe_forward(dv["x"], dv["W_g"], dv["logit_bias"], dv["W1"], dv["b1"],
+                                    dv["W2"], dv["b2"], w.k, w.capacity_factor, workspace=ws, y=y,
+                                    flags=flags)
+            torch.cuda.synchronize()
+            blk[mode].append((time.perf_counter() - tg0) * 1e3 / nx)
+    graph_ms = sum(blk["graph"]) / 2
+    eager_alt_ms = sum(blk["eager"]) / 2
     del g
     C = moe.moe_capacity(w.T, w.N, w.k, w.capacity_factor)
     extras = {"routing_stats_us": stats_us, "aux_balance": float(st_h[2 * w.N]),
@@ -265,18 +278,20 @@ def measure_extras(moe, torch, w, dv, ws, y, flags):
               "shared_expert_tflops": sh_tflops,
               "with_shared_expert_ms_per_step": ss_ms,
               "graph_replay_ms_per_step": graph_ms,
+              "eager_ms_per_step_beside_graph": eager_alt_ms,
               "note": "after the timed steps; moe_routing_stats averaged over 20 calls, the layer "
                       "with first-come capacity + survivor renormalisation + identity fallback "
                       "over 20 steps, with expert-choice routing (every expert takes "
                       "min(C, T) tokens) over 20 steps, a shared expert of width d_ff on every "
                       "token alone (HIP events, 20 calls; TFLOP/s = 4 T d d_ff / time) and "
                       "added to the layer (20 steps), and the plain step captured in a HIP "
-                      "graph and replayed (20 replays)"}
+                      "graph and replayed, in two blocks of 20 replays alternating with two blocks of "
+                      "20 eager steps (both averaged: the same clock conditions)"}
     log(f"extras: routing stats {stats_us:.1f}us, aux {extras['aux_balance']:.4f}, "
         f"all drop policies {pol_ms:.3f} ms/step, expert choice {ec_ms:.3f} ms/step "
         f"({extras['expert_choice_slots']} slots), shared expert {sh_ms:.3f} ms "
         f"({sh_tflops:.0f} TFLOP/s), layer + shared expert {ss_ms:.3f} ms/step, "
-        f"graph replay {graph_ms:.3f} ms/step")
+        f"graph replay {graph_ms:.3f} ms/step (eager beside it {eager_alt_ms:.3f})")
     return extras
 
 
