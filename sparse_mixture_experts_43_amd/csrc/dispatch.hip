@@ -443,6 +443,9 @@ __device__ __forceinline__ void select_body(
   int& sh_cnt = shm.cnt;
   const int tid = threadIdx.x;
   const int l = lane_id(), wv = tid / kWave;
+  // the keys (into LDS when they fit) and their block min and max, whose
+  // common prefix every key shares
+  unsigned long long mn = ~0ull, mx = 0ull;
   if constexpr (LDSC) {
     for (int i0 = 0; i0 < n; i0 += 4 * kScanThreads) {
       unsigned long long v[4];
@@ -454,19 +457,21 @@ __device__ __forceinline__ void select_body(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = i0 + q * kScanThreads + tid;
-        if (i < n) sc[i] = v[q];
+        if (i < n) {
+          sc[i] = v[q];
+          mn = v[q] < mn ? v[q] : mn;
+          mx = v[q] > mx ? v[q] : mx;
+        }
       }
+    }
+  } else {
+    for (int i = tid; i < n; i += kScanThreads) {
+      const unsigned long long u = codes[base + i];
+      mn = u < mn ? u : mn;
+      mx = u > mx ? u : mx;
     }
   }
   auto code = [&](int i) -> unsigned long long { return LDSC ? sc[i] : codes[base + i]; };
-
-  // common prefix of all keys: block min and max
-  unsigned long long mn = ~0ull, mx = 0ull;
-  for (int i = tid; i < n; i += kScanThreads) {
-    const unsigned long long u = code(i);
-    mn = u < mn ? u : mn;
-    mx = u > mx ? u : mx;
-  }
 #pragma unroll
   for (int off2 = 32; off2 > 0; off2 >>= 1) {
     const unsigned long long a = __shfl_xor(mn, off2, kWave), b2 = __shfl_xor(mx, off2, kWave);
@@ -551,32 +556,25 @@ __device__ __forceinline__ void select_body(
   }
   // prefix = threshold code U; keep codes > U, and the first `want` codes == U.
   // Each wave takes a contiguous segment of the expert's requests (token
-  // order), its lanes consecutive elements, ranks from ballot prefixes.
+  // order), its lanes consecutive elements, ranks from ballot prefixes. A
+  // wave keeps all its codes > U and, of its codes == U, as many as the
+  // `want` left after the equal codes of the waves before it.
   const unsigned long long U = prefix;
   const int seg = ((n + kSelWaves - 1) / kSelWaves + kWave - 1) / kWave * kWave;
   const int s_beg = wv * seg, s_end = min(n, s_beg + seg);
   const unsigned long long lt = lanemask_lt();
-  int n_eq = 0;
+  int n_eq = 0, n_gt = 0;
   for (int i0 = s_beg; i0 < s_end; i0 += kWave) {
     const int i = i0 + l;
-    n_eq += __popcll(__ballot(i < s_end && code(i) == U));
+    const unsigned long long u = i < s_end ? code(i) : 0ull;
+    n_eq += __popcll(__ballot(i < s_end && u == U));
+    n_gt += __popcll(__ballot(i < s_end && u > U));
   }
   int tot;
   const int eq_before = block_scan_excl(l == 0 ? n_eq : 0, tmp, &tot);
   const int eq_w = __shfl(eq_before, 0, kWave);  // equal keys before this wave's segment
-  int n_kept = 0;
-  {
-    int r = eq_w;
-    for (int i0 = s_beg; i0 < s_end; i0 += kWave) {
-      const int i = i0 + l;
-      const unsigned long long u = i < s_end ? code(i) : 0ull;
-      const unsigned long long eqm = __ballot(i < s_end && u == U);
-      const bool keep = i < s_end && (u > U || (u == U && r + __popcll(eqm & lt) < want));
-      n_kept += __popcll(__ballot(keep));
-      r += __popcll(eqm);
-    }
-  }
-  const int kept_before = block_scan_excl(l == 0 ? n_kept : 0, tmp, &tot);
+  const int eq_keep = want - eq_w < 0 ? 0 : (want - eq_w > n_eq ? n_eq : want - eq_w);
+  const int kept_before = block_scan_excl(l == 0 ? n_gt + eq_keep : 0, tmp, &tot);
   {
     int r = eq_w;
     int ks = o + __shfl(kept_before, 0, kWave);
@@ -596,11 +594,20 @@ __device__ __forceinline__ void select_body(
       const unsigned long long eqm = __ballot(in && u == U);
       const bool keep = in && (u > U || (u == U && r + __popcll(eqm & lt) < want));
       const unsigned long long km = __ballot(keep);
-      if (keep) write_slot(perm, inv, gate, w, p, ks + __popcll(km & lt));
+      if (keep) {
+        const int slot = ks + __popcll(km & lt);
+        perm[slot] = p;
+        inv[p] = slot;
+      }
       ks += __popcll(km);
       r += __popcll(eqm);
     }
   }
+  // The kept slots' gates after the loop (one batch of weight loads, not one
+  // dependent load per iteration): the expert keeps exactly C pairs, in
+  // slots o .. o + C - 1, whose perm entries this block has just written.
+  __syncthreads();
+  for (int sl = o + tid; sl < o + C; sl += kScanThreads) gate[sl] = w[perm[sl]];
 }
 
 __global__ __launch_bounds__(kScanThreads) void select_kernel(
