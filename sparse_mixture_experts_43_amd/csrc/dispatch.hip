@@ -171,7 +171,12 @@ __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
   const int p0 = min(P, wv * span), p1 = min(P, p0 + span);
   for (int e = l; e < N; e += kWave) my[e] = 0;
   __syncthreads();
-  walk_pairs(sid, p0, p1, N, my, [](int, int, int) {});
+  // this wave's requests per expert (order-free: one LDS add per pair on the
+  // wave's own counters; the positions below follow pair order)
+  for (int p = p0 + l; p < p1; p += kWave) {
+    const int e = sid[p];
+    if (e >= 0) atomicAdd(&my[e], 1);
+  }
   if (threadIdx.x == 0) carry[0] = carry[1] = 0;
   __syncthreads();
   // per expert: totals, bases across waves, expert offsets
@@ -241,31 +246,15 @@ __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
         }
       }
     } else {
-      unsigned long long cv[kBatch];
-      int ev[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int p = q0 + u * kScanThreads + (int)threadIdx.x;
-        const bool live = sv[u] >= 0;
-        cv[u] = live ? rank_code(key, p, fc_k) : 0ull;
-        ev[u] = live ? idx[p] : 0;
-      }
+      // the pairs in bucket order only: the selection that follows computes
+      // their rank codes from `key` and writes inv for every pair it sees
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int p = q0 + u * kScanThreads + (int)threadIdx.x;
         if (p >= P) continue;
         const int s = sv[u];
-        if (s < 0) {
-          inv[p] = -1;
-          continue;
-        }
-        bucket[s] = p;
-        codes[s] = cv[u];
-        // a pair of an expert over capacity starts dropped; the selection
-        // writes only the kept ones
-        const int e = ev[u];
-        const int r = (e + 1 < N ? sh_reqoff[e + 1] : carry[0]) - sh_reqoff[e];
-        if (r > C) inv[p] = -1;
+        if (s < 0) inv[p] = -1;
+        else bucket[s] = p;
       }
     }
   }
@@ -428,12 +417,18 @@ struct SelShared {
   int dig, want, cnt;
 };
 
+// codes == nullptr: the rank codes are computed from the pairs' keys
+// (rank_code of bucket[i]) instead of read.
 template <bool LDSC>
 __device__ __forceinline__ void select_body(
     const int32_t* __restrict__ bucket, const unsigned long long* __restrict__ codes,
+    const double* __restrict__ key, int fc_k,
     const float* __restrict__ w, int n, int base, int o, int C, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, float* __restrict__ gate, unsigned long long* __restrict__ sc,
     SelShared& shm) {
+  auto gcode = [&](int i) -> unsigned long long {
+    return codes != nullptr ? codes[base + i] : rank_code(key, bucket[base + i], fc_k);
+  };
   int* tmp = shm.tmp;
   int* hist = shm.hist;
   unsigned long long* list = shm.list;
@@ -452,7 +447,7 @@ __device__ __forceinline__ void select_body(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = i0 + q * kScanThreads + tid;
-        v[q] = i < n ? codes[base + i] : 0ull;
+        v[q] = i < n ? gcode(i) : 0ull;
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -466,12 +461,12 @@ __device__ __forceinline__ void select_body(
     }
   } else {
     for (int i = tid; i < n; i += kScanThreads) {
-      const unsigned long long u = codes[base + i];
+      const unsigned long long u = gcode(i);
       mn = u < mn ? u : mn;
       mx = u > mx ? u : mx;
     }
   }
-  auto code = [&](int i) -> unsigned long long { return LDSC ? sc[i] : codes[base + i]; };
+  auto code = [&](int i) -> unsigned long long { return LDSC ? sc[i] : gcode(i); };
 #pragma unroll
   for (int off2 = 32; off2 > 0; off2 >>= 1) {
     const unsigned long long a = __shfl_xor(mn, off2, kWave), b2 = __shfl_xor(mx, off2, kWave);
@@ -598,6 +593,10 @@ __device__ __forceinline__ void select_body(
         const int slot = ks + __popcll(km & lt);
         perm[slot] = p;
         inv[p] = slot;
+      } else if (in && codes == nullptr) {
+        // dropped by the capacity limit (the bucketing kernels of the
+        // multi-block path mark these pairs themselves, in parallel)
+        inv[p] = -1;
       }
       ks += __popcll(km);
       r += __popcll(eqm);
@@ -612,6 +611,7 @@ __device__ __forceinline__ void select_body(
 
 __global__ __launch_bounds__(kScanThreads) void select_kernel(
     const int32_t* __restrict__ bucket, const unsigned long long* __restrict__ codes,
+    const double* __restrict__ key, int fc_k,
     const float* __restrict__ w, const int32_t* __restrict__ req,
     const int32_t* __restrict__ reqoff, const int32_t* __restrict__ off, int C,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, float* __restrict__ gate) {
@@ -627,9 +627,9 @@ __global__ __launch_bounds__(kScanThreads) void select_kernel(
   }
   __shared__ SelShared shm;
   if (n <= kSelLds)
-    select_body<true>(bucket, codes, w, n, base, o, C, perm, inv, gate, sel_codes, shm);
+    select_body<true>(bucket, codes, key, fc_k, w, n, base, o, C, perm, inv, gate, sel_codes, shm);
   else
-    select_body<false>(bucket, codes, w, n, base, o, C, perm, inv, gate, nullptr, shm);
+    select_body<false>(bucket, codes, key, fc_k, w, n, base, o, C, perm, inv, gate, nullptr, shm);
 }
 
 // ------------------------------------------------------------ survivor renormalisation
@@ -703,8 +703,10 @@ hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key
     const int nmax = T < kSelLds ? T : kSelLds;
     const size_t lds = (size_t)nmax * sizeof(unsigned long long);
     MOE_SET_LDS_ONCE(select_kernel, 160 * 1024);
-    hipLaunchKernelGGL(select_kernel, dim3(N), dim3(kScanThreads), lds, st, s.bucket, s.codes, w,
-                       req, s.reqoff, off, C, perm, inv, gate);
+    // (the fused path leaves the rank codes to the selection)
+    hipLaunchKernelGGL(select_kernel, dim3(N), dim3(kScanThreads), lds, st, s.bucket,
+                       fused ? nullptr : s.codes, key, fc_k, w, req, s.reqoff, off, C, perm, inv,
+                       gate);
   }
   // nothing can drop when C >= T: the weights stay as they are
   if ((flags & kFlagRenorm) && can_drop)
