@@ -555,6 +555,8 @@ __device__ __forceinline__ void select_body(
   // wave keeps all its codes > U and, of its codes == U, as many as the
   // `want` left after the equal codes of the waves before it.
   const unsigned long long U = prefix;
+  const bool stage = C <= 2 * kSelList;  // kept pair ids gathered in the candidate list
+  int* kept_p = (int*)list;
   const int seg = ((n + kSelWaves - 1) / kSelWaves + kWave - 1) / kWave * kWave;
   const int s_beg = wv * seg, s_end = min(n, s_beg + seg);
   const unsigned long long lt = lanemask_lt();
@@ -591,8 +593,13 @@ __device__ __forceinline__ void select_body(
       const unsigned long long km = __ballot(keep);
       if (keep) {
         const int slot = ks + __popcll(km & lt);
-        perm[slot] = p;
         inv[p] = slot;
+        if (stage) {
+          kept_p[slot - o] = p;
+        } else {
+          perm[slot] = p;
+          gate[slot] = w[p];
+        }
       } else if (in && codes == nullptr) {
         // dropped by the capacity limit (the bucketing kernels of the
         // multi-block path mark these pairs themselves, in parallel)
@@ -602,11 +609,20 @@ __device__ __forceinline__ void select_body(
       r += __popcll(eqm);
     }
   }
-  // The kept slots' gates after the loop (one batch of weight loads, not one
-  // dependent load per iteration): the expert keeps exactly C pairs, in
-  // slots o .. o + C - 1, whose perm entries this block has just written.
-  __syncthreads();
-  for (int sl = o + tid; sl < o + C; sl += kScanThreads) gate[sl] = w[perm[sl]];
+  // The expert keeps exactly C pairs, in slots o .. o + C - 1. When C fits
+  // the (by now unused) candidate list, the kept pair ids were gathered there
+  // and perm and the gates are written after the loop: coalesced stores and
+  // one batch of weight loads instead of a dependent load per iteration. (Not
+  // read back from perm: global memory written by this kernel can be stale in
+  // the CU's L1, which workgroups that ran there earlier may have filled.)
+  if (stage) {
+    __syncthreads();
+    for (int i = tid; i < C; i += kScanThreads) {
+      const int p = kept_p[i];
+      perm[o + i] = p;
+      gate[o + i] = w[p];
+    }
+  }
 }
 
 __global__ __launch_bounds__(kScanThreads) void select_kernel(
