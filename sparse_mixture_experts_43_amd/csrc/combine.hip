@@ -54,25 +54,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
   const int32_t* it = inv + (size_t)t * k;
   bool any = false;
-  // picks in groups of 4: all slot indices first, then every kept pick's row
-  // load issued before the first add (more loads in flight), then the sums in
-  // fixed pick order
-  for (int j0 = 0; j0 < k; j0 += 4) {
-    int s[4];
+  // picks in groups of 8 (all of them for k <= 8): the slot indices first,
+  // then every kept pick's row load issued before the first add (one round
+  // trip per group), then the sums in fixed pick order
+  constexpr int G = 8;
+  for (int j0 = 0; j0 < k; j0 += G) {
+    int s[G];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < G; ++q) {
       s[q] = j0 + q < k ? it[j0 + q] : -1;
       any |= s[q] >= 0;
     }
-    f32x4 v[4][V / 4];
+    f32x4 v[G][V / 4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < G; ++q) {
       const f32x4* src = (const f32x4*)(slot_out + (size_t)(s[q] < 0 ? 0 : s[q]) * d + c);
 #pragma unroll
       for (int h = 0; h < V / 4; ++h) v[q][h] = s[q] >= 0 ? src[h] : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < G; ++q) {
       if (s[q] < 0) continue;
 #pragma unroll
       for (int h = 0; h < V / 4; ++h)
