@@ -206,8 +206,14 @@ def run_and_compare(w: Workload, lib, check_compose=True, seed=None, inputs=None
     res = {}
 
     # the activation-dtype output is the fp32 output rounded once (RNE)
-    assert torch.equal(y_act.view(torch.uint8), y32.to(y_act.dtype).view(torch.uint8)), \
-        "activation-dtype output is not the rounded fp32 output"
+    if not torch.equal(y_act.view(torch.uint8), y32.to(y_act.dtype).view(torch.uint8)):
+        bad = (y_act.view(torch.uint8) != y32.to(y_act.dtype).view(torch.uint8)).view(T, -1)
+        rows = bad.any(1).nonzero().flatten()
+        r0 = int(rows[0])
+        raise AssertionError(
+            f"activation-dtype output is not the rounded fp32 output: {int(rows.numel())} rows "
+            f"differ, first row {r0} (inv {ex['inv'][r0].tolist()}): fp32 "
+            f"{y32[r0, :4].tolist()} vs {y_act[r0, :4].float().tolist()}")
 
     # logits: bit-identical between forward and route, within 1e-5 of the oracle
     assert torch.equal(ex["logits"], logits), "forward and moe_route logits differ"
