@@ -113,6 +113,13 @@ extern "C" {
  * pairs not taken. Not combinable with FIRST_COME / RENORM_SURVIVORS or a
  * topk_idx_opt output. */
 #define MOE_FLAG_EXPERT_CHOICE 32
+/* W1 and W2 (moe_forward, moe_forward_noalloc, moe_expert_ffn) are in the
+ * packed layout written by moe_pack_weights. bf16 only, d and d_ff multiples
+ * of 128; else MOE_ERR_UNSUPPORTED. The results are bit-identical to the same
+ * call with the unpacked weights: only the order of the bytes in memory
+ * changes, so that the expert GEMMs read each weight tile stage as one
+ * contiguous kilobyte instead of 64 bytes from each of 16 rows. */
+#define MOE_FLAG_PACKED_WEIGHTS 64
 
 /* Library ABI version (major*100 + minor). */
 int moe_version(void);
@@ -222,8 +229,8 @@ int moe_dispatch(const int32_t* topk_idx, const float* topk_w, const double* top
  *          slot_out[s] = slot_gate[s] * (W2[e] GELU(W1[e] x[t] + b1[e]) + b2[e])
  *        (hidden activations are rounded to the activation dtype; the
  *        gate-scaled outputs stay fp32 so that only y is rounded once more).
- * flags: MOE_FLAG_HIDDEN_SPLIT is honoured (bf16); MOE_FLAG_Y_F32 has no
- * effect here. T, k, capacity_factor bound S (S <= min(T*k, N*C)) for launch
+ * flags: MOE_FLAG_HIDDEN_SPLIT (bf16) and MOE_FLAG_PACKED_WEIGHTS are honoured;
+ * MOE_FLAG_Y_F32 has no effect here. T, k, capacity_factor bound S (S <= min(T*k, N*C)) for launch
  * sizing: perm, offsets and slot_gate must come from moe_dispatch called with
  * the same T, N, k and capacity_factor. With other offsets the kernels clamp
  * each expert's rows to C and all rows to min(T*k, N*C), so every access
@@ -235,6 +242,23 @@ int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
                    const void* W1, const void* b1, const void* W2, const void* b2,
                    int T, int d, int d_ff, int N, int k, double capacity_factor, int dtype,
                    int flags, void* slot_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Expert weights in the packed layout of MOE_FLAG_PACKED_WEIGHTS, written once
+ * (at load time) and then passed to the FFN entry points with that flag. The
+ * operation is a reordering only (no arithmetic; the pages' FFN of page "Mixture
+ * of Experts (MoE): Architecture, Routing, and Scaling", "Core Architecture",
+ * is unchanged).
+ *   in : W [N, rows, K] bf16, row-major (W1: rows = d_ff, K = d; W2: rows = d,
+ *        K = d_ff), 16-byte aligned
+ *   out: W_packed, the same N*rows*K*2 bytes, caller-owned, 16-byte aligned,
+ *        not overlapping W: for each expert e, row block rb (16 rows) and K
+ *        chunk kc (32 values) a 1 KB piece at byte
+ *        ((e*rows/16 + rb)*K/32 + kc)*1024 whose 16-byte word w holds the 8
+ *        values W[e][rb*16 + w/4][kc*32 + 8*((w%4) ^ ((w/16)%4)) ..+8].
+ * dtype must be MOE_BF16, rows % 16 == 0 and K % 128 == 0
+ * (MOE_ERR_UNSUPPORTED otherwise). Asynchronous on `stream`; no workspace. */
+int moe_pack_weights(const void* W, int N, int rows, int K, int dtype, void* W_packed,
+                     void* stream);
 
 /* Step 7 (wiki page, step 7; weighted combine of the pseudocode).
  *   in : slot_out [T*k, d] fp32 (already gate-scaled), inv [T*k]; x [T,d] in

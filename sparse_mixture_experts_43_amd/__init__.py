@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     MOE_FLAG_FIRST_COME,
     MOE_FLAG_HIDDEN_SPLIT,
     MOE_FLAG_IDENTITY_FALLBACK,
+    MOE_FLAG_PACKED_WEIGHTS,
     MOE_FLAG_RENORM_SURVIVORS,
     MOE_FLAG_Y_F32,
     MOE_NOALLOC_SCRATCH_BYTES,
@@ -24,6 +25,7 @@ from ._lib import (  # noqa: F401
     moe_expert_ffn,
     moe_forward,
     moe_forward_noalloc,
+    moe_pack_weights,
     moe_route,
     moe_routing_stats,
     moe_set_profile_events,

@@ -25,6 +25,7 @@ MOE_FLAG_FIRST_COME = 4
 MOE_FLAG_RENORM_SURVIVORS = 8
 MOE_FLAG_IDENTITY_FALLBACK = 16
 MOE_FLAG_EXPERT_CHOICE = 32
+MOE_FLAG_PACKED_WEIGHTS = 64
 
 _c_int, _c_size, _c_double, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_double, ctypes.c_void_p
 
@@ -65,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "moe_shared_workspace_bytes": (_c_size, [_c_int] * 4),
         "moe_shared_expert": (_c_int, [_vp] * 5 + [_c_int] * 5 + [_vp] + [_vp, _c_size, _vp]),
         "moe_set_profile_events": (_c_int, [ctypes.POINTER(_vp), _c_int]),
+        "moe_pack_weights": (_c_int, [_vp] + [_c_int] * 4 + [_vp, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -79,7 +81,7 @@ EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_capacity",
             "moe_workspace_bytes", "moe_route", "moe_routing_stats", "moe_dispatch",
             "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc",
             "moe_set_profile_events",
-            "moe_shared_workspace_bytes", "moe_shared_expert")
+            "moe_shared_workspace_bytes", "moe_shared_expert", "moe_pack_weights")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -170,6 +172,21 @@ def moe_route(x: torch.Tensor, W_g: torch.Tensor, logit_bias: Optional[torch.Ten
                         workspace.numel(), _stream(dev))
     _raise(st, "moe_route")
     return logits, idx, w, key
+
+
+def moe_pack_weights(W: torch.Tensor) -> torch.Tensor:
+    """Expert weights W [N, rows, K] (bf16) in the packed layout that the FFN
+    entry points read with MOE_FLAG_PACKED_WEIGHTS: a new tensor of the same
+    shape and dtype whose bytes are reordered (see include/moe.h)."""
+    dev = W.device
+    if W.dim() != 3:
+        raise ValueError(f"W must be [N, rows, K], got shape {tuple(W.shape)}")
+    _check(W, "W", dev, torch.bfloat16)
+    N, rows, K = W.shape
+    out = torch.empty_like(W)
+    st = _lib.moe_pack_weights(_ptr(W), N, rows, K, MOE_BF16, _ptr(out), _stream(dev))
+    _raise(st, "moe_pack_weights")
+    return out
 
 
 def moe_routing_stats(logits: torch.Tensor, topk_idx: torch.Tensor,

@@ -517,6 +517,7 @@ struct Plan {
   bool dma1, dma2; // decode GEMMs on the LDS-DMA stream kernel
   int xg;          // decode: 16-slot groups an expert can hold (capacity / 16, rounded up to 1, 2, 4)
   int cap;         // slots an expert can hold: min(C, T)
+  bool packed;     // W1 and W2 in the packed piece layout (moe_pack_weights)
 };
 
 // Split-K factor for a decode GEMM: enough blocks to cover the CUs a few times.
@@ -540,6 +541,7 @@ Plan make_plan(int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype
   const int Ccap = C < T ? C : T;
   p.cap = Ccap;
   p.split = dtype == kBF16 && (flags & kFlagHiddenSplit);
+  p.packed = dtype == kBF16 && (flags & kFlagPacked);
   if (dtype == kF32) {
     p.path = kPathF32;
     p.BM = 64; p.BN1 = 64; p.BN2 = 64;
@@ -600,7 +602,7 @@ template <int BM, int BN, int WM, int WN, bool G1, bool SPLIT>
 void launch_gemm(const bf16* A, const bf16* A_lo, const int32_t* perm, int k, const bf16* W,
                  const bf16* bias, const float* gate, const int4* tl, const int32_t* cnt, int K,
                  int Nout, int grid, void* out, bf16* out_lo, float* part, hipStream_t st,
-                 int* wq = nullptr) {
+                 int* wq, bool packed) {
   constexpr int NTH = (BM / WM) * (BN / WN) * kWave;
   constexpr bool ALO = SPLIT && !G1;
   if (K % kRK == 0) {
@@ -615,7 +617,8 @@ void launch_gemm(const bf16* A, const bf16* A_lo, const int32_t* perm, int k, co
     pgrid = pgrid < bound ? pgrid : bound;
     hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, R, EARLY>), dim3(pgrid),
                        dim3(NTH), lds, st, A, A_lo, perm, k, W, (const void*)bias, gate, tl, cnt, K,
-                       Nout, out, out_lo, 0, 0, wq != nullptr ? nullptr : part, wq);
+                       Nout, out, out_lo, 0, 0, wq != nullptr ? nullptr : part, wq,
+                       packed ? 1 : 0);
     if (part != nullptr && wq == nullptr) {
       // at most per-1 tail tiles per XCD, BM*BN/4/256 group blocks each
       const int work = 8 * (pgrid / 8) * (BM * BN / 4 / kReduceThreads);
@@ -649,11 +652,12 @@ hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, c
   profile_mark(3, st);
   launch_gemm<BM, BN, WM, WN, true, SPLIT>((const bf16*)x, nullptr, perm, k, (const bf16*)W1,
                                            (const bf16*)b1, nullptr, t1, cnts + 0, d, d_ff, g1,
-                                           hid, hid_lo, part, st, wq1);
+                                           hid, hid_lo, part, st, wq1, pl.packed);
   profile_mark(4, st);
   launch_gemm<BM, BN, WM, WN, false, SPLIT>((const bf16*)hid, hid_lo, nullptr, k,
                                             (const bf16*)W2, (const bf16*)b2, gate, t2, cnts + 1,
-                                            d_ff, d, g2, slot_out, nullptr, part, st, wq2);
+                                            d_ff, d, g2, slot_out, nullptr, part, st, wq2,
+                                            pl.packed);
   profile_mark(5, st);
   return hipGetLastError();
 }
@@ -662,7 +666,7 @@ template <bool G1, bool SPLIT, int XG, int KC>
 void launch_decode_dma(int nsplit, const bf16* X, const bf16* X_lo, const int32_t* perm, int k,
                        const int32_t* off, const bf16* W, const bf16* bias, const float* gate,
                        int K, int Nout, int N, void* out, bf16* out_lo, float* part, int S_cap,
-                       int cap, hipStream_t st, bool reduce) {
+                       int cap, hipStream_t st, bool reduce, bool packed) {
   constexpr int RING = decode_ring(XG, SPLIT && !G1, KC);
   using Geo = DecodeGeom<G1, SPLIT, XG, RING, KC>;
   const int nb = cdiv(Nout, kDWRows);
@@ -671,7 +675,7 @@ void launch_decode_dma(int nsplit, const bf16* X, const bf16* X_lo, const int32_
                              Geo::LDS, N * nb * nsplit);
   hipLaunchKernelGGL((decode_dma_kernel<G1, SPLIT, XG, RING, KC>), dim3(grid), dim3(256), Geo::LDS,
                      st, X, X_lo, perm, k, off, W, bias, gate, K, Nout, nb, nsplit, out, out_lo,
-                     part, S_cap, cap, N);
+                     part, S_cap, cap, N, packed ? 1 : 0);
   if (nsplit > 1 && reduce)
     hipLaunchKernelGGL((decode_reduce_kernel<G1, SPLIT>), dim3(N * nb), dim3(256), 0, st, part,
                        nsplit, S_cap, cap < 16 * XG ? cap : 16 * XG, off, bias, gate, Nout, nb,
@@ -685,26 +689,28 @@ void launch_decode_gemm(bool dma, int nsplit, int xg, const bf16* X, const bf16*
                         const int32_t* perm, int k, const int32_t* off, const bf16* W,
                         const bf16* bias, const float* gate, int K, int Nout, int N, void* out,
                         bf16* out_lo, float* part, int S_cap, int cap, hipStream_t st,
-                        bool reduce = true) {
+                        bool reduce, bool packed) {
   if (dma) {
     // the first GEMM (shorter K) streams better in 512-byte row chunks, one
     // workgroup per CU; the second in 256-byte chunks, two per CU (measured)
     if (G1 && K % 256 == 0 && xg <= 2) {
       if (xg <= 1)
         launch_decode_dma<G1, SPLIT, 1, 256>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K,
-                                             Nout, N, out, out_lo, part, S_cap, cap, st, reduce);
+                                             Nout, N, out, out_lo, part, S_cap, cap, st, reduce,
+                                             packed);
       else
         launch_decode_dma<G1, SPLIT, 2, 256>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K,
-                                             Nout, N, out, out_lo, part, S_cap, cap, st, reduce);
+                                             Nout, N, out, out_lo, part, S_cap, cap, st, reduce,
+                                             packed);
     } else if (xg <= 1) {
       launch_decode_dma<G1, SPLIT, 1, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
-                                           N, out, out_lo, part, S_cap, cap, st, reduce);
+                                           N, out, out_lo, part, S_cap, cap, st, reduce, packed);
     } else if (xg == 2) {
       launch_decode_dma<G1, SPLIT, 2, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
-                                           N, out, out_lo, part, S_cap, cap, st, reduce);
+                                           N, out, out_lo, part, S_cap, cap, st, reduce, packed);
     } else {
       launch_decode_dma<G1, SPLIT, 4, 128>(nsplit, X, X_lo, perm, k, off, W, bias, gate, K, Nout,
-                                           N, out, out_lo, part, S_cap, cap, st, reduce);
+                                           N, out, out_lo, part, S_cap, cap, st, reduce, packed);
     }
     return;
   }
@@ -723,11 +729,11 @@ hipError_t launch_decode(const void* x, const int32_t* perm, const int32_t* off,
   profile_mark(3, st);
   launch_decode_gemm<true, SPLIT>(pl.dma1, pl.ks1, pl.xg, (const bf16*)x, nullptr, perm, k, off,
                                   (const bf16*)W1, (const bf16*)b1, nullptr, d, d_ff, N, hid,
-                                  hid_lo, part, S_cap, pl.cap, st);
+                                  hid_lo, part, S_cap, pl.cap, st, true, pl.packed);
   profile_mark(4, st);
   launch_decode_gemm<false, SPLIT>(pl.dma2, pl.ks2, pl.xg, (const bf16*)hid, hid_lo, perm, k, off,
                                    (const bf16*)W2, (const bf16*)b2, gate, d_ff, d, N, slot_out,
-                                   nullptr, part, S_cap, pl.cap, st, !defer2);
+                                   nullptr, part, S_cap, pl.cap, st, !defer2, pl.packed);
   if (defer2) {
     defer->part = part;
     defer->nsplit = pl.ks2;
@@ -814,6 +820,40 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
   return launch_tiled<128, 128, 64, 64, false>(x, perm, gate, W1, b1, W2, b2, d, d_ff, k, pl,
                                                 s.hidden, nullptr, t1, t2, s.counts, slot_out,
                                                 s.part, st);
+}
+
+namespace {
+// Packed weight layout (see gemm_ring.h): output word g (16 bytes) of piece
+// (e, row block rb, K chunk kc) = g / 64 is word w = g % 64 of the piece: row
+// rb*16 + w/4, 8 bf16 from K offset kc*32 + 8*((w%4) ^ ((w/16)%4)). A grid
+// stride over the words; consecutive threads write consecutive words.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const bf16* __restrict__ W, int rows,
+                                                           int K, size_t words,
+                                                           uint4* __restrict__ out) {
+  const int kcs = K / 32, rbs = rows / 16;
+  for (size_t g = (size_t)blockIdx.x * 256 + threadIdx.x; g < words;
+       g += (size_t)gridDim.x * 256) {
+    const int w = (int)(g & 63);
+    const size_t piece = g >> 6;
+    const int kc = (int)(piece % kcs);
+    const size_t rest = piece / kcs;
+    const int rb = (int)(rest % rbs);
+    const size_t e = rest / rbs;
+    const int row = rb * 16 + (w >> 2);
+    const int chunk = (w & 3) ^ ((w >> 4) & 3);
+    out[g] = *(const uint4*)(W + ((e * rows + row) * K + (size_t)kc * 32 + chunk * 8));
+  }
+}
+}  // namespace
+
+hipError_t launch_pack_weights(const void* W, int N, int rows, int K, void* out,
+                               hipStream_t st) {
+  const size_t words = (size_t)N * rows * K / 8;
+  if (words == 0) return hipSuccess;
+  const size_t blocks = (words + 255) / 256;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(blocks < 65536 ? (unsigned)blocks : 65536u),
+                     dim3(256), 0, st, (const bf16*)W, rows, K, words, (uint4*)out);
+  return hipGetLastError();
 }
 
 namespace {

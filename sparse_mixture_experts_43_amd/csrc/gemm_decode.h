@@ -18,6 +18,10 @@ namespace {
 // bank-conflict free. Each wave multiplies its 16 weight rows against the
 // slot groups with v_mfma_f32_16x16x32_bf16. With split-K the blocks write
 // fp32 partial sums and a reduce kernel applies bias and the epilogue.
+// With packed weights (`packed` != 0, the piece layout of gemm_ring.h) a
+// wave's weight copies are the stage's 1 KB pieces of its own 16 rows, which
+// land piece by piece and are read with the ring kernel's fragment addressing:
+// the same fragments, MFMAs and results.
 constexpr int kDKC = 128;             // K per chunk (default)
 constexpr int kDRowB = kDKC * 2;      // 256 bytes per row per chunk
 constexpr int kDWRows = 64;           // weight rows per block
@@ -59,7 +63,7 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
     int kpairs, const int32_t* __restrict__ off, const bf16* __restrict__ W,
     const bf16* __restrict__ bias, const float* __restrict__ gate, int K, int Nout, int nblk_n,
     int nsplit, void* __restrict__ out, bf16* __restrict__ out_lo, float* __restrict__ part,
-    int S_cap, int cap, int n_experts) {
+    int S_cap, int cap, int n_experts, int packed) {
   using Geo = DecodeGeom<G1, SPLIT, XG, RING, KC>;
   constexpr bool XLO = Geo::XLO;
   constexpr int ROWB = Geo::ROWB, CPR = Geo::CPR, RPI = Geo::RPI, WLD = Geo::WLD, XLD = Geo::XLD;
@@ -100,10 +104,18 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
     const int kbeg = c0 * KC;
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
-      const int r = RPI * (4 * i + wv) + rsub;
-      const int c = (l % CPR) ^ (r & 15);
-      const int n = min(n0 + r, Nout - 1);
-      pw[i] = (const unsigned char*)(W + ((size_t)e * Nout + n) * K + kbeg) + 16 * c;
+      if (packed) {
+        // packed weights: wave-load i of wave wv is the 1 KB piece of row
+        // block wv (rows n0 + 16 wv ..), K chunk i of the stage
+        const int rb = min((n0 >> 4) + wv, (Nout >> 4) - 1);
+        pw[i] = (const unsigned char*)(W + (size_t)e * Nout * K) +
+                ((size_t)rb * (K / 32) + (size_t)c0 * (KC / 32) + i) * 1024 + 16 * l;
+      } else {
+        const int r = RPI * (4 * i + wv) + rsub;
+        const int c = (l % CPR) ^ (r & 15);
+        const int n = min(n0 + r, Nout - 1);
+        pw[i] = (const unsigned char*)(W + ((size_t)e * Nout + n) * K + kbeg) + 16 * c;
+      }
     }
 #pragma unroll
     for (int i = 0; i < XG * XLD; ++i) {
@@ -120,8 +132,9 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
     constexpr int NG = decltype(ng_c)::value;
     MOE_LDS unsigned char* st = lds + (slot_i % RING) * Geo::SLOT;
     const int kb = chunk * ROWB;
+    const size_t kw = (size_t)chunk * (packed ? KC * 32 : ROWB);  // weight bytes to the chunk
 #pragma unroll
-    for (int i = 0; i < WLD; ++i) dma16(pw[i] + kb, st + Geo::W_OFF + (4 * i + wv) * 1024);
+    for (int i = 0; i < WLD; ++i) dma16(pw[i] + kw, st + Geo::W_OFF + (4 * i + wv) * 1024);
 #pragma unroll
     for (int i = 0; i < NG * XLD; ++i) {
       dma16(px[i] + kb, st + Geo::X_OFF + (4 * i + wv) * 1024);
@@ -168,7 +181,12 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
 #pragma unroll
       for (int kq = 0; kq < KC / 32; ++kq) {
         const int ch = 4 * kq + (l >> 4);
-        const bf16x8 wf = *(const bf16x8*)(st + Geo::W_OFF + R * ROWB + 16 * (ch ^ Rs));
+        // packed: piece 4 kq + wv, this lane's row l & 15 and 16-byte chunk
+        // l >> 4 at the copy's word 4 (l & 15) + ((l >> 4) ^ ((l >> 2) & 3))
+        const int wo = packed ? (4 * kq + wv) * 1024 + (l & 15) * 64 +
+                                    16 * ((l >> 4) ^ ((l >> 2) & 3))
+                              : R * ROWB + 16 * (ch ^ Rs);
+        const bf16x8 wf = *(const bf16x8*)(st + Geo::W_OFF + wo);
 #pragma unroll
         for (int sg = 0; sg < NG; ++sg) {
           const int xo = (16 * sg + S) * ROWB + 16 * (ch ^ S);

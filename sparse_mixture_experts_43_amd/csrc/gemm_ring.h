@@ -42,6 +42,13 @@ __device__ __forceinline__ float gelu_as(float z) {
 namespace {
 
 // ---------------------------------------------------------------- tiled bf16, LDS-DMA ring
+// Packed weights (`packed` != 0, written by moe_pack_weights): expert e's
+// matrix [Nout, K] is stored as pieces of 16 rows x 32 K, piece (row block rb,
+// K chunk kc) at ((e * Nout/16 + rb) * K/32 + kc) * 1024 bytes, its 16-byte
+// word w holding row rb*16 + w/4, chunk (w%4) ^ ((w/16)%4): exactly the LDS
+// image of one weight copy below, so a copy reads 1 KB contiguous instead of
+// 64 bytes from each of 16 rows (the same tile contents and results).
+//
 // Fast path for K % 32 == 0. Tiles stream into a RING-slot LDS ring with
 // global_load_lds_dwordx4 (each lane's 16 bytes land at base + 16 * lane, so a
 // wave instruction fills 16 rows x 64 bytes); no VGPR staging and no ds_write.
@@ -262,7 +269,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
     const float* __restrict__ gate, const int4* __restrict__ tiles,
     const int32_t* __restrict__ ntiles_p, int K, int Nout, void* __restrict__ out,
     bf16* __restrict__ out_lo, int M_total, int ldo, float* __restrict__ part,
-    int* __restrict__ wq) {
+    int* __restrict__ wq, int packed) {
   constexpr bool G1 = MODE == kEpiGelu;
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int NTH = NW * kWave;
@@ -366,11 +373,22 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
     const bf16* We = W + (size_t)e * Nout * K;
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
-      const int r = (i * NW + wv) * 16 + (l >> 2);
-      const int n = n0 + r < Nout ? n0 + r : Nout - 1;
-      pb[i] = (const unsigned char*)(We + (size_t)n * K) + csw;
+      if (packed) {
+        // packed weights: the 16 rows x 32 K of stage kt are one contiguous
+        // 1 KB piece in this copy's LDS order (row blocks past Nout repeat the
+        // last one; Nout % 16 == 0)
+        const int rb = (n0 + (i * NW + wv) * 16) >> 4;
+        const int nrb = Nout >> 4;
+        pb[i] = (const unsigned char*)We + (size_t)(rb < nrb ? rb : nrb - 1) * (K / kRK) * 1024 +
+                16 * l;
+      } else {
+        const int r = (i * NW + wv) * 16 + (l >> 2);
+        const int n = n0 + r < Nout ? n0 + r : Nout - 1;
+        pb[i] = (const unsigned char*)(We + (size_t)n * K) + csw;
+      }
     }
   };
+  const int wstep = packed ? 1024 : kRowB;  // weight bytes between stages of one row block
   MOE_LDS unsigned char* lds = (MOE_LDS unsigned char*)smem;
   int kb = 0, nks = 0;  // stage range of the current item: [kb, kb + nks)
   // A stage's copies go out in two parts: part 0 (token rows, and their
@@ -393,7 +411,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
     } else {
 #pragma unroll
       for (int i = 0; i < BI; ++i)
-        dma16(pb[i] + kbyte, st + B_OFF + (i * NW + wv) * 1024);
+        dma16(pb[i] + (size_t)src_kt * wstep, st + B_OFF + (i * NW + wv) * 1024);
     }
   };
   // prologue of an item: stages 0 .. RING-3 whole, stage RING-2 part 0 (EARLY:

@@ -136,6 +136,13 @@ static int noalloc_scratch(void** out) {
   return MOE_OK;
 }
 
+// MOE_FLAG_PACKED_WEIGHTS: bf16 experts with d and d_ff multiples of 128
+// (every expert GEMM path then reads the piece layout).
+static int check_packed(int flags, int d, int d_ff, int dtype) {
+  if (!(flags & MOE_FLAG_PACKED_WEIGHTS)) return MOE_OK;
+  return dtype == MOE_BF16 && d % 128 == 0 && d_ff % 128 == 0 ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
 // The layer forward behind moe_forward (caller workspace) and
 // moe_forward_noalloc (noalloc: the device's static scratch array, whose
 // address replaces workspace once the sizes are known to fit).
@@ -150,8 +157,11 @@ static int forward_impl(const void* x, const void* W_g, const float* logit_bias,
   if (st != MOE_OK) return st;
   if (isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
   if (flags & ~(MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32 | MOE_FLAG_FIRST_COME |
-                MOE_FLAG_RENORM_SURVIVORS | MOE_FLAG_IDENTITY_FALLBACK | MOE_FLAG_EXPERT_CHOICE))
+                MOE_FLAG_RENORM_SURVIVORS | MOE_FLAG_IDENTITY_FALLBACK | MOE_FLAG_EXPERT_CHOICE |
+                MOE_FLAG_PACKED_WEIGHTS))
     return MOE_ERR_INVALID_ARG;
+  st = check_packed(flags, d, d_ff, dtype);
+  if (st != MOE_OK) return st;
   const bool ec = (flags & MOE_FLAG_EXPERT_CHOICE) != 0;
   if (ec && ((flags & (MOE_FLAG_FIRST_COME | MOE_FLAG_RENORM_SURVIVORS)) || topk_idx_opt))
     return MOE_ERR_INVALID_ARG;
@@ -355,7 +365,10 @@ int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
                    void* stream) {
   int st = check_shape(T, d, d_ff, N, k, dtype, true);
   if (st != MOE_OK) return st;
-  if (flags & ~(MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32)) return MOE_ERR_INVALID_ARG;
+  if (flags & ~(MOE_FLAG_HIDDEN_SPLIT | MOE_FLAG_Y_F32 | MOE_FLAG_PACKED_WEIGHTS))
+    return MOE_ERR_INVALID_ARG;
+  st = check_packed(flags, d, d_ff, dtype);
+  if (st != MOE_OK) return st;
   if (isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !perm || !offsets || !slot_gate || !W1 || !W2 || !slot_out) return MOE_ERR_INVALID_ARG;
@@ -373,6 +386,21 @@ int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
   return hip_status(launch_expert_ffn(x, perm, offsets, slot_gate, W1, b1, W2, b2, T, d, d_ff, N,
                                       k, C, S_max, dtype, flags, slot_out, fs,
                                       (hipStream_t)stream));
+}
+
+int moe_pack_weights(const void* W, int N, int rows, int K, int dtype, void* W_packed,
+                     void* stream) {
+  if (N < 0 || rows < 0 || K < 0 || dtype < MOE_F32 || dtype > MOE_BF16)
+    return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 || rows % 16 != 0 || K % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((size_t)N * rows * K == 0) return MOE_OK;
+  if (!W || !W_packed) return MOE_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(W_packed, 16)) return MOE_ERR_UNSUPPORTED;
+  const size_t bytes = (size_t)N * rows * K * 2;
+  const char* a = (const char*)W;
+  const char* b = (const char*)W_packed;
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // overlapping buffers
+  return hip_status(launch_pack_weights(W, N, rows, K, W_packed, (hipStream_t)stream));
 }
 
 int moe_combine(const void* slot_out, const int32_t* inv, const void* x, const float* shared_out,

@@ -145,6 +145,7 @@ constexpr int kFlagFirstCome = 4;    // MOE_FLAG_FIRST_COME
 constexpr int kFlagRenorm = 8;       // MOE_FLAG_RENORM_SURVIVORS
 constexpr int kFlagIdentity = 16;    // MOE_FLAG_IDENTITY_FALLBACK
 constexpr int kFlagExpertChoice = 32;  // MOE_FLAG_EXPERT_CHOICE
+constexpr int kFlagPacked = 64;        // MOE_FLAG_PACKED_WEIGHTS
 void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype,
                int flags, FfnScratch* s);
 
@@ -200,6 +201,9 @@ hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d
 hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, int d, int k,
                                  int y_dtype, const void* x, int x_dtype, const float* sh,
                                  void* y, hipStream_t st);
+// Weights [N, rows, K] bf16 -> the packed piece layout of gemm_ring.h (same
+// size; rows % 16 == 0, K % 32 == 0).
+hipError_t launch_pack_weights(const void* W, int N, int rows, int K, void* out, hipStream_t st);
 // Shared expert: the grouped expert FFN run as one expert that holds every
 // token (slot t = token t, weight 1); out fp32 [T, d]. Scratch from
 // carve_shared (the identity dispatch plus the FFN scratch).

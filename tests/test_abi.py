@@ -117,7 +117,23 @@ def test_argument_checks_return_before_launch():
     assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, float("nan"), 1, 0, nul, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -1
     assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 0, nul, p, nul, nul, nul, nul, nul, nul, p, 16, nul) == -3
     # unknown flag bits
-    assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 64, nul, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -1
+    assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 128, nul, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -1
+    # packed weights: bf16 only, d and d_ff multiples of 128
+    assert raw.moe_forward(*fargs, 4, 128, 128, 8, 2, 1.0, 0, 64, nul, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -2
+    assert raw.moe_forward(*fargs, 4, 64, 128, 8, 2, 1.0, 1, 64, nul, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -2
+    assert raw.moe_forward(*fargs, 4, 128, 192, 8, 2, 1.0, 1, 64, nul, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -2
+    ffn = [p] * 8
+    assert raw.moe_expert_ffn(*ffn, 4, 128, 128, 8, 2, 1.0, 0, 64, p, p, 1 << 30, nul) == -2
+    assert raw.moe_expert_ffn(*ffn, 4, 128, 128, 8, 2, 1.0, 1, 128, p, p, 1 << 30, nul) == -1
+    # pack: dtype, rows % 16, K % 128, null, overlap, empty
+    q = ctypes.c_void_p(4096 + (1 << 24))
+    assert raw.moe_pack_weights(p, 2, 32, 128, 0, q, nul) == -2
+    assert raw.moe_pack_weights(p, 2, 32, 128, 7, q, nul) == -1
+    assert raw.moe_pack_weights(p, 2, 24, 128, 1, q, nul) == -2
+    assert raw.moe_pack_weights(p, 2, 32, 96, 1, q, nul) == -2
+    assert raw.moe_pack_weights(nul, 2, 32, 128, 1, q, nul) == -1
+    assert raw.moe_pack_weights(p, 2, 32, 128, 1, ctypes.c_void_p(4096 + 1024), nul) == -1
+    assert raw.moe_pack_weights(nul, 0, 32, 128, 1, nul, nul) == 0
     # expert choice with a flag or output it does not combine with
     assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 32 | 4, nul, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -1
     assert raw.moe_forward(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 32 | 8, nul, p, nul, nul, nul, nul, nul, nul, p, 1 << 30, nul) == -1
@@ -156,7 +172,8 @@ def test_noalloc_host_checks(lib):
     tail = [nul, p, nul, nul, nul, nul, nul, nul, nul]
     assert raw.moe_forward_noalloc(*fargs, -1, 64, 64, 8, 2, 1.0, 1, 0, *tail) == -1
     assert raw.moe_forward_noalloc(*fargs, 4, 64, 64, 8, 2, float("nan"), 1, 0, *tail) == -1
-    assert raw.moe_forward_noalloc(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 64, *tail) == -1
+    assert raw.moe_forward_noalloc(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 128, *tail) == -1
+    assert raw.moe_forward_noalloc(*fargs, 4, 64, 64, 8, 2, 1.0, 1, 64, *tail) == -2
     assert raw.moe_forward_noalloc(*fargs, 4, 60, 64, 8, 2, 1.0, 1, 0, *tail) == -2
     assert raw.moe_forward_noalloc(nul, nul, nul, nul, nul, nul, nul, 0, 64, 64, 8, 2, 1.0, 1, 0,
                                    nul, nul, nul, nul, nul, nul, nul, nul, nul) == 0
