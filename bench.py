@@ -295,7 +295,8 @@ def measure_extras(moe, torch, w, dv, ws, y, flags):
     return extras
 
 
-def run_workload(moe, torch, w, fl, steps, warmup, want_extras, cpu_budget_s, copy_probe_mib=0):
+def run_workload(moe, torch, w, fl, steps, warmup, want_extras, cpu_budget_s, copy_probe_mib=0,
+                 pack=True):
     """Times one workload: W warm-up steps, an untimed pass with stage events,
     then exactly K timed steps. Returns the workload's record (value, roofline
     of the dominant expert GEMM, layer figures, CPU oracle baseline)."""
@@ -309,6 +310,16 @@ def run_workload(moe, torch, w, fl, steps, warmup, want_extras, cpu_budget_s, co
     log(f"inputs drawn on the host in {time.time() - t0:.1f}s")
     dev = torch.device("cuda:0")
     dv = {k: (None if v is None else v.to(dev).contiguous()) for k, v in inp.items()}
+    # The expert weights in the library's packed layout, written once as a
+    # model would at load time (a reordering of the same values; no step
+    # includes it): bf16 layers with d and d_ff multiples of 128.
+    packed = pack and w.dtype == "bf16" and w.d % 128 == 0 and w.d_ff % 128 == 0
+    if packed:
+        dv["W1"] = moe.moe_pack_weights(dv["W1"])
+        dv["W2"] = moe.moe_pack_weights(dv["W2"])
+        flags |= moe.MOE_FLAG_PACKED_WEIGHTS
+        torch.cuda.synchronize()
+        log("expert weights packed (moe_pack_weights, once, outside every timed region)")
     ws = moe.alloc_workspace(moe.moe_workspace_bytes(w.T, w.d, w.d_ff, w.N, w.k, w.capacity_factor,
                                                      dv["x"].dtype), dev)
     y = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
@@ -442,6 +453,7 @@ def run_workload(moe, torch, w, fl, steps, warmup, want_extras, cpu_budget_s, co
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "N": w.N, "k": w.k,
                    "capacity_factor": w.capacity_factor, "hidden": fl, "y_dtype": "f32",
+                   "expert_weights": "packed at load" if packed else "row-major",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"tflops": layer_tflops, "frac_bf16_peak": layer_tflops / peak_f,
@@ -486,6 +498,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the routing-statistics and drop-policy measurements after timing")
+    ap.add_argument("--unpacked", action="store_true",
+                    help="pass the expert weights row-major instead of packed once at load")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the "
                          "reference dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -507,7 +521,8 @@ def main():
     w = get_workload(args.workload)
     fl = args.flags or DEFAULT_FLAGS.get(w.name, "plain")
     head = run_workload(moe, torch, w, fl, args.steps, args.warmup, not args.no_extras,
-                        0 if args.no_cpu_baseline else 10.0, args.copy_probe_mib)
+                        0 if args.no_cpu_baseline else 10.0, args.copy_probe_mib,
+                        not args.unpacked)
     if args.configs == "all":
         others = [n for n in WORKLOADS if n != w.name]
     elif args.configs in ("", "none"):
@@ -518,7 +533,8 @@ def main():
     for name in others:
         wo = get_workload(name)
         configs[name] = run_workload(moe, torch, wo, DEFAULT_FLAGS.get(name, "plain"), args.steps,
-                                     args.warmup, False, 0 if args.no_cpu_baseline else 5.0)
+                                     args.warmup, False, 0 if args.no_cpu_baseline else 5.0,
+                                     pack=not args.unpacked)
     out = {
         "metric": METRIC,
         "value": head["value"],
