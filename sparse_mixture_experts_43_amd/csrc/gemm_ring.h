@@ -638,6 +638,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
     if constexpr (MODE != kEpiLogit) {
       if (threadIdx.x < BM) sh_gate[threadIdx.x] = stg;
       if (threadIdx.x < BN) sh_bias[threadIdx.x] = stb;
+      // the stores must have completed before the barrier: s_barrier alone
+      // does not order them before another wave's reads (with two workgroups
+      // per CU, a wave has read the previous tile's gates for 16 rows without
+      // this wait)
+      lgkm_wait0();
       wg_barrier();
     }
     if (more) {
