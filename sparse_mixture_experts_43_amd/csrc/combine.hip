@@ -93,7 +93,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // The same combine when the second expert GEMM left K-split partials: each
 // kept pick's slot value is finished here as gate * (((0 + p_0) + p_1) + ... +
 // b2), the operations and order of the split-K reduction, then summed over the
-// picks in fixed order, so y is bit-identical to the two-kernel path.
+// picks in fixed order, so y is bit-identical to the two-kernel path. Picks go
+// in groups of 4: their slot indices first, then every partial vector and gate
+// of the group (splits 2 at a time) in flight together, then the sums.
 template <typename T, typename B, typename XT>
 __global__ __launch_bounds__(256) void combine_splitk_kernel(
     const float* __restrict__ part, int nsplit, int S_cap, const B* __restrict__ bias,
@@ -102,6 +104,8 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(
     const float* __restrict__ sh, T* __restrict__ y) {
 #pragma clang fp contract(off)
   constexpr int V = 16 / sizeof(T);
+  constexpr int G = 4;  // picks per group
+  constexpr int Q = 2;  // splits per batch of loads
   const int vpr = d / V;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long long)T_ * vpr) return;
@@ -111,37 +115,62 @@ __global__ __launch_bounds__(256) void combine_splitk_kernel(
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
   bool any = false;
-  for (int j = 0; j < k; ++j) {
-    const int s = inv[(size_t)t * k + j];
-    if (s < 0) continue;
-    any = true;
-    float v[V];
+  for (int j0 = 0; j0 < k; j0 += G) {
+    int s[G];
+    float g[G];
 #pragma unroll
-    for (int i = 0; i < V; ++i) v[i] = 0.f;
-    for (int q = 0; q < nsplit; ++q) {
-      const f32x4* src = (const f32x4*)(part + ((size_t)q * S_cap + s) * d + c);
+    for (int q = 0; q < G; ++q) s[q] = j0 + q < k ? inv[(size_t)t * k + j0 + q] : -1;
 #pragma unroll
-      for (int h = 0; h < V / 4; ++h) {
-        const f32x4 pv = src[h];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[4 * h + i] += pv[i];
-      }
+    for (int q = 0; q < G; ++q) {
+      any |= s[q] >= 0;
+      g[q] = s[q] >= 0 ? gate[s[q]] : 0.f;
     }
-    int e = 0;
-    if (bias != nullptr) {
-      // expert of slot s: the last e with off[e] <= s
-      int lo = 0, hi = N - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= s) lo = mid; else hi = mid - 1;
-      }
-      e = lo;
-    }
-    const float g = gate[s];
+    float v[G][V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      v[i] += bias != nullptr ? to_f32(bias[(size_t)e * d + c + i]) : 0.f;
-      acc[i] += v[i] * g;  // rounded product, as the stored slot value (no fma)
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[q][i] = 0.f;
+    for (int h0 = 0; h0 < nsplit; h0 += Q) {
+      f32x4 pv[Q][G][V / 4];
+#pragma unroll
+      for (int h = 0; h < Q; ++h)
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          const bool ld = h0 + h < nsplit && s[q] >= 0;
+          const f32x4* src =
+              (const f32x4*)(part + ((size_t)(ld ? h0 + h : 0) * S_cap + (ld ? s[q] : 0)) * d + c);
+#pragma unroll
+          for (int u = 0; u < V / 4; ++u) pv[h][q][u] = ld ? src[u] : (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int h = 0; h < Q; ++h)
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          if (h0 + h >= nsplit || s[q] < 0) continue;
+#pragma unroll
+          for (int u = 0; u < V / 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[q][4 * u + i] += pv[h][q][u][i];
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      if (s[q] < 0) continue;
+      int e = 0;
+      if (bias != nullptr) {
+        // expert of slot s: the last e with off[e] <= s
+        int lo = 0, hi = N - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (off[mid] <= s[q]) lo = mid; else hi = mid - 1;
+        }
+        e = lo;
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const float vb = v[q][i] + (bias != nullptr ? to_f32(bias[(size_t)e * d + c + i]) : 0.f);
+        acc[i] += vb * g[q];  // rounded product, as the stored slot value (no fma)
+      }
     }
   }
   if (!any && x != nullptr) load_x_row<V>(x, t, d, c, acc);

@@ -24,6 +24,7 @@
 //               an ordered block scan keeps the strictly larger codes and the
 //               first equal ones in token order.
 #include "moe_common.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -255,6 +256,134 @@ __global__ __launch_bounds__(kScanThreads) void fused_dispatch_kernel(
         const int s = sv[u];
         if (s < 0) inv[p] = -1;
         else bucket[s] = p;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ route + dispatch (few tokens)
+// Few tokens (T <= 64, N <= 64, k <= 16): the split-K router leaves S partial
+// logit tiles part[s][r][n] (r < Tp = 16 cdiv(T, 16), n < NP). One block adds
+// them (splitk_logit, as the router's own top-k kernel does, so both give the
+// same bits), adds the bias and runs the top-k of every row (logits and key to
+// global memory, the picks and weights to LDS as well), then dispatches the
+// P = T*k <= 1024 pairs from LDS:
+//   wave c owns pairs 64c .. 64c+63; per expert one ballot gives the chunk's
+//   count and each pair's rank among the chunk's pairs of that expert;
+//   wave 0 (lane = expert) adds the chunk counts in chunk order (the chunk
+//   bases), scans requests and kept counts over the experts and writes
+//   req / cnt / reqoff / off / n_dropped;
+//   a pair's bucket position is its expert's request offset + the counts of
+//   the earlier chunks + its rank: expert-major, pair order within an expert,
+//   the layout the other dispatch paths produce.
+// With no possible overflow (C >= T) the position is the slot (perm, gate,
+// inv written here); otherwise the request-ordered bucket, which the
+// selection that follows turns into slots. One launch and three global round
+// trips fewer than router + dispatch.
+constexpr int kRouteDispatchPairs = 64 * kMaxK;
+template <int NT>
+__global__ __launch_bounds__(kScanThreads) void route_dispatch_kernel(
+    const float* __restrict__ part, int S, int Tp, const float* __restrict__ bias, int T, int N,
+    int k, float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ w,
+    double* __restrict__ key, int C, int direct, int32_t* __restrict__ req,
+    int32_t* __restrict__ cnt, int32_t* __restrict__ off, int32_t* __restrict__ reqoff,
+    int32_t* __restrict__ n_dropped, int32_t* __restrict__ bucket, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, float* __restrict__ gate) {
+  constexpr int NP = NT * 16;
+  constexpr int kRows = 64;
+  constexpr int NWV = kScanThreads / kWave;
+  static_assert(NWV * kWave >= kRouteDispatchPairs, "one 64-pair chunk per wave");
+  __shared__ float Ls[kRows][NP + 4];
+  __shared__ int32_t s_idx[kRouteDispatchPairs];
+  __shared__ float s_w[kRouteDispatchPairs];
+  __shared__ int s_cc[NWV][kWave];  // per chunk and expert: count, then base
+  __shared__ int s_roff[kWave];
+  const int l = lane_id();
+  const int wv = threadIdx.x / kWave;
+  const size_t stride = (size_t)Tp * NP;
+  for (int i = threadIdx.x; i < kRows * NP; i += kScanThreads) {
+    const int r = i / NP, n = i - r * NP;
+    float v = 0.f;
+    if (r < Tp) {
+      // (fewer loads in flight where four waves per SIMD leave 128 VGPRs to
+      // the wider top-k)
+      v = splitk_logit<NT == 1 ? 32 : 16>(part + (size_t)r * NP + n, S, stride);
+      v += (bias != nullptr && n < N) ? bias[n] : 0.f;
+    }
+    Ls[r][n] = v;
+  }
+  __syncthreads();
+  if constexpr (NT == 1) {
+    // 16 waves x 4 rows (16-lane groups) cover the 64 rows; waves past the
+    // last token skip (their reductions stay inside the wave)
+    if (wv * 4 < T) {
+      const int r = wv * 4 + (l >> 4);
+      topk_row16(&Ls[r][0], r < T, N, k, r, logits, s_idx, s_w, key);
+    }
+  } else {
+    for (int r = wv; r < T; r += NWV) topk_row(&Ls[r][0], N, k, r, logits, s_idx, s_w, key);
+  }
+  __syncthreads();
+  const int P = T * k;
+  const int p = wv * kWave + l;
+  const bool in = p < P;
+  if (in) {
+    idx[p] = s_idx[p];
+    w[p] = s_w[p];
+  }
+  const int e = in ? s_idx[p] : -1;
+  const bool ok = in && (unsigned)e < (unsigned)N;
+  const unsigned long long lt = lanemask_lt();
+  int rank = 0, ccount = 0;
+  for (int ex = 0; ex < N; ++ex) {
+    const unsigned long long m = __ballot(ok && e == ex);
+    if (l == ex) ccount = __popcll(m);
+    if (ok && e == ex) rank = __popcll(m & lt);
+  }
+  s_cc[wv][l] = ccount;
+  __syncthreads();
+  if (wv == 0) {
+    int run = 0;
+    for (int q = 0; q < NWV; ++q) {
+      const int c = s_cc[q][l];
+      s_cc[q][l] = run;
+      run += c;
+    }
+    const int kept = run < C ? run : C;
+    int ir = run, ik = kept;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int yr = __shfl_up(ir, o, kWave), yk = __shfl_up(ik, o, kWave);
+      if (l >= o) {
+        ir += yr;
+        ik += yk;
+      }
+    }
+    if (l < N) {
+      req[l] = run;
+      cnt[l] = kept;
+      reqoff[l] = ir - run;
+      off[l] = ik - kept;
+    }
+    s_roff[l] = ir - run;
+    if (l == kWave - 1) {
+      reqoff[N] = ir;
+      off[N] = ik;
+      *n_dropped = P - ik;
+    }
+  }
+  __syncthreads();
+  if (in) {
+    if (!ok) {
+      inv[p] = -1;
+    } else {
+      const int pos = s_roff[e] + s_cc[wv][e] + rank;
+      if (direct) {
+        perm[pos] = p;
+        gate[pos] = s_w[p];
+        inv[p] = pos;
+      } else {
+        bucket[pos] = p;
       }
     }
   }
@@ -683,10 +812,20 @@ void carve_dispatch(Carver& c, int P, int N, DispatchScratch* s) {
   s->codes = c.take<unsigned long long>((size_t)(P > 0 ? P : 1));
 }
 
+template <int NT>
+void launch_route_dispatch(const RoutePartials& rp, int T, int N, int k, int C, int direct,
+                           int32_t* req, int32_t* cnt, int32_t* off, int32_t* perm, int32_t* inv,
+                           float* gate, int32_t* n_dropped, const DispatchScratch& s,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(route_dispatch_kernel<NT>, dim3(1), dim3(kScanThreads), 0, st, rp.part,
+                     rp.S, rp.Tp, rp.bias, T, N, k, rp.logits, rp.idx, rp.w, rp.key, C, direct,
+                     req, cnt, off, s.reqoff, n_dropped, s.bucket, perm, inv, gate);
+}
+
 hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key, int T, int N,
                            int k, int C, int flags, int32_t* req, int32_t* cnt, int32_t* off,
                            int32_t* perm, int32_t* inv, float* gate, int32_t* n_dropped,
-                           const DispatchScratch& s, hipStream_t st) {
+                           const DispatchScratch& s, hipStream_t st, const RoutePartials* rp) {
   const int P = T * k;
   if (P == 0) return hipSuccess;
   // an expert receives at most T requests, so with C >= T nothing can drop
@@ -694,7 +833,19 @@ hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key
   const bool can_drop = C < T;
   const bool fused = P <= kFusedMaxPairs;
   const int fc_k = (flags & kFlagFirstCome) ? k : 0;
-  if (fused) {
+  if (rp != nullptr) {
+    // few tokens: the router's top-k runs in the dispatch block (P <= 64 * 16)
+    if (T > 64 || rp->NP > 64 || P > kRouteDispatchPairs || rp->idx != idx || rp->w != w ||
+        rp->key != key)
+      return hipErrorInvalidValue;
+    const int direct = can_drop ? 0 : 1;
+    switch (rp->NP / 16) {
+      case 1: launch_route_dispatch<1>(*rp, T, N, k, C, direct, req, cnt, off, perm, inv, gate, n_dropped, s, st); break;
+      case 2: launch_route_dispatch<2>(*rp, T, N, k, C, direct, req, cnt, off, perm, inv, gate, n_dropped, s, st); break;
+      case 3: launch_route_dispatch<3>(*rp, T, N, k, C, direct, req, cnt, off, perm, inv, gate, n_dropped, s, st); break;
+      default: launch_route_dispatch<4>(*rp, T, N, k, C, direct, req, cnt, off, perm, inv, gate, n_dropped, s, st); break;
+    }
+  } else if (fused) {
     const size_t lds = ((size_t)(kScanThreads / kWave) * N + N) * sizeof(int) +
                        (size_t)P * sizeof(int16_t);
     MOE_SET_LDS_ONCE(fused_dispatch_kernel, 160 * 1024);

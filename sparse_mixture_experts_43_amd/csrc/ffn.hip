@@ -520,7 +520,6 @@ struct Plan {
   bool packed;     // W1 and W2 in the packed piece layout (moe_pack_weights)
 };
 
-// Split-K factor for a decode GEMM: enough blocks to cover the CUs a few times.
 // Split-K factor for a decode GEMM: double it (keeping at least 8 chunks of
 // K per share) while there are fewer than 1024 items; measured on the
 // Mixtral-shaped decode layer, more items per workgroup stream better than

@@ -197,13 +197,20 @@ static int forward_impl(const void* x, const void* W_g, const float* logit_bias,
   profile_mark(0, s);
   // expert choice: the router's logits (its top-1 outputs are scratch), then
   // every pair as a candidate
-  hipError_t e = launch_route(x, W_g, logit_bias, T, d, N, ec ? 1 : k, dtype, f.logits, f.idx,
-                              f.w, f.key, f.wgt, s);
+  // few tokens: the split-K router leaves partial logits, and the dispatch
+  // block adds them and runs the top-k (one launch fewer)
+  RoutePartials rp;
+  hipError_t e = ec ? hipSuccess
+                    : launch_route_partials(x, W_g, logit_bias, T, d, N, dtype, f.logits, f.idx,
+                                            f.w, f.key, f.wgt, s, &rp);
+  if (e == hipSuccess && rp.part == nullptr)
+    e = launch_route(x, W_g, logit_bias, T, d, N, ec ? 1 : k, dtype, f.logits, f.idx, f.w, f.key,
+                     f.wgt, s);
   if (e == hipSuccess && ec) e = launch_route_expert_choice(f.logits, T, N, f.idx, f.w, f.key, s);
   if (e != hipSuccess) return hip_status(e);
   profile_mark(1, s);
   e = launch_dispatch(f.idx, f.w, f.key, T, N, kp, C, flags, f.req, f.cnt, f.off, f.perm, f.inv,
-                      f.gate, f.ndrop, f.ds, s);
+                      f.gate, f.ndrop, f.ds, s, rp.part != nullptr ? &rp : nullptr);
   if (e != hipSuccess) return hip_status(e);
   profile_mark(2, s);
   SplitK sk;  // a K-split second GEMM hands its partials straight to the combine

@@ -155,20 +155,44 @@ void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max
 // the combine.
 void profile_mark(int slot, hipStream_t st);
 
+// Split-K router state for few tokens (T <= 64, N <= 64, bf16, d % 128 == 0):
+// partial logit tiles part[s][r][n] (fp32, s < S, r < Tp = 16 cdiv(T, 16),
+// n < NP = 16 cdiv(N, 16)) in the router scratch, and where the routing that
+// finishes from them writes its results.
+struct RoutePartials {
+  const float* part = nullptr;
+  int S = 0, Tp = 0, NP = 0;
+  const float* bias = nullptr;
+  float* logits = nullptr;
+  int32_t* idx = nullptr;
+  float* w = nullptr;
+  double* key = nullptr;
+};
+
 // Launchers (return hipError_t of the last launch).
 size_t route_scratch_bytes(int d, int N, int dtype);  // transposed router weight
 hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T, int d, int N,
                         int k, int dtype, float* logits, int32_t* idx, float* w, double* key,
                         void* scratch, hipStream_t st);
+// Few tokens (the RoutePartials shapes): only the split-K router's first
+// kernel, and *rp filled for launch_dispatch, which finishes the routing. For
+// other shapes nothing is launched and rp->part stays null.
+hipError_t launch_route_partials(const void* x, const void* W_g, const float* bias, int T, int d,
+                                 int N, int dtype, float* logits, int32_t* idx, float* w,
+                                 double* key, void* scratch, hipStream_t st, RoutePartials* rp);
 // flags: kFlagFirstCome, kFlagRenorm.
 // Expert choice: from fp32 logits [T, N], every pair t*N + e as a candidate:
 // idx = e, w = p[t,e], key = log p[t,e] (fp64).
 hipError_t launch_route_expert_choice(const float* logits, int T, int N, int32_t* idx, float* w,
                                      double* key, hipStream_t st);
+// With `rp` (the split-K router's partial logits, few tokens) the dispatch
+// block first finishes the routing: it adds the partials, runs the top-k and
+// writes rp->logits / idx / w / key (the same arrays as idx / w / key here).
 hipError_t launch_dispatch(const int32_t* idx, const float* w, const double* key, int T, int N,
                            int k, int C, int flags, int32_t* req, int32_t* cnt, int32_t* off,
                            int32_t* perm, int32_t* inv, float* gate, int32_t* n_dropped,
-                           const DispatchScratch& s, hipStream_t st);
+                           const DispatchScratch& s, hipStream_t st,
+                           const RoutePartials* rp = nullptr);
 // Routing statistics: scratch bytes and launch (stats: [2N + 2] fp32).
 size_t stats_scratch_bytes(int T, int N);
 hipError_t launch_routing_stats(const float* logits, const int32_t* idx, int T, int N, int k,

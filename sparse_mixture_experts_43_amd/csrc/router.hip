@@ -19,6 +19,7 @@
 // cross-lane butterflies, then the fp64 log-sum-exp and the gates.
 #include "gemm_ring.h"
 #include "moe_common.h"
+#include "topk.h"
 
 #include <utility>
 
@@ -27,219 +28,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-
-// ---------------------------------------------------------------- 16-lane groups, DPP
-// All-reduce within each 16-lane row of a wave with DPP register moves (no
-// LDS crossbar): xor 1 and xor 2 inside quads, then the half-row mirror pairs
-// the two quads of each 8-lane half, the row mirror the two halves. Every
-// lane of the row ends with the reduction of all 16 (any pairing pattern is
-// valid for an associative, commutative combine).
-template <int CTRL>
-__device__ __forceinline__ int dpp_i32(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __builtin_bit_cast(float, dpp_i32<CTRL>(__builtin_bit_cast(int, v)));
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
-  const unsigned lo = (unsigned)dpp_i32<CTRL>((int)(unsigned)b);
-  const unsigned hi = (unsigned)dpp_i32<CTRL>((int)(unsigned)(b >> 32));
-  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
-}
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-// Shift right by one lane within each 16-lane row; lane 0 of a row reads 0.
-constexpr int kDppRowShr1 = 0x111;
-
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& bv, int& bn) {
-  const float ov = dpp_f32<CTRL>(bv);
-  const int on = dpp_i32<CTRL>(bn);
-  if (ov > bv || (ov == bv && on < bn)) {
-    bv = ov;
-    bn = on;
-  }
-}
-
-// Wave-wide versions: the row all-reduce, then the four rows' results (lanes
-// 0, 16, 32, 48) read as scalars and combined in a fixed order; every lane
-// gets the same value.
-__device__ __forceinline__ float wave_max_dpp(float m) {
-  m = fmaxf(m, dpp_f32<kDppXor1>(m));
-  m = fmaxf(m, dpp_f32<kDppXor2>(m));
-  m = fmaxf(m, dpp_f32<kDppHalfMirror>(m));
-  m = fmaxf(m, dpp_f32<kDppMirror>(m));
-  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 0));
-  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 16));
-  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 32));
-  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
-}
-__device__ __forceinline__ double readlane_f64(double v, int lane) {
-  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
-  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, lane);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), lane);
-  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
-}
-__device__ __forceinline__ double wave_sum_dpp(double s) {
-  s += dpp_f64<kDppXor1>(s);
-  s += dpp_f64<kDppXor2>(s);
-  s += dpp_f64<kDppHalfMirror>(s);
-  s += dpp_f64<kDppMirror>(s);
-  return (readlane_f64(s, 0) + readlane_f64(s, 16)) + (readlane_f64(s, 32) + readlane_f64(s, 48));
-}
-__device__ __forceinline__ void wave_argmax_dpp(float& bv, int& bn) {
-  argmax_step<kDppXor1>(bv, bn);
-  argmax_step<kDppXor2>(bv, bn);
-  argmax_step<kDppHalfMirror>(bv, bn);
-  argmax_step<kDppMirror>(bv, bn);
-  float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 0));
-  int n = __builtin_amdgcn_readlane(bn, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16) {
-    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), r));
-    const int on = __builtin_amdgcn_readlane(bn, r);
-    if (ov > v || (ov == v && on < n)) {
-      v = ov;
-      n = on;
-    }
-  }
-  bv = v;
-  bn = n;
-}
-
-// ---------------------------------------------------------------- phase 2
-// Row r of the block's logits tile (LDS, row stride ls_stride floats).
-// `logits` may be null (the row is already in global memory). S: 64-expert
-// slots per lane, S * 64 >= N (slots past N add nothing, so every S gives the
-// same bits; topk_row picks the smallest).
-template <int S>
-__device__ __forceinline__ void topk_row_s(const float* __restrict__ Lrow, int N, int k, int t,
-                                           float* __restrict__ logits, int32_t* __restrict__ idx,
-                                           float* __restrict__ w, double* __restrict__ key) {
-  static_assert(S >= 1 && S <= kMaxN / kWave, "slots");
-  const int l = lane_id();
-  float v[S];
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < S; ++i) {
-    const int n = l + kWave * i;
-    v[i] = (n < N) ? Lrow[n] : -INFINITY;
-    if (n < N) {
-      m = fmaxf(m, v[i]);
-      if (logits != nullptr) logits[(size_t)t * N + n] = v[i];
-    }
-  }
-  m = wave_max_dpp(m);
-
-  // fp64 softmax denominator over all N experts (no branch: v = -inf past N
-  // and exp(-inf) is exactly 0).
-  double s = 0.0;
-  const double md = (double)m;
-#pragma unroll
-  for (int i = 0; i < S; ++i) s += exp((double)v[i] - md);
-  s = wave_sum_dpp(s);
-  const double lse = md + log(s);
-
-  // k rounds of argmax: larger value wins, equal values -> lower index. Lane j
-  // keeps pick j (value, expert, unnormalised probability); no local arrays,
-  // so nothing lands in scratch memory.
-  unsigned taken = 0u;
-  float my_v = 0.f;
-  int my_n = 0;
-  double my_p = 0.0, psum = 0.0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bn = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-      const int n = l + kWave * i;
-      if (n < N && !((taken >> i) & 1u) && (v[i] > bv || bn == 0x7fffffff)) {
-        bv = v[i];
-        bn = n;
-      }
-    }
-    wave_argmax_dpp(bv, bn);
-    if ((bn & (kWave - 1)) == l) taken |= 1u << (bn / kWave);
-    const double pj = exp((double)bv - md);
-    psum += pj;
-    if (l == j) {
-      my_v = bv;
-      my_n = bn;
-      my_p = pj;
-    }
-  }
-  if (l < k) {
-    idx[(size_t)t * k + l] = my_n;
-    w[(size_t)t * k + l] = (float)(my_p / psum);
-    key[(size_t)t * k + l] = (double)my_v - lse;
-  }
-}
-
-__device__ __forceinline__ void topk_row(const float* __restrict__ Lrow, int N, int k, int t,
-                                         float* __restrict__ logits, int32_t* __restrict__ idx,
-                                         float* __restrict__ w, double* __restrict__ key) {
-  if (N <= 64) topk_row_s<1>(Lrow, N, k, t, logits, idx, w, key);
-  else if (N <= 128) topk_row_s<2>(Lrow, N, k, t, logits, idx, w, key);
-  else if (N <= 256) topk_row_s<4>(Lrow, N, k, t, logits, idx, w, key);
-  else if (N <= 512) topk_row_s<8>(Lrow, N, k, t, logits, idx, w, key);
-  else topk_row_s<kMaxN / kWave>(Lrow, N, k, t, logits, idx, w, key);
-}
-
-// N <= 16: topk_row with one 16-lane group per token row (lane c of the group
-// holds expert c), so a wave serves 4 rows; the reductions are the DPP row
-// all-reduces above. Same picks and gates as topk_row; the fp64 softmax sum
-// is added in another order. Every lane of the wave takes part in the
-// reductions; `active` only gates the stores.
-__device__ __forceinline__ void topk_row16(const float* __restrict__ Lrow, bool active, int N,
-                                           int k, int t, float* __restrict__ logits,
-                                           int32_t* __restrict__ idx, float* __restrict__ w,
-                                           double* __restrict__ key) {
-  const int c = lane_id() & 15;
-  const bool has = c < N;
-  const float v = has ? Lrow[c] : -INFINITY;
-  if (active && has && logits != nullptr) logits[(size_t)t * N + c] = v;
-  float m = v;
-  m = fmaxf(m, dpp_f32<kDppXor1>(m));
-  m = fmaxf(m, dpp_f32<kDppXor2>(m));
-  m = fmaxf(m, dpp_f32<kDppHalfMirror>(m));
-  m = fmaxf(m, dpp_f32<kDppMirror>(m));
-  const double md = (double)m;
-  double s = has ? exp((double)v - md) : 0.0;
-  s += dpp_f64<kDppXor1>(s);
-  s += dpp_f64<kDppXor2>(s);
-  s += dpp_f64<kDppHalfMirror>(s);
-  s += dpp_f64<kDppMirror>(s);
-  const double lse = md + log(s);
-  bool taken = false;
-  float my_v = 0.f;
-  int my_n = 0;
-  double my_p = 0.0, psum = 0.0;
-  for (int j = 0; j < k; ++j) {
-    const bool cand = has && !taken;
-    float bv = cand ? v : -INFINITY;
-    int bn = cand ? c : 0x7fffffff;
-    argmax_step<kDppXor1>(bv, bn);
-    argmax_step<kDppXor2>(bv, bn);
-    argmax_step<kDppHalfMirror>(bv, bn);
-    argmax_step<kDppMirror>(bv, bn);
-    if (bn == c) taken = true;
-    const double pj = exp((double)bv - md);
-    psum += pj;
-    if (c == j) {
-      my_v = bv;
-      my_n = bn;
-      my_p = pj;
-    }
-  }
-  if (active && c < k) {
-    idx[(size_t)t * k + c] = my_n;
-    w[(size_t)t * k + c] = (float)(my_p / psum);
-    key[(size_t)t * k + c] = (double)my_v - lse;
-  }
-}
 
 // ---------------------------------------------------------------- expert choice
 // Every (token, expert) pair is a candidate (page "Mixture of Experts: Scaling
@@ -473,6 +261,108 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
     }
   } else {
     for (int r = wv; r < 16; r += WAVES) {
+      const int t = t0 + r;
+      if (t < T) topk_row(&Ls[r][0], N, k, t, logits, idx, w, key);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- split-K router
+// Few tokens (T <= 64), N <= 64, d % 128 == 0. The kernels above give each
+// block 16 tokens and all of K, so a batch this small runs on one to four
+// CUs, each reading all of W_g. Here K is split over S blocks per 16 tokens,
+// so the reads of x and W_g spread over the chip, and a second small kernel
+// adds the S partial logits in a fixed order (s = 0, 1, ...), adds the bias
+// and runs the top-k.
+//
+// Block (s, g), 4 waves: tokens 16g..16g+15; wave v takes the 32-wide K steps
+// (4s + v)*spw ... (4s + v + 1)*spw - 1, the loads of up to kSkU steps in
+// flight together. The B fragment (8 consecutive k of one expert per lane) is
+// gathered with 2-byte loads straight from the N-contiguous W_g; a block's K
+// range of W_g is contiguous, so the gathers of a wave fall in a few cache
+// lines. The 4 waves' tiles are added in LDS in wave order and written as
+// part[s][16g + r][n] (fp32, n < NP). Few partials (S <= 8 up to d = 4096)
+// keep the single block that adds them short.
+constexpr int kSkU = 4;  // K steps of loads in flight per wave
+template <int NT>
+__global__ __launch_bounds__(256) void router_splitk_kernel(const bf16* __restrict__ x,
+                                                            const bf16* __restrict__ Wg, int T,
+                                                            int d, int N, int spw,
+                                                            float* __restrict__ part) {
+  constexpr int NP = NT * 16;
+  __shared__ float red[4][16][NP];
+  const int l = lane_id();
+  const int wv = threadIdx.x / kWave;
+  const int g4 = l >> 4, c16 = l & 15;
+  const int tg = blockIdx.y;
+  const int row = tg * 16 + c16;
+  const bool rok = row < T;
+  const bf16* xr = x + (size_t)(rok ? row : 0) * d;
+  const int nsteps = d / 32;
+  const int st0 = (blockIdx.x * 4 + wv) * spw, st1 = min(nsteps, st0 + spw);
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int sb = st0; sb < st1; sb += kSkU) {
+    bf16x8 a[kSkU], b[kSkU][NT];
+#pragma unroll
+    for (int u = 0; u < kSkU; ++u) {
+      const bool ok = sb + u < st1;
+      const int kk = (sb + u) * 32 + 8 * g4;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) a[u][q] = (bf16)0.f;
+      if (ok && rok) a[u] = *(const bf16x8*)(xr + kk);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int n = 16 * j + c16;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          b[u][j][q] = (ok && n < N) ? Wg[(size_t)(kk + q) * N + n] : (bf16)0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSkU; ++u)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][j], acc[j], 0, 0, 0);
+  }
+  // D layout: lane holds column 16j + l%16, rows 4g + i
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wv][4 * g4 + i][16 * j + c16] = acc[j][i];
+  __syncthreads();
+  const size_t Tp = (size_t)gridDim.y * 16;
+  for (int i = threadIdx.x; i < 16 * NP; i += 256) {
+    const int r = i / NP, n = i - r * NP;
+    const float v = ((red[0][r][n] + red[1][r][n]) + red[2][r][n]) + red[3][r][n];
+    part[((size_t)blockIdx.x * Tp + tg * 16 + r) * NP + n] = v;
+  }
+}
+
+// Sum of the S partial tiles, bias, top-k: 16 tokens per block.
+template <int NT>
+__global__ __launch_bounds__(256) void router_splitk_topk_kernel(
+    const float* __restrict__ part, int S, const float* __restrict__ bias, int T, int N, int k,
+    float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ w,
+    double* __restrict__ key) {
+  constexpr int NP = NT * 16;
+  __shared__ float Ls[16][NP + 4];
+  const int t0 = blockIdx.x * 16;
+  const size_t stride = (size_t)gridDim.x * 16 * NP;
+  for (int i = threadIdx.x; i < 16 * NP; i += 256) {
+    const int r = i / NP, n = i - r * NP;
+    const float sum = splitk_logit<32>(part + (size_t)(t0 + r) * NP + n, S, stride);
+    Ls[r][n] = sum + ((bias != nullptr && n < N) ? bias[n] : 0.f);
+  }
+  __syncthreads();
+  const int wv = threadIdx.x / kWave;
+  if constexpr (NT == 1) {
+    const int r = wv * 4 + (lane_id() >> 4);
+    const int t = t0 + r;
+    topk_row16(&Ls[r][0], t < T, N, k, t, logits, idx, w, key);
+  } else {
+    for (int r = wv; r < 16; r += 4) {
       const int t = t0 + r;
       if (t < T) topk_row(&Ls[r][0], N, k, t, logits, idx, w, key);
     }
@@ -980,7 +870,50 @@ void launch_skinny(bool wide, const void* x, const bf16* Wsrc, const float* bias
                        (const bf16*)x, Wsrc, bias, T, d, N, k, logits, idx, w, key);
 }
 
+bool splitk_route_ok(int T, int d, int N, int dtype) {
+  return dtype == kBF16 && T >= 1 && T <= 64 && N <= 64 && d % 128 == 0;
+}
+
+// S = cdiv(d/128, spw) <= d/128 partial tiles of 16*cdiv(T,16) <= 64 rows x NP
+// fp32: at most 2*d*NP bytes, the size of the router scratch.
+template <int NT>
+void launch_splitk_partials(const void* x, const bf16* W_g, int T, int d, int N, float* part,
+                            int* S_out, hipStream_t st) {
+  const int kb = d / 128;
+  const int spw = cdiv(kb, 8);  // at most 8 partial tiles to add
+  const int S = cdiv(kb, spw);
+  hipLaunchKernelGGL(router_splitk_kernel<NT>, dim3(S, cdiv(T, 16)), dim3(256), 0, st,
+                     (const bf16*)x, W_g, T, d, N, spw, part);
+  *S_out = S;
+}
+
 }  // namespace
+
+hipError_t launch_route_partials(const void* x, const void* W_g, const float* bias, int T, int d,
+                                 int N, int dtype, float* logits, int32_t* idx, float* w,
+                                 double* key, void* scratch, hipStream_t st, RoutePartials* rp) {
+  *rp = RoutePartials{};
+  if (!splitk_route_ok(T, d, N, dtype)) return hipSuccess;
+  const int NP = cdiv(N, 16) * 16;
+  float* part = (float*)scratch;
+  int S = 0;
+  switch (NP / 16) {
+    case 1: launch_splitk_partials<1>(x, (const bf16*)W_g, T, d, N, part, &S, st); break;
+    case 2: launch_splitk_partials<2>(x, (const bf16*)W_g, T, d, N, part, &S, st); break;
+    case 3: launch_splitk_partials<3>(x, (const bf16*)W_g, T, d, N, part, &S, st); break;
+    default: launch_splitk_partials<4>(x, (const bf16*)W_g, T, d, N, part, &S, st); break;
+  }
+  rp->part = part;
+  rp->S = S;
+  rp->Tp = cdiv(T, 16) * 16;
+  rp->NP = NP;
+  rp->bias = bias;
+  rp->logits = logits;
+  rp->idx = idx;
+  rp->w = w;
+  rp->key = key;
+  return hipGetLastError();
+}
 
 size_t route_scratch_bytes(int d, int N, int dtype) {
   if (dtype != kBF16) return 0;
@@ -1014,6 +947,22 @@ hipError_t launch_route(const void* x, const void* W_g, const float* bias, int T
     return hipGetLastError();
   }
   const int NP = cdiv(N, 16) * 16;
+  if (splitk_route_ok(T, d, N, dtype)) {
+    // few tokens: K split over many blocks (partials in the router scratch),
+    // then the sum of the partials and the top-k, 16 tokens per block
+    RoutePartials rp;
+    const hipError_t e = launch_route_partials(x, W_g, bias, T, d, N, dtype, logits, idx, w, key,
+                                               scratch, st, &rp);
+    if (e != hipSuccess) return e;
+    const dim3 g(cdiv(T, 16)), b(256);
+    switch (NP / 16) {
+      case 1: hipLaunchKernelGGL(router_splitk_topk_kernel<1>, g, b, 0, st, rp.part, rp.S, bias, T, N, k, logits, idx, w, key); break;
+      case 2: hipLaunchKernelGGL(router_splitk_topk_kernel<2>, g, b, 0, st, rp.part, rp.S, bias, T, N, k, logits, idx, w, key); break;
+      case 3: hipLaunchKernelGGL(router_splitk_topk_kernel<3>, g, b, 0, st, rp.part, rp.S, bias, T, N, k, logits, idx, w, key); break;
+      default: hipLaunchKernelGGL(router_splitk_topk_kernel<4>, g, b, 0, st, rp.part, rp.S, bias, T, N, k, logits, idx, w, key); break;
+    }
+    return hipGetLastError();
+  }
   if (NP <= 64 && d % 8 == 0 && wt_lds_bytes(d, N) <= wt_lds_budget(NP)) {
     // few experts, small W_g: each block stages W_g^T in LDS (no transpose launch)
     switch (NP / 16) {

@@ -69,6 +69,15 @@ CASES = [
     ("small_route_N40", 48, 256, 128, 40, 4, 0.0, "bf16", True, "normal0.5", 0),
     ("small_route_N64_k16", 64, 128, 64, 64, 16, 0.0, "bf16", False, "zipf1.1", 0),
     ("small_route_T17_split", 17, 512, 256, 8, 2, 0.0, "bf16", True, "none", SPLIT),
+    # few tokens with d % 128 == 0: the split-K router, whose partial logits
+    # the dispatch block adds before its top-k (forward) or a top-k kernel
+    # adds (moe_route); with capacity drops (the selection after it), a ragged
+    # 37 tokens over 2 column tiles, one token with one partial, and d = 16384
+    # (two K steps per wave, 64 partials)
+    ("few_tokens_drops", 64, 256, 128, 8, 2, 0.5, "bf16", True, "zipf1.1", 0),
+    ("few_tokens_N24_ragged", 37, 384, 128, 24, 3, 0.75, "bf16", False, "normal0.5", 0),
+    ("few_tokens_single", 1, 128, 64, 8, 2, 0.0, "bf16", False, "none", 0),
+    ("few_tokens_long_d", 5, 16384, 64, 16, 4, 0.0, "bf16", True, "none", 0),
     ("single_token", 1, 64, 64, 8, 2, 0.0, "bf16", False, "none", 0),
     ("capacity_one", 64, 64, 64, 8, 2, 0.01, "bf16", False, "zipf1.1", 0),
     ("many_experts_N1000", 512, 64, 64, 1000, 16, 1.0, "bf16", False, "none", 0),

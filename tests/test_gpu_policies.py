@@ -40,6 +40,8 @@ POLICY_CASES = [
     ("fine_small_zipf", 2048, 128, 64, 64, 8, 1.25, "bf16", False, "zipf1.1"),
     ("capacity_one", 64, 64, 64, 8, 2, 0.01, "bf16", False, "zipf1.1"),
     ("decode_path_drops", 96, 256, 384, 8, 2, 0.5, "bf16", True, "normal0.5"),
+    # few tokens with d % 128 == 0: routing finished inside the dispatch block
+    ("few_tokens_drops", 64, 256, 128, 8, 2, 0.5, "bf16", True, "zipf1.1"),
 ]
 
 
