@@ -66,7 +66,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
                                                         int4* __restrict__ tiles2,
                                                         int32_t* __restrict__ counts) {
   // counts[4 .. 19]: the two GEMMs' per-XCD work-queue counters, zeroed here
-  if (threadIdx.x < 16) counts[4 + threadIdx.x] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < 16) counts[4 + threadIdx.x] = 0;
   __shared__ int mtoff[kMaxN + 1];
   __shared__ int rbeg[kMaxN], rcnt[kMaxN];  // each expert's rows, clamped to the plan
   __shared__ int tmp[17];
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
     const int mx = pass == 0 ? max1 : max2;
     int4* tl = pass == 0 ? tiles1 : tiles2;
     const int total = min(total_mt * NTn, mx);
-    for (int p = threadIdx.x; p < total; p += 1024) {
+    for (int p = blockIdx.x * 1024 + threadIdx.x; p < total; p += gridDim.x * 1024) {
       if ((expert_major >> pass) & 1) {
         int lo = 0, hi = N - 1;  // expert: largest e with mtoff[e] * NTn <= p
         while (lo < hi) {
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
       const int nt = band * 8 + r;
       tl[p] = make_int4(e, rbeg[e] + mt * BM, min(BM, rcnt[e] - mt * BM), nt);
     }
-    if (threadIdx.x == 0) counts[pass] = total;
+    if (blockIdx.x == 0 && threadIdx.x == 0) counts[pass] = total;
   }
 }
 
@@ -793,7 +793,11 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
   // expert-major for the second, experts of several m-tiles the reverse
   const bool single_mt = (C < T ? C : T) <= pl.BM;
   const int em = pl.path == kPathTiledM ? (single_mt ? 2 : 1) : 0;
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, off, N, S_max, C < T ? C : T,
+  // every block repeats the per-expert scan (N <= 1024) and writes its share
+  // of the tile entries
+  const int mx = pl.max1 > pl.max2 ? pl.max1 : pl.max2;
+  const int sgrid = mx <= 1024 ? 1 : (cdiv(mx, 1024) < 32 ? cdiv(mx, 1024) : 32);
+  hipLaunchKernelGGL(schedule_kernel, dim3(sgrid), dim3(1024), 0, st, off, N, S_max, C < T ? C : T,
                      pl.BM, cdiv(d_ff, pl.BN1), cdiv(d, pl.BN2), pl.max1, pl.max2, em, t1, t2,
                      s.counts);
   if (pl.path == kPathF32) {
