@@ -55,9 +55,12 @@ namespace {
 // Rows are 64 bytes (32 bf16 of K); the 16-byte chunk c of row r sits at
 // position c ^ ((r >> 2) & 3), which keeps the b128 fragment reads of 16
 // consecutive rows on distinct banks. Stage kt+RING-1 is requested while stage
-// kt is multiplied; one workgroup barrier per stage, taken mid-stage so that
-// the next stage's first fragments are read while the current stage's last
-// MFMAs run.
+// kt is multiplied; one workgroup barrier per stage, taken mid-stage. A
+// stage's fragment reads are spread over both halves of the steps around that
+// barrier: its first half of token blocks and its weight blocks during the
+// previous step's second half of MFMAs (after the barrier that makes the stage
+// visible), its second half of token blocks during its own first half of MFMAs
+// (Mixtral-shaped first GEMM -3% against reading them all in one half).
 //
 // Persistent: the grid holds one wave of resident workgroups; workgroup b runs
 // on XCD b % 8 and walks the tiles of that XCD's contiguous share of the tile
@@ -440,16 +443,27 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
   bf16x8 af[2][MT], bfr[2][NTW], alf[ALO ? 2 : 1][ALO ? MT : 1];
   // NA: token blocks of this wave that hold rows of the tile (a partly filled
   // tile skips the fragment reads and MFMAs of the empty ones)
-  auto read_frags = [&](int kt, int set, auto na_c) {
+  // lo: token blocks [0, NA/2) and the weight blocks; hi: blocks [NA/2, NA)
+  auto read_frags_lo = [&](int kt, int set, auto na_c) {
     constexpr int NA = decltype(na_c)::value;
     const unsigned char* st = smem + (kt % RING) * STAGE;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) af[set][i] = *(const bf16x8*)(st + A_OFF + aoffs[i]);
+    for (int i = 0; i < NA / 2; ++i) af[set][i] = *(const bf16x8*)(st + A_OFF + aoffs[i]);
 #pragma unroll
     for (int j = 0; j < NTW; ++j) bfr[set][j] = *(const bf16x8*)(st + B_OFF + boffs[j]);
     if constexpr (ALO) {
 #pragma unroll
-      for (int i = 0; i < NA; ++i) alf[set][i] = *(const bf16x8*)(st + L_OFF + aoffs[i]);
+      for (int i = 0; i < NA / 2; ++i) alf[set][i] = *(const bf16x8*)(st + L_OFF + aoffs[i]);
+    }
+  };
+  auto read_frags_hi = [&](int kt, int set, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
+    const unsigned char* st = smem + (kt % RING) * STAGE;
+#pragma unroll
+    for (int i = NA / 2; i < NA; ++i) af[set][i] = *(const bf16x8*)(st + A_OFF + aoffs[i]);
+    if constexpr (ALO) {
+#pragma unroll
+      for (int i = NA / 2; i < NA; ++i) alf[set][i] = *(const bf16x8*)(st + L_OFF + aoffs[i]);
     }
   };
 
@@ -479,7 +493,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
   auto kloop = [&](auto na_c) {
     constexpr int NA = decltype(na_c)::value;
     constexpr int H = NA / 2;
-    constexpr int NR = NA + NTW + (ALO ? NA : 0);  // fragment reads per stage
+    constexpr int NRL = H + NTW + (ALO ? H : 0);  // reads of the next stage (second half)
+    constexpr int NRH = (NA - H) * (ALO ? 2 : 1);  // reads of this stage's blocks H.. (first half)
     constexpr int M1 = H * NTW * (ALO ? 2 : 1);    // MFMAs per half
     using lo0 = std::integral_constant<int, 0>;
     using mid = std::integral_constant<int, H>;
@@ -497,29 +512,39 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
       } else {
         issue_part(kt + RING - 2, 1);
       }
+      read_frags_hi(kt, SET, na_c);
       mma(SET, lo0{}, mid{});
       if constexpr (M1 > 0) {
-        // those copies spread over the first half
+        // those copies and this stage's remaining fragment reads spread over
+        // the first half
+        constexpr int G1N = M1 / (NRH + C1) > 0 ? M1 / (NRH + C1) : 1;
+#pragma unroll
+        for (int q = 0; q < NRH; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, G1N, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
 #pragma unroll
         for (int q = 0; q < C1; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, M1 / C1 > 0 ? M1 / C1 : 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, G1N, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      // stage kt+1 has landed (only the stages issued after it may still fly)
-      // and no wave still reads the slot of stage kt-1
+      // stage kt+1 has landed (only the stages issued after it may still fly),
+      // this wave's reads of stage kt are done, and no wave still reads the
+      // slot of stage kt-1
       vm_wait_n<(EARLY ? RING - 2 : RING - 3) * LPS>();
+      lgkm_wait0();
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(kt + 1, SET ^ 1, na_c);  // past the last stage: reads a dead slot, never used
+      read_frags_lo(kt + 1, SET ^ 1, na_c);  // past the last stage: reads a dead slot, never used
       if constexpr (!EARLY) issue_part(kt + RING - 1, 0);
       mma(SET, mid{}, hi1{});
       if constexpr (M1 > 0) {
         // one MFMA, one fragment read of the next stage, ...; then the
         // token-row copies of stage kt+RING-1
 #pragma unroll
-        for (int q = 0; q < NR; ++q) {
+        for (int q = 0; q < NRL; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
@@ -530,11 +555,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      // the next stage's fragments are complete before the next step's MFMAs
-      // (and before this wave passes the next barrier)
-      lgkm_wait0();
     };
-    read_frags(0, 0, na_c);
+    read_frags_lo(0, 0, na_c);
     int kt = 0;
     for (; kt + 1 < nks; kt += 2) {
       step(kt, std::integral_constant<int, 0>{});
