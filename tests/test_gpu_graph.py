@@ -17,6 +17,9 @@ CASES = [
     # name, T, d, d_ff, N, k, cf, dtype, bias, skew, flag names
     ("switch_like_drops", 1024, 128, 256, 16, 1, 1.0, "bf16", False, "normal0.5", ("HIDDEN_SPLIT",)),
     ("decode_splitk", 24, 512, 4096, 4, 2, 0.0, "bf16", True, "none", ()),
+    # few tokens with capacity drops: routing finished in the dispatch block,
+    # then the selection
+    ("few_tokens_drops", 64, 256, 128, 8, 2, 0.5, "bf16", True, "zipf1.1", ()),
     ("prefill_tiles", 2048, 256, 512, 2, 1, 0.0, "bf16", False, "none", ()),
     ("expert_choice", 256, 64, 64, 16, 2, 0.5, "bf16", False, "zipf1.1",
      ("EXPERT_CHOICE", "IDENTITY_FALLBACK")),
