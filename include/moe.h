@@ -170,8 +170,9 @@ int moe_shared_expert(const void* x, const void* W1s, const void* b1s, const voi
  *        topk_w   [T,k] fp32, renormalised softmax scores, sum_j = 1
  *        topk_key [T,k] fp64, log softmax probability L[t,e] - logsumexp_t(L)
  *                 computed in fp64 from the fp32 logits (the capacity rank)
- * Needs workspace for bf16 (a transposed copy of W_g; moe_workspace_bytes is
- * enough); fp32 needs none (workspace may be NULL). */
+ * Needs workspace for bf16 (a transposed copy of W_g, or for T <= 64 and
+ * N <= 64 the fp32 partial logits of a K split, at most the same size;
+ * moe_workspace_bytes is enough); fp32 needs none (workspace may be NULL). */
 int moe_route(const void* x, const void* W_g, const float* logit_bias,
               int T, int d, int N, int k, int dtype,
               float* logits, int32_t* topk_idx, float* topk_w, double* topk_key,

@@ -281,8 +281,8 @@ __global__ __launch_bounds__(WAVES * 64) void router_skinny_kernel(
 // gathered with 2-byte loads straight from the N-contiguous W_g; a block's K
 // range of W_g is contiguous, so the gathers of a wave fall in a few cache
 // lines. The 4 waves' tiles are added in LDS in wave order and written as
-// part[s][16g + r][n] (fp32, n < NP). Few partials (S <= 8 up to d = 4096)
-// keep the single block that adds them short.
+// part[s][16g + r][n] (fp32, n < NP). At most 8 partial tiles (spw grows with
+// d) keep the single block that adds them short.
 constexpr int kSkU = 4;  // K steps of loads in flight per wave
 template <int NT>
 __global__ __launch_bounds__(256) void router_splitk_kernel(const bf16* __restrict__ x,
