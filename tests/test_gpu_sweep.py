@@ -39,6 +39,32 @@ def _draw(i: int):
 CASES = [_draw(i) for i in range(32)]
 
 
+def _draw_few(i: int):
+    """Few tokens (T <= 64), N <= 64, bf16, d % 128 == 0: the split-K router and
+    the block that adds its partials, routes and dispatches."""
+    rng = np.random.default_rng(9500 + i)
+    N = int(rng.choice([1, 2, 5, 8, 16, 17, 31, 48, 64]))
+    k = int(rng.integers(1, min(N, 16) + 1))
+    T = int(rng.choice([1, 5, 16, 17, 33, 48, 64]))
+    d = int(rng.integers(1, 9)) * 128
+    d_ff = int(rng.integers(1, 33)) * 16
+    cf = float(rng.choice([0.0, 0.5, 1.0, 1.25]))
+    bias = bool(rng.random() < 0.5)
+    skew = str(rng.choice(["none", "normal0.5", "zipf1.1"]))
+    flags = []
+    if rng.random() < 0.3:
+        flags.append("HIDDEN_SPLIT")
+    for f in ("FIRST_COME", "RENORM_SURVIVORS", "IDENTITY_FALLBACK"):
+        if rng.random() < 0.25:
+            flags.append(f)
+    w = Workload(f"few{i}", T=T, d=d, d_ff=d_ff, N=N, k=k, capacity_factor=cf, dtype="bf16",
+                 ffn_bias=bias, skew=skew, seed=100 + i)
+    return w, tuple(flags)
+
+
+FEW_CASES = [_draw_few(i) for i in range(12)]
+
+
 @pytest.fixture(scope="module")
 def lib():
     if not torch.cuda.is_available():
@@ -51,6 +77,16 @@ def lib():
 def test_sweep(lib, i):
     from gpu_util import run_and_compare
     w, fnames = CASES[i]
+    flags = 0
+    for f in fnames:
+        flags |= getattr(lib, "MOE_FLAG_" + f)
+    run_and_compare(w, lib, flags=flags)
+
+
+@pytest.mark.parametrize("i", range(len(FEW_CASES)), ids=[c[0].name for c in FEW_CASES])
+def test_sweep_few_tokens(lib, i):
+    from gpu_util import run_and_compare
+    w, fnames = FEW_CASES[i]
     flags = 0
     for f in fnames:
         flags |= getattr(lib, "MOE_FLAG_" + f)
