@@ -9,7 +9,9 @@
 // is added to every token last (after the fallback, which replaces only the
 // routed part), so y is still rounded once. The gate-scaled expert outputs
 // arrive in fp32. Each thread owns 16 bytes of one output row: coalesced fp32
-// loads per kept pick, one 16-byte store.
+// loads per kept pick, one 16-byte store. When the second expert GEMM wrote
+// the rows of tokens that kept a single pick straight into y (no fallback, no
+// shared expert), those tokens are skipped here.
 #include "moe_common.h"
 
 namespace moe {
@@ -42,29 +44,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ inv, int T_,
                                                       int d, int k, const XT* __restrict__ x,
                                                       const float* __restrict__ sh,
-                                                      T* __restrict__ y) {
+                                                      T* __restrict__ y, int skip_single) {
   constexpr int V = 16 / sizeof(T);  // output elements per 16-byte store
   const int vpr = d / V;             // vectors per row (d % 8 == 0)
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long long)T_ * vpr) return;
   const int t = (int)(gid / vpr);
   const int c = (int)(gid - (long long)t * vpr) * V;
+  const int32_t* it = inv + (size_t)t * k;
+  // skip_single: a token with exactly one kept pick has its row written by
+  // the second expert GEMM already (counted from the first group's slot
+  // indices when k <= 8, else in a pass of its own)
+  constexpr int G = 8;
+  if (skip_single && k > G) {
+    int kept = 0;
+    for (int j = 0; j < k; ++j) kept += it[j] >= 0 ? 1 : 0;
+    if (kept == 1) return;
+  }
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  const int32_t* it = inv + (size_t)t * k;
   bool any = false;
   // picks in groups of 8 (all of them for k <= 8): the slot indices first,
   // then every kept pick's row load issued before the first add (one round
   // trip per group), then the sums in fixed pick order
-  constexpr int G = 8;
   for (int j0 = 0; j0 < k; j0 += G) {
     int s[G];
+    int kept = 0;
 #pragma unroll
     for (int q = 0; q < G; ++q) {
       s[q] = j0 + q < k ? it[j0 + q] : -1;
       any |= s[q] >= 0;
+      kept += s[q] >= 0 ? 1 : 0;
     }
+    if (skip_single && k <= G && kept == 1) return;
     f32x4 v[G][V / 4];
 #pragma unroll
     for (int q = 0; q < G; ++q) {
@@ -209,7 +222,8 @@ hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, in
 
 hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d, int k,
                           int y_dtype, const void* x, int x_dtype, const float* sh, void* y,
-                          hipStream_t st) {
+                          hipStream_t st, bool skip_single) {
+  const int ss = skip_single ? 1 : 0;
   if (T == 0) return hipSuccess;
   const int V = y_dtype == kF32 ? 4 : 8;
   const long long n = (long long)T * (d / V);
@@ -218,17 +232,17 @@ hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d
   if (y_dtype == kF32) {
     if (x_dtype == kBF16)
       hipLaunchKernelGGL((combine_kernel<float, bf16>), dim3(blocks), dim3(256), 0, st, so, inv,
-                         T, d, k, (const bf16*)x, sh, (float*)y);
+                         T, d, k, (const bf16*)x, sh, (float*)y, ss);
     else
       hipLaunchKernelGGL((combine_kernel<float, float>), dim3(blocks), dim3(256), 0, st, so, inv,
-                         T, d, k, (const float*)x, sh, (float*)y);
+                         T, d, k, (const float*)x, sh, (float*)y, ss);
   } else {
     if (x_dtype == kBF16)
       hipLaunchKernelGGL((combine_kernel<bf16, bf16>), dim3(blocks), dim3(256), 0, st, so, inv,
-                         T, d, k, (const bf16*)x, sh, (bf16*)y);
+                         T, d, k, (const bf16*)x, sh, (bf16*)y, ss);
     else
       hipLaunchKernelGGL((combine_kernel<bf16, float>), dim3(blocks), dim3(256), 0, st, so, inv,
-                         T, d, k, (const float*)x, sh, (bf16*)y);
+                         T, d, k, (const float*)x, sh, (bf16*)y, ss);
   }
   return hipGetLastError();
 }

@@ -28,6 +28,10 @@
 //                 LDS-DMA ring, split K with a fixed-order reduction), or by
 //                 decode_bf16_kernel below when K % 128 != 0.
 //   fp32        : FMA tiles (64 x 64), same schedule mechanism.
+// Direct rows (tiled bf16, when the caller passes y): the schedule kernel
+// marks each slot whose token kept no other pick, and GEMM2's epilogue writes
+// that row straight into y (0 + gate * (acc + b2), as the combine would),
+// leaving the combine only the tokens with zero or several kept picks.
 // With the hidden-split flag, GEMM1 also stores the bf16 residual h - bf16(h)
 // of each hidden activation and GEMM2 runs a second MFMA on it, so GEMM2 sees
 // the hidden layer to about 16 significant bits instead of 8 (twice GEMM2's
@@ -68,7 +72,9 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
                                                         int expert_major,
                                                         int4* __restrict__ tiles1,
                                                         int4* __restrict__ tiles2,
-                                                        int32_t* __restrict__ counts) {
+                                                        int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ inv, int T,
+                                                        int kp, int32_t* __restrict__ dmap) {
   // counts[4 .. 19]: the two GEMMs' per-XCD work-queue counters, zeroed here
   if (blockIdx.x == 0 && threadIdx.x < 16) counts[4 + threadIdx.x] = 0;
   __shared__ int mtoff[kMaxN + 1];
@@ -164,6 +170,33 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
       tl[p] = make_int4(e, rbeg[e] + mt * BM, min(BM, rcnt[e] - mt * BM), nt);
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) counts[pass] = total;
+  }
+  // direct-row map (dmap not null), one thread per token: each kept slot of
+  // token t gets t when it is the token's only kept pick, else -1
+  if (dmap != nullptr) {
+    for (int t = blockIdx.x * 1024 + threadIdx.x; t < T; t += gridDim.x * 1024) {
+      const int32_t* it = inv + (size_t)t * kp;
+      if (kp <= 16) {
+        // all of the token's slot indices requested at once
+        int sl[16];
+        int kept = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          sl[j] = j < kp ? it[j] : -1;
+          kept += sl[j] >= 0 ? 1 : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (sl[j] >= 0 && sl[j] < S_max) dmap[sl[j]] = kept == 1 ? t : -1;
+      } else {
+        int kept = 0;
+        for (int j = 0; j < kp; ++j) kept += it[j] >= 0 ? 1 : 0;
+        for (int j = 0; j < kp; ++j) {
+          const int sl = it[j];
+          if (sl >= 0 && sl < S_max) dmap[sl] = kept == 1 ? t : -1;
+        }
+      }
+    }
   }
 }
 
@@ -609,11 +642,16 @@ size_t ring_part_floats(int BM, int BN, bool alo, int max_tiles) {
 
 // One grouped GEMM launch: the LDS-DMA ring kernel (+ the reduction of its
 // split tail) when K % 32 == 0, else the register-staged kernel (any K % 8 == 0).
+// dr (second GEMM, ring kernel only): direct rows of single-pick tokens, or
+// null.
 template <int BM, int BN, int WM, int WN, bool G1, bool SPLIT>
 void launch_gemm(const bf16* A, const bf16* A_lo, const int32_t* perm, int k, const bf16* W,
                  const bf16* bias, const float* gate, const int4* tl, const int32_t* cnt, int K,
                  int Nout, int grid, void* out, bf16* out_lo, float* part, hipStream_t st,
-                 int* wq, bool packed) {
+                 int* wq, bool packed, const DirectRows* dr = nullptr) {
+  const int32_t* dmap = dr != nullptr ? dr->map : nullptr;
+  void* ydir = dr != nullptr ? dr->y : nullptr;
+  const int ybf16 = dr != nullptr && dr->y_dtype == kBF16 ? 1 : 0;
   constexpr int NTH = (BM / WM) * (BN / WN) * kWave;
   constexpr bool ALO = SPLIT && !G1;
   if (K % kRK == 0) {
@@ -629,13 +667,14 @@ void launch_gemm(const bf16* A, const bf16* A_lo, const int32_t* perm, int k, co
     hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, WN, MODE, SPLIT, R, EARLY>), dim3(pgrid),
                        dim3(NTH), lds, st, A, A_lo, perm, k, W, (const void*)bias, gate, tl, cnt, K,
                        Nout, out, out_lo, 0, 0, wq != nullptr ? nullptr : part, wq,
-                       packed ? 1 : 0);
+                       packed ? 1 : 0, dmap, ydir, ybf16);
     if (part != nullptr && wq == nullptr) {
       // at most per-1 tail tiles per XCD, BM*BN/4/256 group blocks each
       const int work = 8 * (pgrid / 8) * (BM * BN / 4 / kReduceThreads);
       hipLaunchKernelGGL((ring_reduce_kernel<BM, BN, WM, WN, MODE, SPLIT>),
                          dim3(work < 4096 ? work : 4096), dim3(kReduceThreads), 0, st, part, pgrid,
-                         (const void*)bias, gate, tl, cnt, K, Nout, out, out_lo);
+                         (const void*)bias, gate, tl, cnt, K, Nout, out, out_lo, dmap, ydir,
+                         ybf16);
     }
   } else {
     const size_t lds = (size_t)2 * (BM + BN + (ALO ? BM : 0)) * kLdsRow * sizeof(bf16);
@@ -649,7 +688,8 @@ template <int BM, int BN, int WM, int WN, bool SPLIT>
 hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, const void* W1,
                         const void* b1, const void* W2, const void* b2, int d, int d_ff, int k,
                         const Plan& pl, void* hid, bf16* hid_lo, const int4* t1, const int4* t2,
-                        const int32_t* cnts, void* slot_out, float* part, hipStream_t st) {
+                        const int32_t* cnts, void* slot_out, float* part, hipStream_t st,
+                        const DirectRows* dr) {
   const int g1 = cdiv(pl.max1 > 0 ? pl.max1 : 1, 8) * 8;
   const int g2 = cdiv(pl.max2 > 0 ? pl.max2 : 1, 8) * 8;
   // A GEMM with many tiles (at least four per CU: the Mixtral-shaped first
@@ -668,7 +708,7 @@ hipError_t launch_tiled(const void* x, const int32_t* perm, const float* gate, c
   launch_gemm<BM, BN, WM, WN, false, SPLIT>((const bf16*)hid, hid_lo, nullptr, k,
                                             (const bf16*)W2, (const bf16*)b2, gate, t2, cnts + 1,
                                             d_ff, d, g2, slot_out, nullptr, part, st, wq2,
-                                            pl.packed);
+                                            pl.packed, dr);
   profile_mark(5, st);
   return hipGetLastError();
 }
@@ -780,14 +820,17 @@ void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max
     pn = ring_part_floats(pl.BM, pl.BN1, false, mx);
   }
   s->part = pn ? c.take<float>(pn) : nullptr;
+  s->direct = (pl.path == kPathTiledL || pl.path == kPathTiledM) ? c.take<int32_t>(rows) : nullptr;
 }
 
 hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* off,
                              const float* gate, const void* W1, const void* b1, const void* W2,
                              const void* b2, int T, int d, int d_ff, int N, int k, int C,
                              int S_max, int dtype, int flags, void* slot_out,
-                             const FfnScratch& s, hipStream_t st, SplitK* defer) {
+                             const FfnScratch& s, hipStream_t st, SplitK* defer,
+                             DirectRows* dr) {
   if (defer != nullptr) defer->nsplit = 1;
+  if (dr != nullptr) dr->used = false;
   if (T == 0 || S_max == 0) return hipSuccess;
   const Plan pl = make_plan(T, d, d_ff, N, k, C, S_max, dtype, flags);
   int4* t1 = (int4*)s.tiles;
@@ -812,10 +855,22 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
   // every block repeats the per-expert scan (N <= 1024) and writes its share
   // of the tile entries
   const int mx = pl.max1 > pl.max2 ? pl.max1 : pl.max2;
-  const int sgrid = mx <= 1024 ? 1 : (cdiv(mx, 1024) < 32 ? cdiv(mx, 1024) : 32);
+  int sgrid = mx <= 1024 ? 1 : (cdiv(mx, 1024) < 32 ? cdiv(mx, 1024) : 32);
+  // direct rows: the second GEMM on the LDS ring (bf16, d_ff % 32 == 0) writes
+  // the rows of single-pick tokens into y
+  const bool direct = dr != nullptr && dr->y != nullptr && dr->inv != nullptr &&
+                      s.direct != nullptr && d_ff % kRK == 0 &&
+                      (pl.path == kPathTiledL || pl.path == kPathTiledM);
+  if (direct) {
+    dr->map = s.direct;
+    dr->used = true;
+    // a block per 1024 tokens for the map (up to 64)
+    const int tg = cdiv(T, 1024) < 64 ? cdiv(T, 1024) : 64;
+    sgrid = sgrid > tg ? sgrid : tg;
+  }
   hipLaunchKernelGGL(schedule_kernel, dim3(sgrid), dim3(1024), 0, st, off, N, S_max, C < T ? C : T,
                      pl.BM, cdiv(d_ff, pl.BN1), cdiv(d, pl.BN2), pl.max1, pl.max2, em, t1, t2,
-                     s.counts);
+                     s.counts, direct ? dr->inv : nullptr, T, k, direct ? s.direct : nullptr);
   if (pl.path == kPathF32) {
     profile_mark(3, st);
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(pl.max1 > 0 ? pl.max1 : 1), dim3(256), 0, st,
@@ -831,14 +886,14 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
   if (pl.path == kPathTiledL)
     return launch_tiled<256, 256, 128, 64, false>(x, perm, gate, W1, b1, W2, b2, d, d_ff, k, pl,
                                                    s.hidden, nullptr, t1, t2, s.counts, slot_out,
-                                                   s.part, st);
+                                                   s.part, st, direct ? dr : nullptr);
   if (pl.split)
     return launch_tiled<128, 128, 64, 64, true>(x, perm, gate, W1, b1, W2, b2, d, d_ff, k, pl,
                                                  s.hidden, lo, t1, t2, s.counts, slot_out, s.part,
-                                                 st);
+                                                 st, direct ? dr : nullptr);
   return launch_tiled<128, 128, 64, 64, false>(x, perm, gate, W1, b1, W2, b2, d, d_ff, k, pl,
                                                 s.hidden, nullptr, t1, t2, s.counts, slot_out,
-                                                s.part, st);
+                                                s.part, st, direct ? dr : nullptr);
 }
 
 namespace {

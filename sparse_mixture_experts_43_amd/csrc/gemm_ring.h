@@ -175,19 +175,38 @@ struct RingSplit {
   }
 };
 
+// Direct rows (second expert GEMM): a slot whose token kept no other pick
+// holds the token's whole output, so its row goes straight to y[t] (fp32, or
+// bf16 when ybf16) as the combine would write it, 0 + gate * (acc + b2)
+// rounded once, instead of to the slot output.
+__device__ __forceinline__ void store_direct(void* __restrict__ y, int ybf16, int t, int Nout,
+                                             int col, float w0, float w1, float w2, float w3) {
+#pragma clang fp contract(off)
+  const float a0 = 0.f + w0, a1 = 0.f + w1, a2 = 0.f + w2, a3 = 0.f + w3;
+  const size_t o = (size_t)t * Nout + col;
+  if (ybf16) {
+    *(uint2*)((bf16*)y + o) = make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
+  } else {
+    *(f32x4*)((float*)y + o) = f32x4{a0, a1, a2, a3};
+  }
+}
+
 // Epilogue of one tile from the accumulators. Lane l holds, for token block i
 // and weight block j, token row (2i + wr)*16 + (l & 15) of the tile and the 4
 // consecutive output columns wn0 + 16j + 4*(l >> 4) + r (r = 0..3). The
-// tile's gates (second expert GEMM) and biases are read from LDS, where the
-// kernel staged them (sh_gate[row], sh_bias[column - n0]); the logits mode
-// reads its fp32 bias from global memory.
+// tile's gates and direct-row tokens (second expert GEMM) and biases are read
+// from LDS, where the kernel staged them (sh_gate[row], sh_dst[row], -1 for a
+// slot output row; sh_bias[column - n0]); the logits mode reads its fp32 bias
+// from global memory.
 template <int BM, int BN, int WM, int WN, int MODE, bool SPLIT>
 __device__ __forceinline__ void ring_epilogue(const f32x4 (&acc)[WM / 16][WN / 16],
-                                              const float* sh_gate, const float* sh_bias,
-                                              int m0, int mcount, int n0, int wr, int wn0, int l,
+                                              const float* sh_gate, const int* sh_dst,
+                                              const float* sh_bias, int m0, int mcount, int n0,
+                                              int wr, int wn0, int l,
                                               const void* __restrict__ bias, int Nout,
                                               void* __restrict__ out, bf16* __restrict__ out_lo,
-                                              int ldo) {
+                                              int ldo, void* __restrict__ ydir, int ybf16) {
+#pragma clang fp contract(off)
   constexpr bool G1 = MODE == kEpiGelu;
   constexpr int MT = WM / 16, NTW = WN / 16;
 #pragma unroll
@@ -196,7 +215,11 @@ __device__ __forceinline__ void ring_epilogue(const f32x4 (&acc)[WM / 16][WN / 1
     if (r >= mcount) continue;
     const int slot = m0 + r;
     float g = 1.f;
-    if constexpr (MODE == kEpiGate) g = sh_gate[r];
+    int dst = -1;
+    if constexpr (MODE == kEpiGate) {
+      g = sh_gate[r];
+      dst = sh_dst[r];
+    }
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       const int col = n0 + wn0 + j * 16 + 4 * (l >> 4);
@@ -230,6 +253,8 @@ __device__ __forceinline__ void ring_epilogue(const f32x4 (&acc)[WM / 16][WN / 1
           const float r3 = h3 - __builtin_bit_cast(float, hi.y & 0xFFFF0000u);
           *(uint2*)(out_lo + o) = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
         }
+      } else if (dst >= 0) {
+        store_direct(ydir, ybf16, dst, Nout, col, v0 * g, v1 * g, v2 * g, v3 * g);
       } else {
         *(f32x4*)((float*)out + o) = f32x4{v0 * g, v1 * g, v2 * g, v3 * g};
       }
@@ -272,7 +297,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
     const float* __restrict__ gate, const int4* __restrict__ tiles,
     const int32_t* __restrict__ ntiles_p, int K, int Nout, void* __restrict__ out,
     bf16* __restrict__ out_lo, int M_total, int ldo, float* __restrict__ part,
-    int* __restrict__ wq, int packed) {
+    int* __restrict__ wq, int packed, const int32_t* __restrict__ dmap, void* __restrict__ ydir,
+    int ybf16) {
   constexpr bool G1 = MODE == kEpiGelu;
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int NTH = NW * kWave;
@@ -328,6 +354,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
   __shared__ int sh_claim;
   __shared__ __align__(16) float sh_gate[BM];  // the finished tile's gates (second expert GEMM)
   __shared__ __align__(16) float sh_bias[BN];  // and biases by column, for its epilogue
+  // and its direct-row tokens (dmap: token of a slot whose token kept no other
+  // pick, else -1; null: none)
+  __shared__ int sh_dst[MODE == kEpiGate ? BM : 1];
   // no copy is in flight where this is called (the barriers wait for them)
   auto claim = [&]() -> int {
     __syncthreads();
@@ -625,11 +654,16 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
     // stores wait for those copies), and held in one register each instead of
     // per-lane copies live across the K loop.
     float stg = 1.f, stb = 0.f;
+    int sdst = -1;
     if constexpr (MODE != kEpiLogit) {
       const int tid = threadIdx.x;
       if (ps < 0) {
-        if constexpr (MODE == kEpiGate)
-          if (tid < BM && tid < mcount) stg = gate[m0 + tid];
+        if constexpr (MODE == kEpiGate) {
+          if (tid < BM && tid < mcount) {
+            stg = gate[m0 + tid];
+            if (dmap != nullptr) sdst = dmap[m0 + tid];
+          }
+        }
         if (bias != nullptr && tid < BN && n0 + tid < Nout)
           stb = (float)((const bf16*)bias)[(size_t)e * Nout + n0 + tid];
       }
@@ -659,6 +693,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
     vm_wait_n<0>();
     if constexpr (MODE != kEpiLogit) {
       if (threadIdx.x < BM) sh_gate[threadIdx.x] = stg;
+      if constexpr (MODE == kEpiGate)
+        if (threadIdx.x < BM) sh_dst[threadIdx.x] = sdst;
       if (threadIdx.x < BN) sh_bias[threadIdx.x] = stb;
       // the stores must have completed before the barrier: s_barrier alone
       // does not order them before another wave's reads (with two workgroups
@@ -675,8 +711,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
     }
 
     if (cps < 0) {
-      ring_epilogue<BM, BN, WM, WN, MODE, SPLIT>(acc, sh_gate, sh_bias, cm0, cmcount, cn0, wr,
-                                                 wn0, l, bias, Nout, out, out_lo, ldo);
+      ring_epilogue<BM, BN, WM, WN, MODE, SPLIT>(acc, sh_gate, sh_dst, sh_bias, cm0, cmcount, cn0,
+                                                 wr, wn0, l, bias, Nout, out, out_lo, ldo, ydir,
+                                                 ybf16);
     } else {
       // raw partial accumulators, one float4 per lane and block, lane-major
       // so every store is one contiguous 1 KB
@@ -701,7 +738,9 @@ __global__ __launch_bounds__(kReduceThreads) void ring_reduce_kernel(
     const float* __restrict__ part, int grid, const void* __restrict__ bias,
     const float* __restrict__ gate, const int4* __restrict__ tiles,
     const int32_t* __restrict__ ntiles_p, int K, int Nout, void* __restrict__ out,
-    bf16* __restrict__ out_lo) {
+    bf16* __restrict__ out_lo, const int32_t* __restrict__ dmap, void* __restrict__ ydir,
+    int ybf16) {
+#pragma clang fp contract(off)
   constexpr bool G1 = MODE == kEpiGelu;
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int NTH = NW * kWave;
@@ -767,7 +806,11 @@ __global__ __launch_bounds__(kReduceThreads) void ring_reduce_kernel(
       }
     } else {
       const float gg = gate[slot];
-      *(f32x4*)((float*)out + o) = f32x4{v0 * gg, v1 * gg, v2 * gg, v3 * gg};
+      const int dst = dmap != nullptr ? dmap[slot] : -1;
+      if (dst >= 0)
+        store_direct(ydir, ybf16, dst, Nout, col, v0 * gg, v1 * gg, v2 * gg, v3 * gg);
+      else
+        *(f32x4*)((float*)out + o) = f32x4{v0 * gg, v1 * gg, v2 * gg, v3 * gg};
     }
   }
 }

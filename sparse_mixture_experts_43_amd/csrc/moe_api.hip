@@ -214,14 +214,24 @@ static int forward_impl(const void* x, const void* W_g, const float* logit_bias,
   if (e != hipSuccess) return hip_status(e);
   profile_mark(2, s);
   SplitK sk;  // a K-split second GEMM hands its partials straight to the combine
-  e = launch_expert_ffn(x, f.perm, f.off, f.gate, W1, b1, W2, b2, T, d, d_ff, N, kp, C, S_max,
-                        dtype, flags, f.slot_out, f.fs, s, &sk);
-  if (e != hipSuccess) return hip_status(e);
   const int y_dtype = (flags & MOE_FLAG_Y_F32) ? MOE_F32 : dtype;
   const void* xf = (flags & MOE_FLAG_IDENTITY_FALLBACK) ? x : nullptr;
+  // A token that kept exactly one pick outputs that pick's gate-scaled row,
+  // unless the identity fallback or a shared expert adds to it: then the
+  // second expert GEMM may write the row into y itself (DirectRows).
+  DirectRows dr;
+  if (!ec && xf == nullptr && shared_out == nullptr) {
+    dr.y = y;
+    dr.y_dtype = y_dtype;
+    dr.inv = f.inv;
+  }
+  e = launch_expert_ffn(x, f.perm, f.off, f.gate, W1, b1, W2, b2, T, d, d_ff, N, kp, C, S_max,
+                        dtype, flags, f.slot_out, f.fs, s, &sk, &dr);
+  if (e != hipSuccess) return hip_status(e);
   e = sk.nsplit > 1
           ? launch_combine_splitk(sk, f.inv, T, d, kp, y_dtype, xf, dtype, shared_out, y, s)
-          : launch_combine(f.slot_out, f.inv, T, d, kp, y_dtype, xf, dtype, shared_out, y, s);
+          : launch_combine(f.slot_out, f.inv, T, d, kp, y_dtype, xf, dtype, shared_out, y, s,
+                           dr.used);
   profile_mark(6, s);
   return hip_status(e);
 }

@@ -138,6 +138,20 @@ struct FfnScratch {
   int32_t* counts;    // [20]: tile counts written by the schedule kernel, then the
                       // GEMMs' per-XCD work-queue counters (zeroed by it)
   float* part;        // split-K partial sums of the decode GEMMs, or null
+  int32_t* direct;    // [S_max]: direct-row map (DirectRows), tiled bf16 paths only
+};
+// Direct rows: when the combine would only copy a token's single kept pick,
+// the second expert GEMM writes that row of y itself and the combine leaves
+// it alone. The schedule kernel writes map[slot] = token when the slot's
+// token kept no other pick (counted from inv), else -1. The caller fills y,
+// y_dtype and inv; launch_expert_ffn sets map and used when its path writes
+// direct rows (tiled bf16 on the LDS ring), else leaves used false.
+struct DirectRows {
+  void* y = nullptr;
+  int y_dtype = 0;
+  const int32_t* inv = nullptr;  // [T*k] pair -> slot or -1
+  int32_t* map = nullptr;
+  bool used = false;
 };
 constexpr int kFlagHiddenSplit = 1;  // MOE_FLAG_HIDDEN_SPLIT
 constexpr int kFlagYF32 = 2;         // MOE_FLAG_Y_F32
@@ -215,13 +229,16 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
                              const float* gate, const void* W1, const void* b1, const void* W2,
                              const void* b2, int T, int d, int d_ff, int N, int k, int C,
                              int S_max, int dtype, int flags, void* slot_out,
-                             const FfnScratch& s, hipStream_t st, SplitK* defer = nullptr);
+                             const FfnScratch& s, hipStream_t st, SplitK* defer = nullptr,
+                             DirectRows* dr = nullptr);
 // y_dtype: dtype of y; x (x_dtype, [T, d]) is read for tokens with no kept
 // pick when not null (identity fallback), else such tokens get zeros; sh (fp32
 // [T, d], a shared expert's output) is added to every token when not null.
+// skip_single: tokens that kept exactly one pick are left alone (their rows
+// were written by the second expert GEMM: DirectRows).
 hipError_t launch_combine(const void* slot_out, const int32_t* inv, int T, int d, int k,
                           int y_dtype, const void* x, int x_dtype, const float* sh, void* y,
-                          hipStream_t st);
+                          hipStream_t st, bool skip_single = false);
 hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, int d, int k,
                                  int y_dtype, const void* x, int x_dtype, const float* sh,
                                  void* y, hipStream_t st);
