@@ -201,14 +201,21 @@ hipError_t launch_combine_splitk(const SplitK& sk, const int32_t* inv, int T, in
                                  int y_dtype, const void* x, int x_dtype, const float* sh,
                                  void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  // the split-K path exists for bf16 weights (and activations) only; y may be
-  // fp32 or bf16
-  if (x_dtype != kBF16) x = nullptr;
-  const bf16* b = (const bf16*)sk.bias;
-  const bf16* xb = (const bf16*)x;
   const int V = y_dtype == kF32 ? 4 : 8;
   const long long n = (long long)T * (d / V);
   const int blocks = (int)((n + 255) / 256);
+  if (sk.f32) {
+    // fp32 layer (fp32 y, bias and x)
+    hipLaunchKernelGGL((combine_splitk_kernel<float, float, float>), dim3(blocks), dim3(256), 0,
+                       st, sk.part, sk.nsplit, sk.S_cap, (const float*)sk.bias, sk.gate, sk.off,
+                       sk.N, inv, T, d, k, x_dtype == kF32 ? (const float*)x : nullptr, sh,
+                       (float*)y);
+    return hipGetLastError();
+  }
+  // otherwise bf16 weights and activations; y may be fp32 or bf16
+  if (x_dtype != kBF16) x = nullptr;
+  const bf16* b = (const bf16*)sk.bias;
+  const bf16* xb = (const bf16*)x;
   if (y_dtype == kF32)
     hipLaunchKernelGGL((combine_splitk_kernel<float, bf16, bf16>), dim3(blocks), dim3(256), 0, st,
                        sk.part, sk.nsplit, sk.S_cap, b, sk.gate, sk.off, sk.N, inv, T, d, k, xb,

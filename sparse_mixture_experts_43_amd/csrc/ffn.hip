@@ -27,7 +27,10 @@
 //                 rows as the 16-row operand, slots as the 16-column operand,
 //                 LDS-DMA ring, split K with a fixed-order reduction), or by
 //                 decode_bf16_kernel below when K % 128 != 0.
-//   fp32        : FMA tiles (64 x 64), same schedule mechanism.
+//   fp32        : FMA tiles (64 x 64), same schedule mechanism; a second GEMM
+//                 with few tiles splits its K over up to 8 blocks per tile,
+//                 the fp32 partials summed in split order by the combine
+//                 (moe_forward) or reduce_f32_kernel (moe_expert_ffn).
 // Direct rows (tiled bf16, when the caller passes y): the schedule kernel
 // marks each slot whose token kept no other pick, and GEMM2's epilogue writes
 // that row straight into y (0 + gate * (acc + b2), as the combine would),
@@ -489,17 +492,23 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
 }
 
 // ---------------------------------------------------------------- fp32
+// K split (second GEMM, gridDim.y = nsplit > 1): block (tile, q) takes the
+// q-th range of kchunk K values (a multiple of 16) and writes its raw fp32
+// tile to part[q][slot][n] (S_cap rows per split); the reduction adds the
+// splits in order q = 0, 1, ... and applies bias and gate.
 template <bool G1>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
     const float* __restrict__ A, const int32_t* __restrict__ perm, int kpairs,
     const float* __restrict__ W, const float* __restrict__ bias, const float* __restrict__ gate,
     const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int Nout,
-    float* __restrict__ out) {
+    float* __restrict__ out, int kchunk, float* __restrict__ part, int S_cap) {
   constexpr int BM = 64, BN = 64, BK = 16;
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
   const int tile = blockIdx.x;
   if (tile >= *ntiles_p) return;
+  const int kbeg = blockIdx.y * kchunk;
+  const int kend = kbeg + kchunk < K ? kbeg + kchunk : K;
   const int4 te = tiles[tile];
   const int e = te.x, m0 = te.y, mcount = te.z, n0 = te.w * BN;
   const int tid = threadIdx.x;
@@ -510,10 +519,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   const float* brow = W + ((size_t)e * Nout + bn) * K;
   const int ty = tid / 16, tx = tid % 16;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += BK) {
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
     const int kk = k0 + lk;
     float4 av = make_float4(0.f, 0.f, 0.f, 0.f), bv = av;
-    if (kk < K) {
+    if (kk < kend) {
       av = *(const float4*)(arow + kk);
       bv = *(const float4*)(brow + kk);
     }
@@ -543,10 +552,40 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + tx * 4 + j;
       if (col >= Nout) continue;
+      if (part != nullptr) {
+        part[((size_t)blockIdx.y * S_cap + slot) * Nout + col] = acc[i][j];
+        continue;
+      }
       float v = acc[i][j] + (bias != nullptr ? bias[(size_t)e * Nout + col] : 0.f);
       v = G1 ? gelu_erf(v) : v * gate[slot];
       out[(size_t)slot * Nout + col] = v;
     }
+  }
+}
+
+// The reduction of a K-split fp32 second GEMM: slot value gate * (((0 + p_0)
+// + p_1) + ... + b2), the operations and order of combine_splitk_kernel, so
+// moe_expert_ffn + moe_combine give the bits of the forward, which folds the
+// reduction into its combine. A block per (expert, 64 output columns),
+// threads over (slot, column).
+__global__ __launch_bounds__(256) void reduce_f32_kernel(
+    const float* __restrict__ part, int nsplit, int S_cap, int cap, const int32_t* __restrict__ off,
+    const float* __restrict__ bias, const float* __restrict__ gate, int Nout, int nblk_n,
+    float* __restrict__ out) {
+#pragma clang fp contract(off)
+  const int e = blockIdx.x / nblk_n;
+  const int nb = blockIdx.x - e * nblk_n;
+  int m0, mcount;
+  expert_rows(off, e, S_cap, cap, m0, mcount);
+  const int n0 = nb * 64;
+  for (int i = threadIdx.x; i < mcount * 64; i += 256) {
+    const int sl = i / 64, n = n0 + i % 64;
+    if (n >= Nout) continue;
+    const int slot = m0 + sl;
+    float v = 0.f;
+    for (int q = 0; q < nsplit; ++q) v += part[((size_t)q * S_cap + slot) * Nout + n];
+    v += bias != nullptr ? bias[(size_t)e * Nout + n] : 0.f;
+    out[(size_t)slot * Nout + n] = v * gate[slot];
   }
 }
 
@@ -610,8 +649,19 @@ Plan make_plan(int T, int d, int d_ff, int N, int k, int C, int S_max, int dtype
   const long long mt = a < b ? a : b;
   p.max1 = (int)(mt * cdiv(d_ff, p.BN1));
   p.max2 = (int)(mt * cdiv(d, p.BN2));
+  if (p.path == kPathF32) {
+    // second GEMM: split K (d_ff) while fewer than 256 blocks could run, each
+    // split keeping at least 64 K values (the tiny fp32 layer: 16 tiles of
+    // K = 512 on 256 CUs otherwise)
+    int s = 1;
+    while (p.max2 * s < 256 && d_ff / (2 * s) >= 64 && s < 8) s *= 2;
+    p.ks2 = s;
+  }
   return p;
 }
+
+// K values per split of an fp32 GEMM (a multiple of the kernel's 16-wide steps)
+int f32_kchunk(int K, int nsplit) { return cdiv(cdiv(K, nsplit), 16) * 16; }
 
 
 
@@ -818,6 +868,8 @@ void carve_ffn(Carver& c, int T, int d, int d_ff, int N, int k, int C, int S_max
   } else if (pl.path == kPathTiledL || pl.path == kPathTiledM) {
     const int mx = pl.max1 > pl.max2 ? pl.max1 : pl.max2;
     pn = ring_part_floats(pl.BM, pl.BN1, false, mx);
+  } else if (pl.path == kPathF32 && pl.ks2 > 1) {
+    pn = (size_t)pl.ks2 * rows * d;
   }
   s->part = pn ? c.take<float>(pn) : nullptr;
   s->direct = (pl.path == kPathTiledL || pl.path == kPathTiledM) ? c.take<int32_t>(rows) : nullptr;
@@ -875,11 +927,30 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
     profile_mark(3, st);
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(pl.max1 > 0 ? pl.max1 : 1), dim3(256), 0, st,
                        (const float*)x, perm, k, (const float*)W1, (const float*)b1, nullptr, t1,
-                       s.counts + 0, d, d_ff, (float*)s.hidden);
+                       s.counts + 0, d, d_ff, (float*)s.hidden, f32_kchunk(d, 1), nullptr, 0);
     profile_mark(4, st);
-    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(pl.max2 > 0 ? pl.max2 : 1), dim3(256), 0, st,
-                       (const float*)s.hidden, nullptr, k, (const float*)W2, (const float*)b2, gate,
-                       t2, s.counts + 1, d_ff, d, (float*)slot_out);
+    const int ks = pl.ks2;
+    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(pl.max2 > 0 ? pl.max2 : 1, ks), dim3(256), 0,
+                       st, (const float*)s.hidden, nullptr, k, (const float*)W2, (const float*)b2,
+                       gate, t2, s.counts + 1, d_ff, d, (float*)slot_out, f32_kchunk(d_ff, ks),
+                       ks > 1 ? s.part : nullptr, S_max);
+    if (ks > 1) {
+      if (defer != nullptr) {
+        // the combine finishes the slot values (combine_splitk_kernel)
+        defer->part = s.part;
+        defer->nsplit = ks;
+        defer->S_cap = S_max;
+        defer->bias = b2;
+        defer->f32 = true;
+        defer->gate = gate;
+        defer->off = off;
+        defer->N = N;
+      } else {
+        const int nbn = cdiv(d, 64);
+        hipLaunchKernelGGL(reduce_f32_kernel, dim3(N * nbn), dim3(256), 0, st, s.part, ks, S_max,
+                           pl.cap, off, (const float*)b2, gate, d, nbn, (float*)slot_out);
+      }
+    }
     profile_mark(5, st);
     return hipGetLastError();
   }

@@ -219,6 +219,7 @@ struct SplitK {
   int nsplit = 1;
   int S_cap = 0;
   const void* bias = nullptr;   // b2 [N, d] activation dtype, or null
+  bool f32 = false;             // fp32 activations (bias, x) instead of bf16
   const float* gate = nullptr;  // slot gates
   const int32_t* off = nullptr; // expert offsets [N+1] (slot -> expert for the bias)
   int N = 0;
