@@ -11,7 +11,9 @@
 // arrive in fp32. Each thread owns 16 bytes of one output row: coalesced fp32
 // loads per kept pick, one 16-byte store. When the second expert GEMM wrote
 // the rows of tokens that kept a single pick straight into y (no fallback, no
-// shared expert), those tokens are skipped here.
+// shared expert), those tokens are skipped here. With more than 8 pairs per
+// token (expert choice) and a whole wave on one token row, the wave finds the
+// kept pairs with one ballot per 64 and loads their rows 8 at a time.
 #include "moe_common.h"
 
 namespace moe {
@@ -65,6 +67,47 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
   bool any = false;
+  if (k > G && vpr % kWave == 0) {
+    // Many picks per token (expert choice: every expert is a candidate) and a
+    // whole wave on one token row: the wave reads 64 of the token's slot
+    // indices at once (one per lane), a ballot marks the kept ones, and their
+    // rows are loaded 8 at a time (all in flight together) and added in pick
+    // order, the order of the loop below: the same sums, bit for bit.
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int j0 = 0; j0 < k; j0 += kWave) {
+      const int sv = j0 + lane < k ? it[j0 + lane] : -1;
+      unsigned long long m = __ballot(sv >= 0);
+      while (m != 0ull) {
+        int s[G];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          s[q] = -1;
+          if (m != 0ull) {
+            s[q] = __shfl(sv, __ffsll((long long)m) - 1, kWave);
+            m &= m - 1;
+          }
+        }
+        f32x4 v[G][V / 4];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          const f32x4* src = (const f32x4*)(slot_out + (size_t)(s[q] < 0 ? 0 : s[q]) * d + c);
+#pragma unroll
+          for (int h = 0; h < V / 4; ++h)
+            v[q][h] = s[q] >= 0 ? src[h] : (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          if (s[q] < 0) continue;
+          any = true;
+#pragma unroll
+          for (int h = 0; h < V / 4; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[4 * h + i] += v[q][h][i];
+        }
+      }
+    }
+    k = 0;  // the loop below has nothing left to do
+  }
   // picks in groups of 8 (all of them for k <= 8): the slot indices first,
   // then every kept pick's row load issued before the first add (one round
   // trip per group), then the sums in fixed pick order

@@ -28,6 +28,10 @@ EC_CASES = [
     ("ec_large_pairs", 2048, 128, 64, 64, 4, 1.0, "bf16", False, "zipf1.1"),
     ("ec_dense_no_cap", 128, 64, 64, 8, 2, 0.0, "bf16", True, "none"),
     ("ec_decode_path", 96, 256, 384, 8, 2, 0.5, "bf16", True, "normal0.5"),
+    # more than 8 candidate pairs per token and rows wide enough for a whole
+    # wave per token row (the combine's ballot path), bf16 and fp32
+    ("ec_wide_rows", 512, 512, 256, 16, 2, 0.5, "bf16", False, "zipf1.1"),
+    ("ec_f32_wide_rows", 256, 256, 128, 12, 2, 0.5, "f32", True, "normal0.5"),
 ]
 
 

@@ -61,6 +61,9 @@ CASES = [
     # the documented maxima: N = 1024 experts with k = 16 (the widest top-k
     # rows), d = 65536 (router and first GEMM over the longest K), d_ff = 65536
     ("max_N_k", 256, 64, 64, 1024, 16, 1.0, "bf16", False, "normal0.5", 0),
+    # top-12 with drops on rows wide enough for the combine's ballot path (and
+    # single-pick tokens written by the second GEMM)
+    ("topk12_wide_rows", 512, 512, 256, 16, 12, 0.2, "bf16", False, "zipf1.1", 0),
     ("max_d", 8, 65536, 64, 4, 2, 0.0, "bf16", False, "none", 0),
     ("max_dff", 8, 64, 65536, 4, 2, 0.0, "bf16", True, "none", 0),
     ("dense_k_eq_N", 128, 64, 128, 4, 4, 0.0, "bf16", False, "none", 0),
