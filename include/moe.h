@@ -255,7 +255,8 @@ int moe_expert_ffn(const void* x, const int32_t* perm, const int32_t* offsets,
  *        not overlapping W: for each expert e, row block rb (16 rows) and K
  *        chunk kc (32 values) a 1 KB piece at byte
  *        ((e*rows/16 + rb)*K/32 + kc)*1024 whose 16-byte word w holds the 8
- *        values W[e][rb*16 + w/4][kc*32 + 8*((w%4) ^ ((w/16)%4)) ..+8].
+ *        values W[e][rb*16 + r(w)][kc*32 + 8*c(w) ..+8], with h = w/16,
+ *        g = (w/4)%4, r(w) = (g%2) + 2*h + 8*(g/2) and c(w) = (w%4) ^ h.
  * dtype must be MOE_BF16, rows % 16 == 0 and K % 128 == 0
  * (MOE_ERR_UNSUPPORTED otherwise). Asynchronous on `stream`; no workspace. */
 int moe_pack_weights(const void* W, int N, int rows, int K, int dtype, void* W_packed,

@@ -970,7 +970,7 @@ hipError_t launch_expert_ffn(const void* x, const int32_t* perm, const int32_t* 
 namespace {
 // Packed weight layout (see gemm_ring.h): output word g (16 bytes) of piece
 // (e, row block rb, K chunk kc) = g / 64 is word w = g % 64 of the piece: row
-// rb*16 + w/4, 8 bf16 from K offset kc*32 + 8*((w%4) ^ ((w/16)%4)). A grid
+// rb*16 + piece_row(w), 8 bf16 from K offset kc*32 + 8*piece_chunk(w). A grid
 // stride over the words; consecutive threads write consecutive words.
 __global__ __launch_bounds__(256) void pack_weights_kernel(const bf16* __restrict__ W, int rows,
                                                            int K, size_t words,
@@ -984,8 +984,8 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const bf16* __restric
     const size_t rest = piece / kcs;
     const int rb = (int)(rest % rbs);
     const size_t e = rest / rbs;
-    const int row = rb * 16 + (w >> 2);
-    const int chunk = (w & 3) ^ ((w >> 4) & 3);
+    const int row = rb * 16 + piece_row(w);
+    const int chunk = piece_chunk(w);
     out[g] = *(const uint4*)(W + ((e * rows + row) * K + (size_t)kc * 32 + chunk * 8));
   }
 }

@@ -182,9 +182,8 @@ __global__ __launch_bounds__(256) void decode_dma_kernel(
       for (int kq = 0; kq < KC / 32; ++kq) {
         const int ch = 4 * kq + (l >> 4);
         // packed: piece 4 kq + wv, this lane's row l & 15 and 16-byte chunk
-        // l >> 4 at the copy's word 4 (l & 15) + ((l >> 4) ^ ((l >> 2) & 3))
-        const int wo = packed ? (4 * kq + wv) * 1024 + (l & 15) * 64 +
-                                    16 * ((l >> 4) ^ ((l >> 2) & 3))
+        // l >> 4 at the copy's word piece_slot(l & 15, l >> 4)
+        const int wo = packed ? (4 * kq + wv) * 1024 + 16 * piece_slot(l & 15, l >> 4)
                               : R * ROWB + 16 * (ch ^ Rs);
         const bf16x8 wf = *(const bf16x8*)(st + Geo::W_OFF + wo);
 #pragma unroll

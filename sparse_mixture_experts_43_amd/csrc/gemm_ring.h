@@ -45,16 +45,21 @@ namespace {
 // Packed weights (`packed` != 0, written by moe_pack_weights): expert e's
 // matrix [Nout, K] is stored as pieces of 16 rows x 32 K, piece (row block rb,
 // K chunk kc) at ((e * Nout/16 + rb) * K/32 + kc) * 1024 bytes, its 16-byte
-// word w holding row rb*16 + w/4, chunk (w%4) ^ ((w/16)%4): exactly the LDS
-// image of one weight copy below, so a copy reads 1 KB contiguous instead of
-// 64 bytes from each of 16 rows (the same tile contents and results).
+// word w holding row rb*16 + piece_row(w), chunk piece_chunk(w): exactly the
+// LDS image of one weight copy below, so a copy reads 1 KB contiguous instead
+// of 64 bytes from each of 16 rows (the same tile contents and results).
 //
 // Fast path for K % 32 == 0. Tiles stream into a RING-slot LDS ring with
 // global_load_lds_dwordx4 (each lane's 16 bytes land at base + 16 * lane, so a
-// wave instruction fills 16 rows x 64 bytes); no VGPR staging and no ds_write.
-// Rows are 64 bytes (32 bf16 of K); the 16-byte chunk c of row r sits at
-// position c ^ ((r >> 2) & 3), which keeps the b128 fragment reads of 16
-// consecutive rows on distinct banks. Stage kt+RING-1 is requested while stage
+// wave instruction fills the 1 KB of 16 rows x 32 K); no VGPR staging and no
+// ds_write. Within such a 1 KB piece, the 16-byte chunk c (K 8c .. 8c+7) of
+// row r sits in slot piece_slot(r, c) (below), so that the b128 fragment
+// reads (lane l: row l & 15, chunk l >> 4) of any 16 lanes that share two of
+// their lane-index bits, and of any 8 lanes that share three, fall on 16
+// distinct groups of 4 banks. (Row-major 64-byte rows with the chunks
+// XOR-swizzled by (r >> 2) & 3 kept only the 16 consecutive lanes on distinct
+// banks; rocprofv3 counted 4 bank-conflict cycles per fragment read.) Stage
+// kt+RING-1 is requested while stage
 // kt is multiplied; one workgroup barrier per stage, taken mid-stage. A
 // stage's fragment reads are spread over both halves of the steps around that
 // barrier: its first half of token blocks and its weight blocks during the
@@ -77,6 +82,20 @@ namespace {
 constexpr int kRK = 32;         // K per ring stage
 constexpr int kRing = 4;        // default ring slots
 constexpr int kRowB = kRK * 2;  // bytes per tile row per stage
+
+// Slot (16-byte word, 0..63) of row r (0..15), K chunk c (0..3) in a 1 KB
+// piece of 16 rows x 32 K, and its inverse: slot = 16 h + 4 g + (c ^ h) with
+// h = bits 1-2 of r and g = bit 0 of r plus bit 3 of r times 2.
+__host__ __device__ __forceinline__ int piece_slot(int r, int c) {
+  const int h = (r >> 1) & 3;
+  const int g = (r & 1) | ((r >> 3) << 1);
+  return 16 * h + 4 * g + (c ^ h);
+}
+__host__ __device__ __forceinline__ int piece_row(int s) {
+  const int h = s >> 4, g = (s >> 2) & 3;
+  return (g & 1) | (h << 1) | ((g >> 1) << 3);
+}
+__host__ __device__ __forceinline__ int piece_chunk(int s) { return (s & 3) ^ (s >> 4); }
 
 #define MOE_LDS __attribute__((address_space(3)))
 
@@ -387,15 +406,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
   const int wn0 = (wv % (BN / WN)) * WN;
 
   // DMA source pointers: wave-load i covers tile rows (i*NW + wv)*16 .. +16;
-  // lane l fills row +l/4, position l%4, which holds chunk (l%4) ^ ((l>>4)&3).
-  const int csw = ((l & 3) ^ ((l >> 4) & 3)) * 16;  // byte offset of the chunk
+  // lane l fills slot l of the piece: row piece_row(l), chunk piece_chunk(l).
+  const int csw = piece_chunk(l) * 16;  // byte offset of the chunk
   const unsigned char* pa[AI];
   const unsigned char* pl[ALO ? AI : 1];
   const unsigned char* pb[BI];
   auto set_ptrs = [&](int e, int m0, int mcount, int n0) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      const int r = (i * NW + wv) * 16 + (l >> 2);
+      const int r = (i * NW + wv) * 16 + piece_row(l);
       const int rr = r < mcount ? r : mcount - 1;
       const int slot = m0 + rr;
       const size_t row = G1 ? (size_t)(perm[slot] / kpairs) : (size_t)slot;
@@ -414,7 +433,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
         pb[i] = (const unsigned char*)We + (size_t)(rb < nrb ? rb : nrb - 1) * (K / kRK) * 1024 +
                 16 * l;
       } else {
-        const int r = (i * NW + wv) * 16 + (l >> 2);
+        const int r = (i * NW + wv) * 16 + piece_row(l);
         const int n = n0 + r < Nout ? n0 + r : Nout - 1;
         pb[i] = (const unsigned char*)(We + (size_t)n * K) + csw;
       }
@@ -459,15 +478,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_ring_kernel(
   };
 
   // Fragment reads (v_mfma_f32_16x16x32_bf16 operands): lane l reads row
-  // 16*blk + (l & 15), 16-byte chunk l >> 4 (K 8*(l>>4) .. +8), which sits at
-  // position (l >> 4) ^ (((l & 15) >> 2) & 3); the 16 lanes of a quarter-wave
-  // hit all 64 banks once.
-  const int pos = (((l >> 4) ^ ((l >> 2) & 3)) * 16);
+  // 16*blk + (l & 15), 16-byte chunk l >> 4 (K 8*(l>>4) .. +8), which sits in
+  // slot piece_slot(l & 15, l >> 4) of the block's 1 KB piece.
+  const int pos = piece_slot(l & 15, l >> 4) * 16;
   int aoffs[MT], boffs[NTW];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) aoffs[i] = ((2 * i + wr) * 16 + (l & 15)) * kRowB + pos;
+  for (int i = 0; i < MT; ++i) aoffs[i] = (2 * i + wr) * 16 * kRowB + pos;
 #pragma unroll
-  for (int j = 0; j < NTW; ++j) boffs[j] = (wn0 + j * 16 + (l & 15)) * kRowB + pos;
+  for (int j = 0; j < NTW; ++j) boffs[j] = (wn0 + j * 16) * kRowB + pos;
 
   bf16x8 af[2][MT], bfr[2][NTW], alf[ALO ? 2 : 1][ALO ? MT : 1];
   // NA: token blocks of this wave that hold rows of the tile (a partly filled

@@ -242,7 +242,7 @@ using namespace moe;
 
 extern "C" {
 
-int moe_version(void) { return 102; }
+int moe_version(void) { return 103; }
 
 const char* moe_strerror(int status) {
   switch (status) {

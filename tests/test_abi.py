@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_strerror(lib):
     from sparse_mixture_experts_43_amd._lib import _lib as raw
-    assert lib.moe_version() == 102
+    assert lib.moe_version() == 103
     for code in (0, -1, -2, -3, -4, 7):
         assert raw.moe_strerror(code)
 

@@ -65,8 +65,9 @@ def _host_pack(W: np.ndarray) -> np.ndarray:
     N, rows, K = W.shape
     out = np.empty(N * rows * K, dtype=W.dtype)
     w = np.arange(64)
-    row_in = w // 4
-    chunk = (w % 4) ^ ((w // 16) % 4)
+    h, g = w // 16, (w // 4) % 4
+    row_in = (g % 2) + 2 * h + 8 * (g // 2)
+    chunk = (w % 4) ^ h
     pos = 0
     for e in range(N):
         for rb in range(rows // 16):
